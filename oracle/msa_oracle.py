@@ -1,0 +1,391 @@
+"""CPU oracle for MiniMax-M3-style block-sparse paged decode attention.
+
+TEST INFRASTRUCTURE ONLY. This module is the plain, slow reference that the HIP
+library is checked against. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import it; the product path never does. It
+shares no code with the HIP library: it reads host numpy arrays in the layouts
+the C header documents and computes every step from its definition, in float64.
+
+Sources (prhub.com.cn summaries of vLLM pull requests):
+  [P1] PR #47287, "add ROCm AITER sparse paged attention for MiniMax-M3"
+  [P2] PR #54682, "optimise gfx950 MiniMax-M3 decode index and top-k"
+  [P4] PR #56170, "MiniMax M3 cu_seqlens_k first element zeroed on the device"
+Section names are the pages' own: 功能与动机 (motivation), 实现拆解 (implementation
+breakdown, numbered items), 关键源码片段 (key source excerpt), 评论区精华 (review
+highlights), 风险与影响 (risks).
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * index score = raw dot product of the row's index query with each token's
+    index key, one index head, no scale;
+  * pooling over a 128-token block = max over the block's visible tokens;
+  * a row at absolute position pos sees keys 0..pos (v = pos + 1);
+  * selection keeps min(topk, nb) blocks under the total order (score
+    descending, block id ascending, -0 == +0) and lists them by ascending id;
+  * every selected block expands to all 8 of its 16-token sub-pages, sub-page i
+    of physical page P being 8P + i; the row is zero-filled up to 8*topk;
+  * attention over the selected blocks' visible tokens with an exact softmax;
+    FP8 values are dequantised as scale x e4m3fn(code).
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py to
+closed forms, brute force, library routines or invariants, except the modelling
+readings above (score formula and pooling operator), which no page fixes:
+that these match the real model is parity unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 128       # tokens per KV / index-K page and per sparse block
+SUB = 16         # tokens per sub-page of the page-16 view
+SUBS_PER_PAGE = PAGE // SUB
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64: the bf16 pattern is the top half of
+    an IEEE binary32 word."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP 8-bit floating point E4M3 ("fn": finite, no infinities).
+
+    Bit layout S.EEEE.MMM, exponent bias 7. E == 0 encodes subnormals
+    (-1)^S * 2^-6 * M/8; otherwise (-1)^S * 2^(E-7) * (1 + M/8). The two codes
+    S.1111.111 are NaN; S.1111.110 is the largest finite magnitude, 448.
+    FP8 K/V are the storage format named in [P1] 实现拆解 item 2.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = sign * np.ldexp(m / 8.0, -6)
+    val = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: batch metadata
+# ---------------------------------------------------------------------------
+def build_metadata(seq_lens: np.ndarray, query_lens: np.ndarray) -> dict:
+    """Device-side batch metadata, [P4] 实现拆解 items 1-3 and 关键源码片段.
+
+    cu_seqlens_k starts with a zero and continues with the running sum of the
+    requests' KV lengths; cu_seqlens_q is the running start of each request's
+    query rows; every query row gets its request id and absolute position,
+    which is the request's prior context plus the row's offset inside the
+    request's new tokens (context_len = seq_len - query_len). Decode rows come
+    first and prefill rows after, so one formula covers both.
+    cu_blocks counts the 128-token blocks of each request's KV.
+    """
+    L = [int(x) for x in seq_lens]
+    ql = [int(x) for x in query_lens]
+    R = len(L)
+    cu_q = [0] * (R + 1)
+    cu_k = [0] * (R + 1)
+    cu_b = [0] * (R + 1)
+    row_req, row_pos = [], []
+    for r in range(R):
+        cu_q[r + 1] = cu_q[r] + ql[r]
+        cu_k[r + 1] = cu_k[r] + L[r]
+        cu_b[r + 1] = cu_b[r] + (L[r] + PAGE - 1) // PAGE
+        context_len = L[r] - ql[r]
+        for i in range(ql[r]):
+            row_req.append(r)
+            row_pos.append(context_len + i)
+    return {
+        "cu_seqlens_q": np.array(cu_q, dtype=np.int64),
+        "cu_seqlens_k": np.array(cu_k, dtype=np.int64),
+        "cu_blocks": np.array(cu_b, dtype=np.int64),
+        "row_req": np.array(row_req, dtype=np.int64),
+        "row_pos": np.array(row_pos, dtype=np.int64),
+    }
+
+
+def visible_keys(row_pos: int) -> int:
+    """A row at absolute position pos attends to keys 0..pos (causal)."""
+    return int(row_pos) + 1
+
+
+def num_blocks(v: int) -> int:
+    return (int(v) + PAGE - 1) // PAGE
+
+
+# ---------------------------------------------------------------------------
+# Step 2: index scores and per-block pooling
+# ---------------------------------------------------------------------------
+def index_keys_of_request(index_k_bits: np.ndarray, bt_row: np.ndarray, ntok: int) -> np.ndarray:
+    """Logical index keys [ntok][128] of one request: token t lives in physical
+    page bt_row[t // 128], slot t % 128 (the page-128 cache, [P1] 实现拆解 item 3)."""
+    out = np.empty((ntok, index_k_bits.shape[-1]), dtype=np.float64)
+    for j in range(num_blocks(ntok)):
+        lo, hi = j * PAGE, min((j + 1) * PAGE, ntok)
+        out[lo:hi] = bf16_to_f64(index_k_bits[int(bt_row[j]), : hi - lo])
+    return out
+
+
+def token_scores(index_q_row: np.ndarray, keys: np.ndarray, v: int) -> np.ndarray:
+    """Score of one query row against each visible token t < v: the dot product
+    of the row's index query with the token's index key ([P2] 功能与动机 and
+    实现拆解 item 1 name the per-row decode scorer; the formula is a reading)."""
+    qi = bf16_to_f64(index_q_row)
+    return keys[:v] @ qi
+
+
+def pool_blocks(tok_scores: np.ndarray, nb: int) -> np.ndarray:
+    """Block score = max of the token scores inside the 128-token block; the
+    last block may be partial and pools over its visible tokens only."""
+    out = np.empty(nb, dtype=np.float64)
+    for b in range(nb):
+        out[b] = np.max(tok_scores[b * PAGE:(b + 1) * PAGE])
+    return out
+
+
+def block_scores(index_q: np.ndarray, index_k: np.ndarray, block_table: np.ndarray,
+                 seq_lens: np.ndarray, query_lens: np.ndarray, ld_s: int,
+                 rows=None) -> np.ndarray:
+    """[N][ld_s] pooled scores; -inf at and beyond each row's block count.
+
+    ``rows`` restricts the computation to a subset of rows (others stay -inf)."""
+    meta = build_metadata(seq_lens, query_lens)
+    N = len(meta["row_req"])
+    out = np.full((N, ld_s), -np.inf, dtype=np.float64)
+    want = range(N) if rows is None else sorted(set(int(r) for r in rows))
+    by_req: dict[int, list[int]] = {}
+    for n in want:
+        by_req.setdefault(int(meta["row_req"][n]), []).append(n)
+    for r, ns in by_req.items():
+        keys = index_keys_of_request(index_k, block_table[r], int(seq_lens[r]))
+        for n in ns:
+            v = visible_keys(meta["row_pos"][n])
+            nb = num_blocks(v)
+            out[n, :nb] = pool_blocks(token_scores(index_q[n], keys, v), nb)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 3: top-k selection, page-16 table, context length
+# ---------------------------------------------------------------------------
+def select_blocks(scores_row: np.ndarray, nb: int, topk: int) -> np.ndarray:
+    """Top-k blocks of one row ([P2] 实现拆解 item 1: the fused top-k picks each
+    row's blocks): order the eligible blocks by score descending with the lower
+    block id first among equals, keep the first min(topk, nb), and list them by
+    ascending block id. Python float comparison treats -0.0 and +0.0 as equal."""
+    cand = [(float(scores_row[b]), b) for b in range(nb)]
+    ranked = sorted(cand, key=lambda sb: (-sb[0], sb[1]))   # stable
+    keep = ranked[:min(topk, nb)]
+    return np.array(sorted(b for _, b in keep), dtype=np.int64)
+
+
+def select_blocks_by_rank(scores_row: np.ndarray, nb: int, topk: int) -> np.ndarray:
+    """Second formulation of the same selection: block b is kept iff fewer than
+    min(topk, nb) eligible blocks beat it (higher score, or equal score and
+    lower id)."""
+    kk = min(topk, nb)
+    s = [float(scores_row[b]) for b in range(nb)]
+    keep = []
+    for b in range(nb):
+        beaten_by = sum(1 for c in range(nb) if s[c] > s[b] or (s[c] == s[b] and c < b))
+        if beaten_by < kk:
+            keep.append(b)
+    return np.array(keep, dtype=np.int64)
+
+
+def sparse_table_row(sel: np.ndarray, bt_row: np.ndarray, topk: int) -> np.ndarray:
+    """Page-16 sparse block table row ([P1] 实现拆解 item 3: a page-16 K/V view
+    derived from the page-128 layout; [P2] 实现拆解 items 1 and 4: the table row
+    is written from the selected values). Selected block j (in ascending order)
+    occupies entries 8j..8j+7 = 8*bt_row[sel_j] + i; entries from 8*len(sel) up
+    to the row width 8*topk are zero and nothing is written past the width
+    ([P1] 评论区精华: the zero-padding store must stay inside the row)."""
+    out = np.zeros(SUBS_PER_PAGE * topk, dtype=np.int64)
+    for j, b in enumerate(sel):
+        for i in range(SUBS_PER_PAGE):
+            out[SUBS_PER_PAGE * j + i] = SUBS_PER_PAGE * int(bt_row[int(b)]) + i
+    return out
+
+
+def context_length(sel: np.ndarray, v: int) -> int:
+    """Tokens the row attends to: each selected block contributes its visible
+    tokens, min(128, v - 128*b) ([P2] 实现拆解 item 1: the fused pass also
+    outputs context lengths)."""
+    return int(sum(min(PAGE, int(v) - PAGE * int(b)) for b in sel))
+
+
+def selection_row_outputs(sel: np.ndarray, topk: int) -> np.ndarray:
+    """sel written as [topk] with -1 after the kept blocks."""
+    out = np.full(topk, -1, dtype=np.int64)
+    out[:len(sel)] = sel
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 4: sparse paged attention over the selected blocks
+# ---------------------------------------------------------------------------
+def kv_token(cache: np.ndarray, bt_row: np.ndarray, t: int, hkv: int, kv_dtype: int,
+             plane: str) -> np.ndarray:
+    """Raw stored values of one token for KV head hkv, addressed logically:
+    physical page P = bt_row[t // 128], sub-page 8P + (t % 128) // 16, slot t % 16.
+    K sub-pages are token-major [16][Hkv][128]; V sub-pages are dim-major
+    [Hkv][128][16]."""
+    page = int(bt_row[t // PAGE])
+    sub = SUBS_PER_PAGE * page + (t % PAGE) // SUB
+    slot = t % SUB
+    raw = cache[sub, slot, hkv, :] if plane == "k" else cache[sub, hkv, :, slot]
+    return bf16_to_f64(raw) if kv_dtype == 0 else e4m3fn_to_f64(raw)
+
+
+def token_scale(scale: np.ndarray | None, scale_mode: int, bt_row: np.ndarray, t: int,
+                hkv: int) -> float:
+    """FP8 K/V scale of one token ([P1] 实现拆解 item 2 and 关键文件: k_scale and
+    v_scale, 'scalar' or 'per_token_head'). Per-token-head scales are stored
+    [P][128][Hkv] (same as [8P][16][Hkv])."""
+    if scale_mode == 0:
+        return 1.0
+    if scale_mode == 1:
+        return float(np.asarray(scale).reshape(-1)[0])
+    page = int(bt_row[t // PAGE])
+    s = np.asarray(scale).reshape(-1, PAGE, np.asarray(scale).shape[-1])
+    return float(s[page, t % PAGE, hkv])
+
+
+def dequant_tokens(cache, scale, scale_mode, kv_dtype, bt_row, tokens, hkv, plane):
+    """K-hat / V-hat rows: scale x stored value, float64."""
+    out = np.empty((len(tokens), cache.shape[-1] if plane == "k" else cache.shape[-2]),
+                   dtype=np.float64)
+    for i, t in enumerate(tokens):
+        out[i] = token_scale(scale, scale_mode, bt_row, t, hkv) * \
+            kv_token(cache, bt_row, t, hkv, kv_dtype, plane)
+    return out
+
+
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Exact attention of query heads q [H][D] over keys k [T][D], values
+    v [T][D]: two-pass softmax (max, then normalised exponentials)."""
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    z = sm_scale * (q @ k.T)                       # [H][T]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return (e @ v) / e.sum(axis=1, keepdims=True)
+
+
+def sparse_attention_row(q_row_bits: np.ndarray, k_cache, v_cache, kv_dtype: int,
+                         scale_mode: int, k_scale, v_scale, bt_row: np.ndarray,
+                         sel: np.ndarray, v: int, sm_scale: float) -> np.ndarray:
+    """Attention of one row's query heads over only the selected blocks' visible
+    tokens ([P1] 功能与动机: attention over a small number of logical blocks;
+    实现拆解 item 3: paged attention over the page-16 view). Tokens are walked
+    logically through the request's page-128 table, not through the page-16
+    table, so that the GPU's table walk is checked against the definition.
+    Query head h reads KV head h // (Hq / Hkv)."""
+    hq = q_row_bits.shape[0]
+    hkv_n = k_cache.shape[2]
+    group = hq // hkv_n
+    tokens = [t for b in sel for t in range(PAGE * int(b), min(PAGE * (int(b) + 1), v))]
+    q = bf16_to_f64(q_row_bits)
+    out = np.zeros((hq, q.shape[1]), dtype=np.float64)
+    for g in range(hkv_n):
+        kh = dequant_tokens(k_cache, k_scale, scale_mode, kv_dtype, bt_row, tokens, g, "k")
+        vh = dequant_tokens(v_cache, v_scale, scale_mode, kv_dtype, bt_row, tokens, g, "v")
+        out[g * group:(g + 1) * group] = softmax_attention(q[g * group:(g + 1) * group], kh, vh, sm_scale)
+    return out
+
+
+def dense_causal_attention_row(q_row_bits, k_cache, v_cache, kv_dtype, scale_mode, k_scale,
+                               v_scale, bt_row, v, sm_scale) -> np.ndarray:
+    """Textbook causal attention of one row over every visible key t < v."""
+    hq = q_row_bits.shape[0]
+    hkv_n = k_cache.shape[2]
+    group = hq // hkv_n
+    q = bf16_to_f64(q_row_bits)
+    out = np.zeros((hq, q.shape[1]), dtype=np.float64)
+    tokens = list(range(int(v)))
+    for g in range(hkv_n):
+        kh = dequant_tokens(k_cache, k_scale, scale_mode, kv_dtype, bt_row, tokens, g, "k")
+        vh = dequant_tokens(v_cache, v_scale, scale_mode, kv_dtype, bt_row, tokens, g, "v")
+        for h in range(g * group, (g + 1) * group):
+            z = np.array([sm_scale * float(q[h] @ kh[t]) for t in range(len(tokens))])
+            if len(tokens) == 0:
+                continue
+            w = np.exp(z - z.max())
+            w /= w.sum()
+            out[h] = w @ vh
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The whole decode step
+# ---------------------------------------------------------------------------
+def decode_step(batch, rows=None, scores_fp32: np.ndarray | None = None) -> dict:
+    """metadata -> scores -> selection -> table/ctx -> attention, for ``rows``
+    (default: all rows).
+
+    The selection is a floating-point decision; it is taken on float32 scores
+    (the precision of the device kernel's accumulator). ``scores_fp32`` lets a
+    caller pass the device's own float32 block scores so that the selection,
+    table and context lengths can be compared bit for bit."""
+    meta = build_metadata(batch.seq_lens, batch.query_lens)
+    N = len(meta["row_req"])
+    rows = list(range(N)) if rows is None else [int(r) for r in rows]
+    if scores_fp32 is None:
+        s64 = block_scores(batch.index_q, batch.index_k, batch.block_table, batch.seq_lens,
+                           batch.query_lens, batch.ld_s, rows=rows)
+        s32 = s64.astype(np.float32)
+    else:
+        s64 = None
+        s32 = np.asarray(scores_fp32, dtype=np.float32)
+    topk = batch.topk
+    sel_out = np.full((N, topk), -1, dtype=np.int64)
+    table = np.zeros((N, SUBS_PER_PAGE * topk), dtype=np.int64)
+    ctx = np.zeros(N, dtype=np.int64)
+    out = np.zeros((N, batch.num_q_heads, batch.q.shape[-1]), dtype=np.float64)
+    for n in rows:
+        r = int(meta["row_req"][n])
+        v = visible_keys(meta["row_pos"][n])
+        nb = num_blocks(v)
+        sel = select_blocks(s32[n].astype(np.float64), nb, topk)
+        sel_out[n] = selection_row_outputs(sel, topk)
+        table[n] = sparse_table_row(sel, batch.block_table[r], topk)
+        ctx[n] = context_length(sel, v)
+        out[n] = sparse_attention_row(batch.q[n], batch.k_cache, batch.v_cache, batch.kv_dtype,
+                                      batch.scale_mode, batch.k_scale, batch.v_scale,
+                                      batch.block_table[r], sel, v, batch.sm_scale)
+    return {"meta": meta, "scores": s64, "scores_fp32": s32, "sel": sel_out,
+            "table": table, "ctx": ctx, "out": out, "rows": rows}
+
+
+def attention_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows) -> np.ndarray:
+    """Attention for given rows driven by a page-16 table and context lengths
+    (the path's own contract: entry u // 16 of the row names the sub-page of
+    token u, slot u % 16). Used to check the device's attention on the device's
+    own table, so selection near-ties do not mix into attention error."""
+    out = np.zeros((len(rows), batch.num_q_heads, batch.q.shape[-1]), dtype=np.float64)
+    hkv_n = batch.k_cache.shape[2]
+    group = batch.num_q_heads // hkv_n
+    for i, n in enumerate(rows):
+        c = int(ctx[n])
+        q = bf16_to_f64(batch.q[n])
+        for g in range(hkv_n):
+            kh = np.empty((c, batch.k_cache.shape[-1]))
+            vh = np.empty((c, batch.v_cache.shape[-2]))
+            for u in range(c):
+                sub = int(table[n][u // SUB])
+                slot = u % SUB
+                ks = vs = 1.0
+                if batch.scale_mode == 1:
+                    ks = float(batch.k_scale.reshape(-1)[0])
+                    vs = float(batch.v_scale.reshape(-1)[0])
+                elif batch.scale_mode == 2:
+                    ks = float(batch.k_scale[sub, slot, g])
+                    vs = float(batch.v_scale[sub, slot, g])
+                dec = bf16_to_f64 if batch.kv_dtype == 0 else e4m3fn_to_f64
+                kh[u] = ks * dec(batch.k_cache[sub, slot, g, :])
+                vh[u] = vs * dec(batch.v_cache[sub, g, :, slot])
+            out[i, g * group:(g + 1) * group] = softmax_attention(
+                q[g * group:(g + 1) * group], kh, vh, batch.sm_scale)
+    return out

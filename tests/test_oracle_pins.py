@@ -1,0 +1,501 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Every check here ties an oracle function to a closed form, a brute-force
+enumeration, an independent library routine, a hand-derived fixture or an
+invariant of the mathematics, so that a dropped term, a wrong index or sign, or
+a transposed operand in the oracle fails at least one test. No GPU is used.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import msa_synth as syn
+from oracle import msa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers written independently of the oracle: a writer that scatters logical
+# per-token arrays into the paged layouts, and bf16 / fp8 encoders from torch
+# ---------------------------------------------------------------------------
+def bf16_bits(x):
+    t = torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def fp8_codes(x):
+    t = torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def write_paged(logical_k, logical_v, page_of_block, num_pages, dtype=np.uint16):
+    """Scatter logical K [T][Hkv][D] and V [T][Hkv][D] (already encoded) into
+    K sub-pages [8P][16][Hkv][D] (token-major) and V sub-pages [8P][Hkv][D][16]
+    (dim-major)."""
+    T, hkv, D = logical_k.shape
+    kc = np.zeros((num_pages * 8, 16, hkv, D), dtype=dtype)
+    vc = np.zeros((num_pages * 8, hkv, D, 16), dtype=dtype)
+    for t in range(T):
+        page = page_of_block[t // 128]
+        sub = page * 8 + (t % 128) // 16
+        kc[sub, t % 16] = logical_k[t]
+        for h in range(hkv):
+            vc[sub, h, :, t % 16] = logical_v[t, h]
+    return kc, vc
+
+
+def write_scales(logical_s, page_of_block, num_pages):
+    T, hkv = logical_s.shape
+    s = np.ones((num_pages * 8, 16, hkv), dtype=np.float32)
+    for t in range(T):
+        page = page_of_block[t // 128]
+        s[page * 8 + (t % 128) // 16, t % 16] = logical_s[t]
+    return s
+
+
+def write_index_pages(logical_ik, page_of_block, num_pages):
+    T, D = logical_ik.shape
+    out = np.zeros((num_pages, 128, D), dtype=np.uint16)
+    for t in range(T):
+        out[page_of_block[t // 128], t % 128] = logical_ik[t]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def test_bf16_decode_all_patterns_match_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = O.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+
+
+def test_e4m3fn_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3fn_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+    (0x38, 1.0), (0x39, 1.125), (0x40, 2.0), (0x7E, 448.0), (0xFE, -448.0),
+    (0xB8, -1.0), (0x77, 240.0),
+])
+def test_e4m3fn_spec_values(code, value):
+    # values fixed by the OCP 8-bit floating point specification (E4M3, bias 7)
+    assert O.e4m3fn_to_f64(np.array([code], np.uint8))[0] == value
+
+
+def test_e4m3fn_nan_and_negative_zero():
+    v = O.e4m3fn_to_f64(np.array([0x7F, 0xFF, 0x80], np.uint8))
+    assert math.isnan(v[0]) and math.isnan(v[1])
+    assert v[2] == 0.0 and math.copysign(1.0, v[2]) == -1.0
+
+
+# ---------------------------------------------------------------------------
+# metadata
+# ---------------------------------------------------------------------------
+def test_metadata_hand_derived_example():
+    g = json.load(open(os.path.join(GOLDEN, "metadata_example.json")))
+    m = O.build_metadata(np.array(g["seq_lens"]), np.array(g["query_lens"]))
+    for key in ("cu_seqlens_q", "cu_seqlens_k", "cu_blocks", "row_req", "row_pos"):
+        assert m[key].tolist() == g[key], key
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_metadata_invariants(seed):
+    rng = syn.SplitMix64(100 + seed)
+    R = int(rng.integers(1, 40, 1)[0])
+    L = rng.integers(0, 5000, R)
+    ql = np.minimum(rng.integers(0, 9, R), L)
+    m = O.build_metadata(L, ql)
+    # library prefix sums
+    assert m["cu_seqlens_k"].tolist() == [0] + np.cumsum(L).tolist()
+    assert m["cu_seqlens_q"].tolist() == [0] + np.cumsum(ql).tolist()
+    assert m["cu_blocks"].tolist() == [0] + np.cumsum(-(-L // 128)).tolist()
+    # every request's last row sits at position L-1, rows are contiguous per request
+    for r in range(R):
+        rows = np.nonzero(m["row_req"] == r)[0]
+        assert len(rows) == ql[r]
+        if ql[r]:
+            assert rows.tolist() == list(range(m["cu_seqlens_q"][r], m["cu_seqlens_q"][r + 1]))
+            assert m["row_pos"][rows[-1]] == L[r] - 1
+            assert np.all(np.diff(m["row_pos"][rows]) == 1)
+
+
+def test_metadata_prefill_slice_matches_page_formula():
+    # the prefill metadata of the PR #56170 page is the prefill part of the
+    # batch: cu_seqlens_q = query_start_loc[num_decodes:] - num_decode_tokens and
+    # cu_seqlens_k = [0, cumsum(seq_lens[num_decodes:])]
+    L = np.array([16384] * 6 + [32768, 5000])
+    ql = np.array([1] * 6 + [4096, 17])
+    nd = 6
+    m = O.build_metadata(L, ql)
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    assert (m["cu_seqlens_q"][nd:] - m["cu_seqlens_q"][nd]).tolist() == (qsl[nd:] - qsl[nd]).tolist()
+    pf = np.empty(len(L) - nd + 1, dtype=np.int64)
+    pf[:1] = 0
+    np.cumsum(L[nd:], out=pf[1:])
+    assert (m["cu_seqlens_k"][nd:] - m["cu_seqlens_k"][nd]).tolist() == pf.tolist()
+    ctx = L - ql
+    first_prefill_row = int(qsl[nd])
+    assert m["row_pos"][first_prefill_row] == ctx[nd]
+
+
+# ---------------------------------------------------------------------------
+# scores and pooling
+# ---------------------------------------------------------------------------
+def _one_request(seed, L, nreq_pages_extra=3):
+    rng = syn.SplitMix64(seed)
+    nb = -(-L // 128)
+    P = nb + nreq_pages_extra
+    pages = rng.permutation(P)[:nb]
+    logical = syn.bf16_normal(rng, (L, 128))
+    ik = write_index_pages(logical, pages, P)
+    return pages, logical, ik
+
+
+def test_scores_one_hot_query_reads_one_coordinate():
+    L = 300
+    pages, logical, ik = _one_request(1, L)
+    for d in (0, 37, 127):
+        q = np.zeros(128, np.float32)
+        q[d] = 1.0
+        keys = O.index_keys_of_request(ik, pages, L)
+        s = O.token_scores(bf16_bits(q), keys, L)
+        np.testing.assert_array_equal(s, O.bf16_to_f64(logical[:, d]))
+
+
+def test_scores_all_ones_equal_dim():
+    L = 200
+    ik = np.full((2, 128, 128), bf16_bits([1.0])[0], np.uint16)
+    keys = O.index_keys_of_request(ik, np.array([1, 0]), L)
+    s = O.token_scores(bf16_bits(np.ones(128)), keys, L)
+    assert np.all(s == 128.0)
+
+
+def test_scores_brute_force_tiny():
+    L = 150
+    pages, logical, ik = _one_request(2, L)
+    rng = syn.SplitMix64(3)
+    q = syn.bf16_normal(rng, (128,))
+    keys = O.index_keys_of_request(ik, pages, L)
+    s = O.token_scores(q, keys, L)
+    qf = [float(x) for x in torch.from_numpy(q.view(np.int16).copy()).view(torch.bfloat16).float()]
+    for t in range(L):
+        page = int(pages[t // 128])
+        row = torch.from_numpy(ik[page, t % 128].view(np.int16).copy()).view(torch.bfloat16).float()
+        ref = math.fsum(qf[d] * float(row[d]) for d in range(128))
+        assert abs(s[t] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_scores_invariant_under_page_permutation():
+    L = 700
+    rng = syn.SplitMix64(4)
+    logical = syn.bf16_normal(rng, (L, 128))
+    q = syn.bf16_normal(rng, (128,))
+    nb = -(-L // 128)
+    outs = []
+    for seed in (5, 6):
+        pages = syn.SplitMix64(seed).permutation(nb + 2)[:nb]
+        ik = write_index_pages(logical, pages, nb + 2)
+        outs.append(O.token_scores(q, O.index_keys_of_request(ik, pages, L), L))
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_pool_planted_maxima_and_partial_block():
+    L = 3 * 128 + 10           # 4 blocks, the last one partial
+    rng = syn.SplitMix64(7)
+    logical = bf16_bits(0.01 * O.bf16_to_f64(syn.bf16_normal(rng, (L + 118, 128))))
+    q = np.zeros(128, np.float32)
+    q[5] = 1.0
+    # values at block edges catch a pooled range that is off by one at either end
+    planted = {0: (17, 3.0), 1: (128, 5.0), 2: (383, 4.0), 3: (384 + 9, 2.5)}
+    for b, (t, val) in planted.items():
+        logical[t, 5] = bf16_bits([val])[0]
+    # a huge value in the invisible tail of block 3 must not be pooled
+    logical[384 + 50, 5] = bf16_bits([100.0])[0]
+    pages = np.array([3, 0, 2, 1])
+    ik = write_index_pages(logical, pages, 4)
+    keys = O.index_keys_of_request(ik, pages, L + 118)
+    s = O.token_scores(bf16_bits(q), keys, L)
+    pooled = O.pool_blocks(s, 4)
+    assert pooled.tolist() == [3.0, 5.0, 4.0, 2.5]
+
+
+def test_block_scores_tail_is_minus_inf_and_rows_follow_positions():
+    b = syn.make_batch("t", 9, seq_lens=[300, 129], query_lens=[3, 2], topk=2, num_q_heads=16,
+                       max_seq_len=1024)
+    s = O.block_scores(b.index_q, b.index_k, b.block_table, b.seq_lens, b.query_lens, b.ld_s)
+    # request 0 rows at pos 297, 298, 299 -> 3 blocks; request 1 rows at 127, 128 -> 1, 2 blocks
+    nbs = [3, 3, 3, 1, 2]
+    for n, nb in enumerate(nbs):
+        assert np.all(np.isfinite(s[n, :nb]))
+        assert np.all(s[n, nb:] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# selection, table, context length
+# ---------------------------------------------------------------------------
+def test_table_and_ctx_hand_derived_cases():
+    g = json.load(open(os.path.join(GOLDEN, "table_example.json")))
+    for c in g["cases"]:
+        nb = O.num_blocks(c["v"])
+        sel = O.select_blocks(np.array(c["scores"]), nb, c["topk"])
+        assert O.selection_row_outputs(sel, c["topk"]).tolist()[:len(c["sel"])] == c["sel"]
+        tab = O.sparse_table_row(sel, np.array(c["bt_row"]), c["topk"])
+        assert len(tab) == 8 * c["topk"]
+        assert tab.tolist()[:len(c["table"])] == c["table"]
+        assert np.all(tab[len(c["table"]):] == 0)
+        assert O.context_length(sel, c["v"]) == c["ctx"]
+
+
+def _greedy_select(scores, nb, topk):
+    # brute force: repeatedly extract the best remaining block (max score, then
+    # lowest id), then list the extracted ids in ascending order
+    left = list(range(nb))
+    got = []
+    for _ in range(min(topk, nb)):
+        best = left[0]
+        for b in left[1:]:
+            if scores[b] > scores[best]:
+                best = b
+        got.append(best)
+        left.remove(best)
+    return sorted(got)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_selection_formulations_agree(seed):
+    rng = syn.SplitMix64(200 + seed)
+    nb = int(rng.integers(1, 70, 1)[0])
+    topk = int(rng.integers(1, 80, 1)[0])
+    mode = seed % 3
+    if mode == 0:
+        s = rng.normal(nb)
+    elif mode == 1:                       # heavy ties
+        s = np.round(rng.normal(nb) * 2) / 2
+    else:                                 # signed zeros and a few values
+        s = np.where(rng.uniform(nb) < 0.5, 0.0, -0.0)
+        s[rng.integers(0, nb - 1, 3)] = 1.0
+    a = O.select_blocks(s, nb, topk)
+    b = O.select_blocks_by_rank(s, nb, topk)
+    c = _greedy_select(s, nb, topk)
+    assert a.tolist() == b.tolist() == c
+    assert len(a) == min(topk, nb)
+
+
+def test_selection_all_signed_zeros_picks_lowest_ids():
+    s = np.array([-0.0, 0.0, -0.0, 0.0, 0.0, -0.0])
+    assert O.select_blocks(s, 6, 4).tolist() == [0, 1, 2, 3]
+
+
+def test_selection_ignores_scores_past_nb():
+    s = np.array([1.0, 2.0, 3.0, 99.0, 98.0])
+    assert O.select_blocks(s, 3, 2).tolist() == [1, 2]
+
+
+def test_table_never_exceeds_width_and_encodes_subpages():
+    rng = syn.SplitMix64(11)
+    for _ in range(20):
+        nb = int(rng.integers(1, 30, 1)[0])
+        topk = int(rng.integers(1, 40, 1)[0])
+        bt = rng.permutation(nb + 5)[:nb]
+        sel = O.select_blocks(rng.normal(nb), nb, topk)
+        tab = O.sparse_table_row(sel, bt, topk)
+        assert tab.shape == (8 * topk,)
+        for j, blk in enumerate(sel):
+            assert (tab[8 * j:8 * j + 8] // 8 == bt[blk]).all()
+            assert (tab[8 * j:8 * j + 8] % 8 == np.arange(8)).all()
+        assert (tab[8 * len(sel):] == 0).all()
+
+
+def test_ctx_all_blocks_equals_visible_keys():
+    for v in (1, 127, 128, 129, 1000, 4096):
+        nb = O.num_blocks(v)
+        assert O.context_length(np.arange(nb), v) == v
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def _paged_kv_case(seed, L, hq=8, kv_fp8=False, per_token_scales=False):
+    rng = syn.SplitMix64(seed)
+    nb = -(-L // 128)
+    P = nb + 2
+    pages = rng.permutation(P)[:nb]
+    if kv_fp8:
+        kl = syn.fp8_normal(rng, (L, 1, 128))
+        vl = syn.fp8_normal(rng, (L, 1, 128))
+        kc, vc = write_paged(kl, vl, pages, P, dtype=np.uint8)
+        kf = torch.from_numpy(kl.copy()).view(torch.float8_e4m3fn).double().numpy()
+        vf = torch.from_numpy(vl.copy()).view(torch.float8_e4m3fn).double().numpy()
+    else:
+        kl = syn.bf16_normal(rng, (L, 1, 128))
+        vl = syn.bf16_normal(rng, (L, 1, 128))
+        kc, vc = write_paged(kl, vl, pages, P)
+        kf = torch.from_numpy(kl.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+        vf = torch.from_numpy(vl.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    ks = vs = None
+    mode = 0
+    if per_token_scales:
+        mode = 2
+        ksl = (0.5 + 1.5 * rng.uniform(L)).astype(np.float32).reshape(L, 1)
+        vsl = (0.5 + 1.5 * rng.uniform(L)).astype(np.float32).reshape(L, 1)
+        ks = write_scales(ksl, pages, P)
+        vs = write_scales(vsl, pages, P)
+        kf = kf * ksl.astype(np.float64)[:, :, None]
+        vf = vf * vsl.astype(np.float64)[:, :, None]
+    q = syn.bf16_normal(rng, (hq, 128))
+    qf = torch.from_numpy(q.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    return dict(pages=pages, kc=kc, vc=vc, ks=ks, vs=vs, mode=mode, q=q, qf=qf, kf=kf, vf=vf,
+                dtype=1 if kv_fp8 else 0)
+
+
+def _sdpa(qf, kf, vf, v, scale):
+    # library routine: torch's scaled-dot-product attention on the logical arrays
+    q = torch.from_numpy(qf)[None, :, None, :]                          # [1,H,1,D]
+    k = torch.from_numpy(kf[:v, 0, :]).expand(qf.shape[0], v, 128)[None]
+    vv = torch.from_numpy(vf[:v, 0, :]).expand(qf.shape[0], v, 128)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, vv, scale=scale)
+    return o[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("fp8,pth", [(False, False), (True, False), (True, True)])
+def test_dense_attention_matches_torch_sdpa_through_paged_layout(fp8, pth):
+    L = 333
+    c = _paged_kv_case(20, L, kv_fp8=fp8, per_token_scales=pth)
+    sc = 1 / math.sqrt(128)
+    got = O.dense_causal_attention_row(c["q"], c["kc"], c["vc"], c["dtype"], c["mode"], c["ks"],
+                                       c["vs"], c["pages"], L, sc)
+    np.testing.assert_allclose(got, _sdpa(c["qf"], c["kf"], c["vf"], L, sc), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fp8,pth", [(False, False), (True, True)])
+def test_sparse_with_all_blocks_equals_dense(fp8, pth):
+    L = 600
+    c = _paged_kv_case(21, L, kv_fp8=fp8, per_token_scales=pth)
+    nb = O.num_blocks(L)
+    sc = 1 / math.sqrt(128)
+    for v in (L, 513, 130, 1):
+        sel = O.select_blocks(np.zeros(nb), O.num_blocks(v), nb + 3)
+        a = O.sparse_attention_row(c["q"], c["kc"], c["vc"], c["dtype"], c["mode"], c["ks"], c["vs"],
+                                   c["pages"], sel, v, sc)
+        d = O.dense_causal_attention_row(c["q"], c["kc"], c["vc"], c["dtype"], c["mode"], c["ks"],
+                                         c["vs"], c["pages"], v, sc)
+        np.testing.assert_allclose(a, d, rtol=0, atol=1e-12)
+
+
+def test_sparse_attention_matches_sdpa_on_selected_tokens():
+    L = 900
+    c = _paged_kv_case(22, L)
+    sel = np.array([1, 4, 7])                 # block 7 is partial: tokens 896..899
+    sc = 0.07
+    got = O.sparse_attention_row(c["q"], c["kc"], c["vc"], 0, 0, None, None, c["pages"], sel, L, sc)
+    toks = [t for b in sel for t in range(128 * b, min(128 * b + 128, L))]
+    ref = _sdpa(c["qf"], c["kf"][toks], c["vf"][toks], len(toks), sc)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_zero_query_is_mean_of_values():
+    L = 300
+    c = _paged_kv_case(23, L)
+    q0 = bf16_bits(np.zeros((8, 128)))
+    sel = np.array([0, 2])
+    got = O.sparse_attention_row(q0, c["kc"], c["vc"], 0, 0, None, None, c["pages"], sel, L, 0.1)
+    toks = list(range(0, 128)) + list(range(256, 300))
+    mean = c["vf"][toks, 0, :].mean(axis=0)
+    np.testing.assert_allclose(got, np.broadcast_to(mean, got.shape), rtol=0, atol=1e-12)
+
+
+def test_attention_constant_values_and_single_key():
+    L = 200
+    c = _paged_kv_case(24, L)
+    vc = np.full_like(c["vc"], bf16_bits([1.75])[0])
+    got = O.sparse_attention_row(c["q"], c["kc"], vc, 0, 0, None, None, c["pages"], np.array([0, 1]), L, 0.1)
+    assert np.all(np.abs(got - 1.75) < 1e-12)
+    one = O.sparse_attention_row(c["q"], c["kc"], c["vc"], 0, 0, None, None, c["pages"], np.array([0]), 1, 0.1)
+    np.testing.assert_array_equal(one, np.broadcast_to(c["vf"][0, 0], one.shape))
+
+
+def test_online_softmax_agrees_with_two_pass():
+    L = 500
+    c = _paged_kv_case(25, L)
+    sc = 1 / math.sqrt(128)
+    ref = O.sparse_attention_row(c["q"], c["kc"], c["vc"], 0, 0, None, None, c["pages"],
+                                 np.arange(4), L, sc)
+    # streaming (online) softmax over 16-token chunks, float64
+    m = np.full(8, -np.inf)
+    l = np.zeros(8)
+    acc = np.zeros((8, 128))
+    for s in range(0, L, 16):
+        kk = c["kf"][s:min(s + 16, L), 0]
+        vv = c["vf"][s:min(s + 16, L), 0]
+        z = sc * c["qf"] @ kk.T
+        mn = np.maximum(m, z.max(axis=1))
+        a = np.exp(m - mn)
+        p = np.exp(z - mn[:, None])
+        l = l * a + p.sum(axis=1)
+        acc = acc * a[:, None] + p @ vv
+        m = mn
+    np.testing.assert_allclose(acc / l[:, None], ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_scalar_equals_constant_per_token_head():
+    L = 260
+    c = _paged_kv_case(26, L, kv_fp8=True)
+    P8 = c["kc"].shape[0]
+    sel = np.array([0, 2])
+    a = O.sparse_attention_row(c["q"], c["kc"], c["vc"], 1, 1, np.array([1.5], np.float32),
+                               np.array([0.75], np.float32), c["pages"], sel, L, 0.09)
+    b = O.sparse_attention_row(c["q"], c["kc"], c["vc"], 1, 2, np.full((P8, 16, 1), 1.5, np.float32),
+                               np.full((P8, 16, 1), 0.75, np.float32), c["pages"], sel, L, 0.09)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_fp8_power_of_two_scale_equals_bf16_of_scaled_values():
+    # e4m3 values times a power of two are exact in bf16, so the fp8 path with
+    # scale 2^k must equal the bf16 path on the bf16 encoding of 2^k * value
+    L = 300
+    c = _paged_kv_case(27, L, kv_fp8=True)
+    kf = torch.from_numpy(c["kc"].copy()).view(torch.float8_e4m3fn).float() * 4.0
+    vf = torch.from_numpy(c["vc"].copy()).view(torch.float8_e4m3fn).float() * 0.5
+    kb = kf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vb = vf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    sel = np.array([0, 1, 2])
+    a = O.sparse_attention_row(c["q"], c["kc"], c["vc"], 1, 1, np.array([4.0], np.float32),
+                               np.array([0.5], np.float32), c["pages"], sel, L, 0.05)
+    b = O.sparse_attention_row(c["q"], kb, vb, 0, 0, None, None, c["pages"], sel, L, 0.05)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_table_walk_equals_logical_walk():
+    b = syn.make_batch("t", 30, seq_lens=[1000, 260], query_lens=[2, 1], topk=3, num_q_heads=16,
+                       kv_dtype=syn.KV_FP8, scale_mode=syn.SCALE_PER_TOKEN_HEAD)
+    res = O.decode_step(b)
+    via_table = O.attention_from_table(b, res["table"], res["ctx"], res["rows"])
+    np.testing.assert_allclose(via_table, res["out"], rtol=0, atol=1e-13)
+
+
+def test_decode_step_chain_on_tiny_workload():
+    b = syn.config("tiny")
+    res = O.decode_step(b)
+    assert res["ctx"][0] == 4 * 128
+    sel = res["sel"][0]
+    assert len(sel) == 4 and (np.diff(sel) > 0).all()
+    # the kept blocks beat every other block
+    s = res["scores_fp32"][0]
+    others = [x for x in range(16) if x not in sel]
+    assert s[sel].min() >= s[others].max()
+    assert res["table"][0].tolist() == [8 * int(blk) + i for blk in sel for i in range(8)]
