@@ -1,0 +1,304 @@
+// Host side of the C ABI declared in include/msa.h: argument validation,
+// launch policy (grid sizes from host-known bounds and the device's compute
+// unit count), workspace layout and the stream-ordered launches. No call here
+// allocates, copies between host and device, or synchronises.
+#include <atomic>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+using msa::kDim;
+using msa::kHeadTile;
+using msa::kPage;
+using msa::kRowsPerUnit;
+using msa::kSub;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Attention split policy: the smallest split (a multiple of 128 tokens) whose
+// workgroup count stays within two workgroups per compute unit, so that short
+// batches still spread over the whole chip while long ones keep few partials.
+struct AttnPlan {
+  int hgroups;
+  int split_tok;
+  int nsplit;
+};
+
+AttnPlan attn_plan(int num_rows, int num_q_heads, int max_ctx) {
+  AttnPlan p;
+  p.hgroups = static_cast<int>(ceil_div(num_q_heads, kHeadTile));
+  const int64_t ctx = max_ctx < 1 ? 1 : max_ctx;
+  const int64_t target = 2LL * cu_count();
+  int64_t split = 128;
+  while (split < ctx && static_cast<int64_t>(num_rows) * p.hgroups * ceil_div(ctx, split) > target) split *= 2;
+  p.split_tok = static_cast<int>(split);
+  p.nsplit = static_cast<int>(ceil_div(ctx, split));
+  return p;
+}
+
+struct WsLayout {
+  size_t counters, partials, scores, total;
+};
+
+WsLayout ws_layout(int num_rows, int num_q_heads, int max_ctx, int ld_s) {
+  const AttnPlan p = attn_plan(num_rows, num_q_heads, max_ctx);
+  WsLayout w;
+  size_t off = 0;
+  w.counters = off;
+  off += align256(sizeof(int32_t) * static_cast<size_t>(num_rows) * p.hgroups);
+  w.partials = off;
+  if (p.nsplit > 1)
+    off += align256(sizeof(float) * static_cast<size_t>(num_rows) * p.hgroups * p.nsplit *
+                    (2 * kHeadTile + kHeadTile * kDim));
+  w.scores = off;
+  if (ld_s > 0) off += align256(sizeof(float) * static_cast<size_t>(num_rows) * ld_s);
+  w.total = off;
+  return w;
+}
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+msa_status check_batch(const msa_batch* b, bool need_meta_outputs) {
+  if (!b) return MSA_ERR_INVALID_ARG;
+  if (b->num_reqs < 0 || b->num_rows < 0 || b->max_seq_len < 0) return MSA_ERR_INVALID_ARG;
+  if (b->num_reqs > MSA_MAX_REQS) return MSA_ERR_UNSUPPORTED;
+  if (b->num_rows > 0 && b->num_reqs == 0) return MSA_ERR_INVALID_ARG;
+  if (b->num_reqs == 0) return MSA_OK;
+  if (b->ld_bt < 1 || b->num_pages < 1) return MSA_ERR_INVALID_ARG;
+  if (!b->seq_lens || !b->query_lens || !b->block_table) return MSA_ERR_INVALID_ARG;
+  if (need_meta_outputs && (!b->cu_seqlens_q || !b->cu_seqlens_k || !b->cu_blocks || !b->cu_units))
+    return MSA_ERR_INVALID_ARG;
+  if (need_meta_outputs && b->num_rows > 0 && (!b->row_req || !b->row_pos)) return MSA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(b->num_pages) * msa::kSubsPerPage * kSub * kDim > (1LL << 40)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+int blocks_bound(const msa_batch* b) { return static_cast<int>(ceil_div(b->max_seq_len, kPage)); }
+
+msa_status check_kv(const msa_kv* kv) {
+  if (!kv || !kv->k_cache || !kv->v_cache) return MSA_ERR_INVALID_ARG;
+  if (kv->kv_dtype != MSA_KV_BF16 && kv->kv_dtype != MSA_KV_FP8_E4M3FN) return MSA_ERR_INVALID_ARG;
+  if (kv->scale_mode < MSA_SCALE_NONE || kv->scale_mode > MSA_SCALE_PER_TOKEN_HEAD) return MSA_ERR_INVALID_ARG;
+  if (kv->num_pages < 1) return MSA_ERR_INVALID_ARG;
+  if (kv->num_kv_heads != 1) return MSA_ERR_UNSUPPORTED;
+  if (kv->kv_dtype == MSA_KV_FP8_E4M3FN && kv->scale_mode == MSA_SCALE_NONE) return MSA_ERR_UNSUPPORTED;
+  if (kv->scale_mode != MSA_SCALE_NONE && (!kv->k_scale || !kv->v_scale)) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+MsaMetaArgs meta_args(const msa_batch* b, int32_t* zero_ptr, int64_t zero_count) {
+  MsaMetaArgs m;
+  m.seq_lens = b->seq_lens;
+  m.query_lens = b->query_lens;
+  m.cu_q = b->cu_seqlens_q;
+  m.cu_k = b->cu_seqlens_k;
+  m.cu_blocks = b->cu_blocks;
+  m.cu_units = b->cu_units;
+  m.row_req = b->row_req;
+  m.row_pos = b->row_pos;
+  m.zero_ptr = zero_ptr;
+  m.zero_count = zero_count;
+  m.num_reqs = b->num_reqs;
+  m.num_rows = b->num_rows;
+  const int64_t cap = static_cast<int64_t>(kPage) * b->ld_bt;
+  m.len_cap = static_cast<int32_t>(cap < b->max_seq_len ? cap : b->max_seq_len);
+  return m;
+}
+
+msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, const void* index_k,
+                        float* scores, int32_t ld_s) {
+  MsaScoreArgs a;
+  a.index_q = static_cast<const uint16_t*>(index_q);
+  a.index_k = static_cast<const uint16_t*>(index_k);
+  a.block_table = b->block_table;
+  a.cu_q = b->cu_seqlens_q;
+  a.cu_k = b->cu_seqlens_k;
+  a.cu_units = b->cu_units;
+  a.scores = scores;
+  a.ld_s = ld_s;
+  a.ld_bt = b->ld_bt;
+  a.num_reqs = b->num_reqs;
+  a.num_rows = b->num_rows;
+  a.num_pages = b->num_pages;
+  // units <= blocks_bound * sum_r ceil(ql_r/64) <= blocks_bound * (R + ceil(N/64))
+  const int64_t units = static_cast<int64_t>(blocks_bound(b)) * (b->num_reqs + ceil_div(b->num_rows, kRowsPerUnit));
+  int64_t wgs = ceil_div(units, 4);
+  const int64_t cap = 8LL * cu_count();
+  if (wgs > cap) wgs = cap;
+  if (wgs < 1) wgs = 1;
+  return hip_status(msa_launch_score(a, static_cast<int>(wgs), s));
+}
+
+msa_status launch_topk(hipStream_t s, const msa_batch* b, const float* scores, int32_t ld_s, int32_t topk,
+                       int32_t* table, int32_t* ctx, int32_t* sel) {
+  MsaTopkArgs a;
+  a.scores = scores;
+  a.block_table = b->block_table;
+  a.row_req = b->row_req;
+  a.row_pos = b->row_pos;
+  a.table = table;
+  a.ctx = ctx;
+  a.sel = sel;
+  a.ld_s = ld_s;
+  a.ld_bt = b->ld_bt;
+  a.topk = topk;
+  a.num_rows = b->num_rows;
+  a.num_reqs = b->num_reqs;
+  return hip_status(msa_launch_topk(a, s));
+}
+
+msa_status launch_attn(hipStream_t s, const void* q, int32_t num_rows, int32_t num_q_heads, const msa_kv* kv,
+                       const int32_t* table, int32_t ld_table, const int32_t* ctx, int32_t max_ctx,
+                       float sm_scale, void* out, void* ws, bool zero_counters) {
+  const AttnPlan p = attn_plan(num_rows, num_q_heads, max_ctx);
+  const WsLayout w = ws_layout(num_rows, num_q_heads, max_ctx, 0);
+  MsaAttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = kv->k_cache;
+  a.v_cache = kv->v_cache;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
+  a.table = table;
+  a.ctx = ctx;
+  a.out = static_cast<uint16_t*>(out);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + w.partials);
+  a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.counters);
+  a.num_rows = num_rows;
+  a.num_q_heads = num_q_heads;
+  a.num_hgroups = p.hgroups;
+  a.ld_table = ld_table;
+  a.max_ctx = max_ctx;
+  a.split_tok = p.split_tok;
+  a.nsplit = p.nsplit;
+  a.num_subpages = kv->num_pages * msa::kSubsPerPage;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  if (zero_counters && p.nsplit > 1) {
+    hipError_t e = msa_launch_zero(a.counters, static_cast<int64_t>(num_rows) * p.hgroups, s);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+  }
+  return hip_status(msa_launch_attn(a, kv->kv_dtype, kv->scale_mode, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch) {
+  msa_status st = check_batch(batch, true);
+  if (st != MSA_OK) return st;
+  if (batch->num_reqs == 0) return MSA_OK;
+  return hip_status(msa_launch_meta(meta_args(batch, nullptr, 0), static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_index_score(msa_stream_t stream, const msa_batch* batch, const void* index_q, const void* index_k,
+                           float* block_scores, int32_t ld_s) {
+  msa_status st = check_batch(batch, true);
+  if (st != MSA_OK) return st;
+  if (batch->num_rows == 0) return MSA_OK;
+  if (!index_q || !index_k || !block_scores) return MSA_ERR_INVALID_ARG;
+  if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
+  return launch_score(static_cast<hipStream_t>(stream), batch, index_q, index_k, block_scores, ld_s);
+}
+
+msa_status msa_topk_block_table(msa_stream_t stream, const msa_batch* batch, const float* block_scores,
+                                int32_t ld_s, int32_t topk, int32_t* sparse_table, int32_t* ctx_lens,
+                                int32_t* sel_blocks) {
+  msa_status st = check_batch(batch, true);
+  if (st != MSA_OK) return st;
+  if (topk < 1) return MSA_ERR_INVALID_ARG;
+  if (topk > MSA_MAX_TOPK) return MSA_ERR_UNSUPPORTED;
+  if (batch->num_rows == 0) return MSA_OK;
+  if (!block_scores || !sparse_table || !ctx_lens) return MSA_ERR_INVALID_ARG;
+  if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
+  return launch_topk(static_cast<hipStream_t>(stream), batch, block_scores, ld_s, topk, sparse_table, ctx_lens,
+                     sel_blocks);
+}
+
+msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num_rows, int32_t num_q_heads,
+                                 const msa_kv* kv, const int32_t* sparse_table, int32_t ld_table,
+                                 const int32_t* ctx_lens, int32_t max_ctx, float sm_scale, void* out,
+                                 void* workspace, size_t workspace_bytes) {
+  if (num_rows < 0 || max_ctx < 0 || ld_table < 0) return MSA_ERR_INVALID_ARG;
+  if (num_q_heads < 1) return MSA_ERR_INVALID_ARG;
+  if (num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
+  msa_status st = check_kv(kv);
+  if (st != MSA_OK) return st;
+  if (num_rows == 0) return MSA_OK;
+  if (!q || !sparse_table || !ctx_lens || !out) return MSA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(ld_table) * kSub < max_ctx || ld_table < 1) return MSA_ERR_INVALID_ARG;
+  const WsLayout w = ws_layout(num_rows, num_q_heads, max_ctx, 0);
+  if (!workspace || workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
+  return launch_attn(static_cast<hipStream_t>(stream), q, num_rows, num_q_heads, kv, sparse_table, ld_table,
+                     ctx_lens, max_ctx, sm_scale, out, workspace, true);
+}
+
+msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q, const void* index_k,
+                             const void* q, int32_t num_q_heads, const msa_kv* kv, int32_t topk, float sm_scale,
+                             void* out, int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
+                             float* block_scores, int32_t ld_s, void* workspace, size_t workspace_bytes) {
+  msa_status st = check_batch(batch, true);
+  if (st != MSA_OK) return st;
+  st = check_kv(kv);
+  if (st != MSA_OK) return st;
+  if (topk < 1 || num_q_heads < 1) return MSA_ERR_INVALID_ARG;
+  if (topk > MSA_MAX_TOPK || num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (batch->num_rows == 0) return batch->num_reqs ? msa_build_metadata(stream, batch) : MSA_OK;
+  if (!index_q || !index_k || !q || !out || !sparse_table || !ctx_lens) return MSA_ERR_INVALID_ARG;
+  if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
+  if (kv->num_pages != batch->num_pages) return MSA_ERR_INVALID_ARG;
+  const int32_t max_ctx = kPage * topk;
+  const WsLayout w = ws_layout(batch->num_rows, num_q_heads, max_ctx, block_scores ? 0 : ld_s);
+  if (!workspace || workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
+  const AttnPlan p = attn_plan(batch->num_rows, num_q_heads, max_ctx);
+  // metadata + zeroed split counters, in one launch
+  st = hip_status(msa_launch_meta(
+      meta_args(batch, reinterpret_cast<int32_t*>(ws + w.counters), static_cast<int64_t>(batch->num_rows) * p.hgroups),
+      s));
+  if (st != MSA_OK) return st;
+  st = launch_score(s, batch, index_q, index_k, scores, ld_s);
+  if (st != MSA_OK) return st;
+  st = launch_topk(s, batch, scores, ld_s, topk, sparse_table, ctx_lens, sel_blocks);
+  if (st != MSA_OK) return st;
+  return launch_attn(s, q, batch->num_rows, num_q_heads, kv, sparse_table, 8 * topk, ctx_lens, max_ctx, sm_scale,
+                     out, workspace, false);
+}
+
+size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ctx, int32_t ld_s) {
+  if (num_rows < 0 || num_q_heads < 1 || max_ctx < 0 || ld_s < 0) return 0;
+  return ws_layout(num_rows, num_q_heads, max_ctx, ld_s).total;
+}
+
+const char* msa_status_string(msa_status status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+int32_t msa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Internal declarations shared by the library's HIP sources: vector types,
+// number-format helpers, MFMA wrappers, wave/block reductions and the kernel
+// launchers that msa_api.hip calls. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kPage = 128;        // tokens per page-128 page / sparse block
+constexpr int kSub = 16;          // tokens per page-16 sub-page
+constexpr int kSubsPerPage = 8;   // sub-pages per page
+constexpr int kDim = 128;         // head dim and index dim
+constexpr int kRowsPerUnit = 64;  // query rows of one request per score unit
+constexpr int kHeadTile = 16;     // query heads per attention MFMA tile
+constexpr int kMaxReqs = 8192;    // requests per batch (LDS-resident prefix)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Four e4m3fn codes (one dword) -> four bf16 values packed in two dwords.
+// e4m3 values are exactly representable in bf16, so taking the top half of
+// the exact fp32 conversion is exact.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  u32x2 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  return r;
+}
+
+// D = A(16x32) * B(32x16) + C; lane l supplies A row l%16 / B column l%16 and
+// eight consecutive K entries selected by l/16; D lane l holds rows 4*(l/16)+i
+// of column l%16.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same with K = 16: four K entries per lane.
+__device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max16(float v) {  // max over the 16 lanes of a row
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+__device__ __forceinline__ float max_across_rows(float v) {  // lanes l, l^16, l^32, l^48
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float sum_across_rows(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exclusive prefix sum over a 256-thread block; `scratch` holds 4 ints.
+__device__ __forceinline__ int block256_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int t = scratch[w];
+    base += (w < wave) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace msa
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (host functions defined next to each kernel).
+// ---------------------------------------------------------------------------
+struct MsaMetaArgs {
+  const int32_t* seq_lens;
+  const int32_t* query_lens;
+  int32_t* cu_q;
+  int32_t* cu_k;
+  int32_t* cu_blocks;
+  int32_t* cu_units;
+  int32_t* row_req;
+  int32_t* row_pos;
+  int32_t* zero_ptr;   // optional int32 region cleared by the same launch
+  int64_t zero_count;
+  int32_t num_reqs;
+  int32_t num_rows;
+  int32_t len_cap;     // seq_lens are clamped to [0, len_cap]
+};
+hipError_t msa_launch_meta(const MsaMetaArgs& a, hipStream_t s);
+hipError_t msa_launch_zero(int32_t* p, int64_t count, hipStream_t s);
+
+struct MsaScoreArgs {
+  const uint16_t* index_q;
+  const uint16_t* index_k;
+  const int32_t* block_table;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* cu_units;
+  float* scores;
+  int32_t ld_s;
+  int32_t ld_bt;
+  int32_t num_reqs;
+  int32_t num_rows;
+  int32_t num_pages;
+};
+hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s);
+
+struct MsaTopkArgs {
+  const float* scores;
+  const int32_t* block_table;
+  const int32_t* row_req;
+  const int32_t* row_pos;
+  int32_t* table;
+  int32_t* ctx;
+  int32_t* sel;        // may be null
+  int32_t ld_s;
+  int32_t ld_bt;
+  int32_t topk;
+  int32_t num_rows;
+  int32_t num_reqs;
+};
+hipError_t msa_launch_topk(const MsaTopkArgs& a, hipStream_t s);
+
+struct MsaAttnArgs {
+  const uint16_t* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* table;
+  const int32_t* ctx;
+  uint16_t* out;
+  float* partials;     // [rows][hgroups][nsplit][16*2 + 16*128]
+  int32_t* counters;   // [rows][hgroups], zero on entry, zero on exit
+  int32_t num_rows;
+  int32_t num_q_heads;
+  int32_t num_hgroups;
+  int32_t ld_table;
+  int32_t max_ctx;
+  int32_t split_tok;   // tokens per workgroup, a multiple of 64
+  int32_t nsplit;      // ceil(max_ctx / split_tok)
+  int32_t num_subpages;
+  float scale_log2;    // sm_scale * log2(e)
+};
+hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, hipStream_t s);

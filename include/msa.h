@@ -1,0 +1,226 @@
+/*
+ * msa.h — C ABI of the block-sparse paged decode-attention library for AMD
+ * MI355X (gfx950).
+ *
+ * The method (MiniMax-M3-style sparse attention) is described on the
+ * prhub.com.cn summaries of vLLM pull requests, cited below by PR number and the
+ * page's own section names:
+ *   #47287  ROCm AITER sparse paged attention for MiniMax-M3
+ *   #54682  gfx950 decode index scoring and top-k
+ *   #56170  cu_seqlens_k first element zeroed on the device
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns every
+ *     buffer, including the workspace; the library allocates nothing and keeps
+ *     no state except a per-device cached compute-unit count.
+ *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return. They never copy between host and device and never
+ *     synchronise, so they can be captured into a HIP graph.
+ *   - Host-checkable problems (null required pointer, unsupported shape, small
+ *     workspace) return an error status and enqueue nothing.
+ *   - Device data is not validated, but every kernel clamps what it reads from
+ *     device arrays (lengths, table entries, page ids) so that malformed data
+ *     gives wrong numbers rather than out-of-bounds accesses.
+ *   - Fixed sizes: 128-token KV / index-K pages = 128-token sparse blocks, a
+ *     page-16 view (8 sub-pages per page), head dim 128, index dim 128, one KV
+ *     head and one index head.
+ *
+ * Data layouts (all row-major, innermost last)
+ *   index_q      [N][128]                bf16
+ *   index_k      [P][128][128]           bf16   page, token slot, dim
+ *   q, out       [N][Hq][128]            bf16
+ *   k_cache      [8P][16][Hkv][128]      bf16 | fp8 e4m3fn   token-major sub-pages
+ *   v_cache      [8P][Hkv][128][16]      bf16 | fp8 e4m3fn   dim-major sub-pages
+ *   k/v_scale    scalar: [1] fp32;  per-token-head: [8P][16][Hkv] fp32
+ *   block_table  [R][ld_bt]              int32  physical page-128 ids
+ *   block_scores [N][ld_s]               fp32
+ *   sparse_table [N][ld_table]           int32  page-16 sub-page ids
+ *   Sub-page i of physical page p is 8*p + i. Token t of a request lives in
+ *   page block_table[r][t / 128], slot t % 128.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* msa_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null required pointer, negative size, bad enum */
+  MSA_ERR_UNSUPPORTED = -2, /* shape outside what the kernels implement */
+  MSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MSA_ERR_HIP = -4          /* a launch failed (hipGetLastError) */
+} msa_status;
+
+typedef enum { MSA_KV_BF16 = 0, MSA_KV_FP8_E4M3FN = 1 } msa_kv_dtype;
+
+typedef enum {
+  MSA_SCALE_NONE = 0,          /* K-hat = K, V-hat = V (bf16 caches) */
+  MSA_SCALE_SCALAR = 1,        /* one fp32 scale for K and one for V */
+  MSA_SCALE_PER_TOKEN_HEAD = 2 /* one fp32 scale per (token, KV head) */
+} msa_scale_mode;
+
+enum {
+  MSA_PAGE_TOKENS = 128,
+  MSA_SUBPAGE_TOKENS = 16,
+  MSA_HEAD_DIM = 128,
+  MSA_INDEX_DIM = 128,
+  MSA_MAX_REQS = 8192,      /* requests per batch */
+  MSA_MAX_Q_HEADS = 128,    /* query heads sharing the one KV head */
+  MSA_MAX_TOPK = 8192,      /* selected blocks per row */
+  MSA_SCORE_ROWS_PER_UNIT = 64 /* query rows of one request scored per work unit */
+};
+
+/*
+ * Batch description: host struct holding device pointers and host scalars.
+ * Decode requests come first and prefill requests after (#56170 page,
+ * 关键源码片段), though nothing here depends on that order.
+ */
+typedef struct msa_batch {
+  const int32_t* seq_lens;    /* [num_reqs] L_r: KV tokens incl. this step's new ones */
+  const int32_t* query_lens;  /* [num_reqs] ql_r: query rows, 0 <= ql_r <= L_r */
+  const int32_t* block_table; /* [num_reqs][ld_bt] page-128 physical ids */
+  /* outputs of msa_build_metadata, inputs of the other calls */
+  int32_t* cu_seqlens_q;      /* [num_reqs+1] 0, ql_0, ql_0+ql_1, ... */
+  int32_t* cu_seqlens_k;      /* [num_reqs+1] 0, L_0, L_0+L_1, ... */
+  int32_t* cu_blocks;         /* [num_reqs+1] prefix of ceil(L_r/128) */
+  int32_t* cu_units;          /* [num_reqs+1] prefix of ceil(L_r/128)*ceil(ql_r/64):
+                                 the score kernel's work units */
+  int32_t* row_req;           /* [num_rows] request id of each query row */
+  int32_t* row_pos;           /* [num_rows] absolute position L_r - ql_r + i */
+  int32_t num_reqs;           /* host, exact */
+  int32_t num_rows;           /* host, exact: sum of query_lens */
+  int32_t ld_bt;              /* host: row stride of block_table (>= blocks of any request) */
+  int32_t max_seq_len;        /* host: upper bound of every seq_len (sizes grids) */
+  int32_t num_pages;          /* host: P, physical pages in index_k / k_cache / v_cache */
+} msa_batch;
+
+/* K/V cache description (host struct with device pointers). */
+typedef struct msa_kv {
+  const void* k_cache;   /* [8P][16][Hkv][128] */
+  const void* v_cache;   /* [8P][Hkv][128][16] */
+  const float* k_scale;  /* NULL (MSA_SCALE_NONE), [1] or [8P][16][Hkv] */
+  const float* v_scale;
+  int32_t kv_dtype;      /* msa_kv_dtype */
+  int32_t scale_mode;    /* msa_scale_mode; MSA_SCALE_NONE requires bf16 */
+  int32_t num_kv_heads;  /* must be 1 */
+  int32_t num_pages;     /* P: the caches hold 8P sub-pages */
+} msa_kv;
+
+/*
+ * msa_build_metadata — device-side batch metadata with no host round trip
+ * (#56170 page, 实现拆解 items 1-3 and 关键源码片段: cu_seqlens_k is a zero
+ * followed by the running sum of seq_lens, written on the device; prefill rows
+ * get a request id and an absolute position).
+ * Writes cu_seqlens_q, cu_seqlens_k, cu_blocks, cu_units, row_req, row_pos.
+ * Errors: INVALID_ARG for null pointers or num_reqs/num_rows < 0;
+ * UNSUPPORTED for num_reqs > MSA_MAX_REQS.
+ */
+msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch);
+
+/*
+ * msa_index_score — index scores pooled per 128-token block (#54682 page,
+ * 功能与动机 and 实现拆解 item 1: the per-row decode scorer, with work mapped
+ * to each request's real block count and index-K tiles shared by a request's
+ * rows).
+ *   block_scores[n][b] = max over visible tokens t of block b (t <= row_pos[n])
+ *                        of dot(index_q[n], index_k[token t]),  b < nb_n
+ *   block_scores[n][b] = -inf for nb_n <= b < ld_s,  nb_n = ceil((row_pos[n]+1)/128)
+ * Requires msa_build_metadata on the same batch earlier on the stream.
+ * index_q [N][128] bf16, index_k [P][128][128] bf16, block_scores [N][ld_s] fp32.
+ * Errors: INVALID_ARG for null pointers; UNSUPPORTED if ld_s < ceil(max_seq_len/128).
+ */
+msa_status msa_index_score(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                           const void* index_k, float* block_scores, int32_t ld_s);
+
+/*
+ * msa_topk_block_table — fused top-k selection, page-16 sparse block table and
+ * context lengths (#54682 page, 实现拆解 items 1 and 4; #47287 page, 实现拆解
+ * item 3 and 评论区精华 on keeping the zero padding inside the row).
+ * For each row n with nb_n eligible blocks, K' = min(topk, nb_n) blocks are kept
+ * under the total order (score descending, block id ascending, -0 == +0) and
+ * listed by ascending block id b_0 < ... < b_{K'-1}:
+ *   sparse_table[n][8j+i] = 8*block_table[r][b_j] + i   (j < K', i < 8)
+ *   sparse_table[n][m]    = 0                            (8K' <= m < 8*topk)
+ *   ctx_lens[n]           = sum_j min(128, row_pos[n]+1 - 128*b_j)
+ *   sel_blocks[n][j]      = b_j, then -1                 (optional, may be NULL)
+ * Nothing is written at or past column 8*topk of sparse_table (its row stride
+ * is 8*topk).
+ * Errors: INVALID_ARG for null required pointers or topk < 1; UNSUPPORTED for
+ * topk > MSA_MAX_TOPK or ld_s < ceil(max_seq_len/128).
+ */
+msa_status msa_topk_block_table(msa_stream_t stream, const msa_batch* batch,
+                                const float* block_scores, int32_t ld_s, int32_t topk,
+                                int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks);
+
+/*
+ * msa_sparse_paged_attn — paged attention over a page-16 sparse table with an
+ * online softmax (#47287 page, 功能与动机: attention over a few selected logical
+ * blocks; 实现拆解 item 2: FP8 k_scale / v_scale, scalar or per-token-head;
+ * 实现拆解 item 3: the page-16 view of the page-128 cache).
+ * Row n, query head h (KV head 0): tokens u < ctx_lens[n] live in sub-page
+ * sparse_table[n][u/16], slot u%16;
+ *   out[n][h] = sum_u softmax_u(sm_scale * q[n][h] . K-hat_u) V-hat_u
+ * with K-hat = k_scale * K, V-hat = v_scale * V. Rows with ctx 0 give zeros.
+ * Output is bf16 (round to nearest even). Also serves a selection reused from
+ * another layer: the table need not come from msa_topk_block_table.
+ *   max_ctx (host): upper bound of ctx_lens; larger device values are clamped.
+ *   ld_table: row stride of sparse_table, >= ceil(max_ctx/16).
+ *   workspace: >= msa_workspace_bytes(num_rows, num_q_heads, max_ctx, 0) bytes,
+ *   256-byte aligned; its contents need no initialisation.
+ * Errors: INVALID_ARG for null required pointers or sizes < 0; UNSUPPORTED for
+ * num_kv_heads != 1, num_q_heads > MSA_MAX_Q_HEADS, bad dtype/scale pairing
+ * (MSA_SCALE_NONE with fp8); WORKSPACE if the workspace is too small.
+ */
+msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num_rows,
+                                 int32_t num_q_heads, const msa_kv* kv,
+                                 const int32_t* sparse_table, int32_t ld_table,
+                                 const int32_t* ctx_lens, int32_t max_ctx, float sm_scale,
+                                 void* out, void* workspace, size_t workspace_bytes);
+
+/*
+ * msa_sparse_decode — the whole decode step on one stream with no host
+ * synchronisation: metadata, index score + pooling, top-k + page-16 table +
+ * context lengths, sparse paged attention and the split merge (#54682 page,
+ * 实现拆解 items 2-3: the indexer writes the sparse table that attention then
+ * consumes; completion counters are reset in-stream so the step can be
+ * replayed from a HIP graph).
+ *   sparse_table [N][8*topk], ctx_lens [N]: written (outputs of the top-k step).
+ *   sel_blocks [N][topk]: optional (NULL skips it).
+ *   block_scores [N][ld_s]: optional; when NULL the scores live in the
+ *   workspace. ld_s >= ceil(max_seq_len/128).
+ *   workspace: >= msa_workspace_bytes(num_rows, num_q_heads, 128*topk,
+ *   block_scores ? 0 : ld_s) bytes.
+ * Errors: union of the errors of the steps.
+ */
+msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                             const void* index_k, const void* q, int32_t num_q_heads,
+                             const msa_kv* kv, int32_t topk, float sm_scale, void* out,
+                             int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
+                             float* block_scores, int32_t ld_s, void* workspace,
+                             size_t workspace_bytes);
+
+/*
+ * msa_workspace_bytes — workspace needed by msa_sparse_paged_attn (ld_s = 0)
+ * or msa_sparse_decode (max_ctx = 128*topk; ld_s > 0 when the scores live in
+ * the workspace) on the current device. Returns 0 for invalid arguments.
+ */
+size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ctx, int32_t ld_s);
+
+/* Human-readable name of a status code (static storage). */
+const char* msa_status_string(msa_status status);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int32_t msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -186,18 +186,20 @@ def make_batch(name: str, seed: int, seq_lens, query_lens, topk: int, num_q_head
                *, kv_dtype: int = KV_BF16, scale_mode: int = SCALE_NONE,
                permute_pages: bool = True, max_seq_len: int | None = None,
                scale_lo: float = 0.5, scale_hi: float = 2.0, num_kv_heads: int = 1,
-               extra_pages: int = 0, ld_bt: int | None = None) -> Batch:
-    """Build a batch from explicit lengths (lengths are not drawn here)."""
+               extra_pages: int = 0, ld_bt: int | None = None, data: bool = True) -> Batch:
+    """Build a batch from explicit lengths (lengths are not drawn here).
+    With ``data=False`` only lengths and the block table are drawn; the tensor
+    fields are empty (for tests of metadata and selection alone)."""
     rng = SplitMix64(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     query_lens = np.asarray(query_lens, dtype=np.int32)
     return _fill(rng, name, seed, seq_lens, query_lens, topk, num_q_heads, kv_dtype,
                  scale_mode, permute_pages, max_seq_len, scale_lo, scale_hi,
-                 num_kv_heads, extra_pages, ld_bt)
+                 num_kv_heads, extra_pages, ld_bt, data)
 
 
 def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
-          permute_pages, max_seq_len, scale_lo, scale_hi, hkv, extra_pages, ld_bt):
+          permute_pages, max_seq_len, scale_lo, scale_hi, hkv, extra_pages, ld_bt, data=True):
     R = int(seq_lens.shape[0])
     nblk = [-(-int(L) // PAGE) for L in seq_lens]
     P = int(sum(nblk)) + int(extra_pages)
@@ -212,6 +214,15 @@ def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
         bt[r, :nblk[r]] = perm[pos:pos + nblk[r]]
         pos += nblk[r]
     N = int(query_lens.sum())
+    if not data:
+        e16, e8 = np.zeros(0, np.uint16), np.zeros(0, np.uint8)
+        return Batch(name=name, seed=seed, seq_lens=seq_lens, query_lens=query_lens,
+                     block_table=bt, num_pages=P, max_seq_len=int(max_seq_len), topk=int(topk),
+                     num_q_heads=int(hq), num_kv_heads=int(hkv), kv_dtype=int(kv_dtype),
+                     scale_mode=int(scale_mode), sm_scale=1.0 / math.sqrt(HEAD_DIM),
+                     index_q=e16, index_k=e16, q=e16,
+                     k_cache=e16 if kv_dtype == KV_BF16 else e8,
+                     v_cache=e16 if kv_dtype == KV_BF16 else e8, k_scale=None, v_scale=None)
     index_q = bf16_normal(rng, (N, INDEX_DIM))
     index_k = bf16_normal(rng, (P, PAGE, INDEX_DIM))
     q = bf16_normal(rng, (N, hq, HEAD_DIM))

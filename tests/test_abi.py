@@ -1,0 +1,161 @@
+"""The C ABI library loads, exports what include/msa.h declares, and rejects
+bad arguments on the host without launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_paged_msa_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:msa_status|size_t|const char\*|int32_t)\s+(msa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msa.load()
+
+
+def test_header_declares_the_path_entry_points():
+    names = header_functions()
+    for want in ("msa_build_metadata", "msa_index_score", "msa_topk_block_table",
+                 "msa_sparse_paged_attn", "msa_sparse_decode", "msa_workspace_bytes"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (msa_\w+)", out))
+    assert exported == set(header_functions())
+    assert set(msa.EXPORTS) == exported
+
+
+def test_library_makes_no_host_round_trips():
+    # no copy, synchronisation or allocation call is imported by the library
+    out = subprocess.run(["nm", "-D", "--undefined-only", msa.LIB_PATH], capture_output=True, text=True).stdout
+    for bad in ("hipMemcpy", "Synchronize", "hipMalloc", "hipFree", "hipMemset", "hipHostRegister"):
+        assert bad not in out, bad
+
+
+def test_status_strings(lib):
+    assert msa.status_string(0) == "MSA_OK"
+    assert msa.status_string(-3) == "MSA_ERR_WORKSPACE"
+    assert msa.msa_version() >= 100
+
+
+def test_workspace_bytes_monotone_and_aligned():
+    a = msa.msa_workspace_bytes(8, 16, 2048, 0)
+    b = msa.msa_workspace_bytes(8, 16, 2048, 256)
+    c = msa.msa_workspace_bytes(16, 16, 2048, 256)
+    assert 0 < a < b <= c
+    assert a % 256 == 0 and b % 256 == 0
+    assert msa.msa_workspace_bytes(-1, 16, 1, 0) == 0
+
+
+def _fake_batch(**kw):
+    base = dict(seq_lens=0x1000, query_lens=0x2000, block_table=0x3000, cu_seqlens_q=0x4000,
+                cu_seqlens_k=0x5000, cu_blocks=0x6000, cu_units=0x7000, row_req=0x8000, row_pos=0x9000,
+                num_reqs=2, num_rows=2, ld_bt=4, max_seq_len=512, num_pages=8)
+    base.update(kw)
+    return msa.MsaBatch(**base)
+
+
+def _fake_kv(**kw):
+    base = dict(k_cache=0x1000, v_cache=0x2000, k_scale=0, v_scale=0, kv_dtype=0, scale_mode=0,
+                num_kv_heads=1, num_pages=8)
+    base.update(kw)
+    return msa.MsaKV(**base)
+
+
+def _code(fn, *args):
+    try:
+        fn(*args)
+    except msa.MsaError as e:
+        return e.status
+    return 0
+
+
+# Each of these must fail host-side validation before any launch.
+@pytest.mark.parametrize("batch,expect", [
+    (dict(num_reqs=-1), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_reqs=9000), msa.MSA_ERR_UNSUPPORTED),
+    (dict(seq_lens=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(cu_units=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(ld_bt=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_reqs=0, num_rows=3), msa.MSA_ERR_INVALID_ARG),
+])
+def test_metadata_rejects(batch, expect):
+    assert _code(msa.msa_build_metadata, _fake_batch(**batch), 0) == expect
+
+
+def test_index_score_rejects_small_ld_s():
+    assert _code(msa.msa_index_score, _fake_batch(), 0x1, 0x2, 0x3, 3, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_index_score, _fake_batch(), 0, 0x2, 0x3, 4, 0) == msa.MSA_ERR_INVALID_ARG
+
+
+def test_topk_rejects():
+    b = _fake_batch()
+    assert _code(msa.msa_topk_block_table, b, 0x1, 4, 0, 0x2, 0x3, None, 0) == msa.MSA_ERR_INVALID_ARG
+    assert _code(msa.msa_topk_block_table, b, 0x1, 4, 9000, 0x2, 0x3, None, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_topk_block_table, b, 0x1, 2, 4, 0x2, 0x3, None, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_topk_block_table, b, 0x1, 4, 4, 0, 0x3, None, 0) == msa.MSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kv,expect", [
+    (dict(num_kv_heads=2), msa.MSA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1, scale_mode=0), msa.MSA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1, scale_mode=2, k_scale=0x10, v_scale=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(kv_dtype=5), msa.MSA_ERR_INVALID_ARG),
+    (dict(k_cache=0), msa.MSA_ERR_INVALID_ARG),
+])
+def test_attention_rejects_kv(kv, expect):
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, _fake_kv(**kv), 0x2, 8, 0x3, 128, 0.1,
+                 0x4, 0x5, 1 << 20, 0) == expect
+
+
+def test_attention_rejects_heads_table_and_workspace():
+    kv = _fake_kv()
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 200, kv, 0x2, 8, 0x3, 128, 0.1, 0x4, 0x5, 1 << 20, 0) \
+        == msa.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 7, 0x3, 128, 0.1, 0x4, 0x5, 1 << 20, 0) \
+        == msa.MSA_ERR_INVALID_ARG
+    need = msa.msa_workspace_bytes(4, 16, 128, 0)
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 8, 0x3, 128, 0.1, 0x4, 0x5, need - 1, 0) \
+        == msa.MSA_ERR_WORKSPACE
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 8, 0x3, 128, 0.1, 0x4, 0, need, 0) \
+        == msa.MSA_ERR_WORKSPACE
+
+
+def test_empty_calls_are_noops():
+    kv = _fake_kv()
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 0, 16, kv, 0x2, 8, 0x3, 128, 0.1, 0x4, 0, 0, 0) == 0
+    b = _fake_batch(num_reqs=0, num_rows=0)
+    assert _code(msa.msa_build_metadata, b, 0) == 0
+    assert _code(msa.msa_index_score, b, 0x1, 0x2, 0x3, 4, 0) == 0
+
+
+def test_decode_rejects_before_launch():
+    b = _fake_batch()
+    kv = _fake_kv()
+    args = [b, 0x1, 0x2, 0x3, 16, kv, 4, 0.1, 0x4, 0x5, 0x6, None, None, 4, 0x7, 1 << 30, 0]
+    bad = list(args)
+    bad[6] = 0                              # topk
+    assert _code(msa.msa_sparse_decode, *bad) == msa.MSA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[13] = 2                             # ld_s below ceil(512/128)
+    assert _code(msa.msa_sparse_decode, *bad) == msa.MSA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[15] = 16                            # workspace too small
+    assert _code(msa.msa_sparse_decode, *bad) == msa.MSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[5] = _fake_kv(num_pages=9)          # caches and batch disagree on P
+    assert _code(msa.msa_sparse_decode, *bad) == msa.MSA_ERR_INVALID_ARG

@@ -1,0 +1,361 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars: bit-exact metadata, selections, sparse tables and context lengths (the
+selection is checked on the device's own fp32 block scores); block scores
+within 1e-3 * max(|oracle|, 1) with exact -inf past each row's block count;
+attention within 2e-2 absolute (bf16 K/V) or 6e-2 (fp8 K/V) of the oracle run
+on the device's own table and context lengths.
+"""
+import dataclasses
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import msa_synth as syn
+from oracle import msa_oracle as O
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SCORE_RTOL = 1e-3
+ATOL_BF16 = 2e-2
+ATOL_FP8 = 6e-2
+
+
+def atol_for(b):
+    return ATOL_FP8 if b.kv_dtype == syn.KV_FP8 else ATOL_BF16
+
+
+def check_scores(b, gpu, rows):
+    ref = O.block_scores(b.index_q, b.index_k, b.block_table, b.seq_lens, b.query_lens, b.ld_s, rows=rows)
+    meta = O.build_metadata(b.seq_lens, b.query_lens)
+    for n in rows:
+        nb = O.num_blocks(O.visible_keys(meta["row_pos"][n]))
+        g, o = gpu[n], ref[n]
+        assert np.all(np.isneginf(g[nb:])), f"row {n}: tail past nb={nb} is not -inf"
+        err = np.abs(g[:nb] - o[:nb]) / np.maximum(np.abs(o[:nb]), 1.0)
+        assert np.all(np.isfinite(g[:nb])), f"row {n}: non-finite score"
+        assert err.max(initial=0.0) <= SCORE_RTOL, f"row {n}: score rel err {err.max()}"
+    return ref
+
+
+def check_selection(b, gpu_scores, table, ctx, sel, rows):
+    """Bit-exact against the oracle selector fed the device's fp32 scores."""
+    meta = O.build_metadata(b.seq_lens, b.query_lens)
+    for n in rows:
+        r = int(meta["row_req"][n])
+        v = O.visible_keys(meta["row_pos"][n])
+        nb = O.num_blocks(v)
+        s = O.select_blocks(gpu_scores[n].astype(np.float64), nb, b.topk)
+        assert sel[n].tolist() == O.selection_row_outputs(s, b.topk).tolist(), f"row {n}: selection"
+        assert table[n].tolist() == O.sparse_table_row(s, b.block_table[r], b.topk).tolist(), f"row {n}: table"
+        assert ctx[n] == O.context_length(s, v), f"row {n}: ctx"
+
+
+def check_selection_valid(b, oracle_scores, sel, rows):
+    """The device's choice is a valid top-k of the oracle's own scores within
+    the score tolerance (near-ties may fall either way)."""
+    meta = O.build_metadata(b.seq_lens, b.query_lens)
+    for n in rows:
+        nb = O.num_blocks(O.visible_keys(meta["row_pos"][n]))
+        kk = min(b.topk, nb)
+        chosen = [int(x) for x in sel[n][:kk]]
+        s = oracle_scores[n][:nb]
+        tol = SCORE_RTOL * np.maximum(np.abs(s), 1.0) * 2
+        thr = np.sort(s)[::-1][kk - 1]
+        others = np.setdiff1d(np.arange(nb), chosen)
+        assert np.all(s[chosen] + tol[chosen] >= thr), f"row {n}: a kept block is clearly below the k-th score"
+        if len(others):
+            assert np.all(s[others] - tol[others] <= thr), f"row {n}: a dropped block is clearly above the k-th"
+
+
+def check_attention(b, out, table, ctx, rows):
+    ref = O.attention_from_table(b, table, ctx, rows)
+    err = np.abs(out[rows] - ref)
+    assert err.max() <= atol_for(b), f"attention max abs err {err.max()} (rows {rows})"
+    return err.max()
+
+
+# ---------------------------------------------------------------------------
+# metadata
+# ---------------------------------------------------------------------------
+META_CASES = [
+    ([5, 300, 128, 0, 4097], [1, 4, 2, 0, 1]),
+    ([1], [1]),
+    ([16384] * 6 + [32768] * 2, [1] * 6 + [4096] * 2),
+    ([0, 0, 7, 0], [0, 0, 7, 0]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(META_CASES) + 3))
+def test_metadata_bitexact(gpu_lib, case):
+    if case < len(META_CASES):
+        L, ql = META_CASES[case]
+        b = syn.make_batch("meta", case, L, ql, topk=2, num_q_heads=16, max_seq_len=max(max(L), 1))
+    else:
+        b = syn.random_batch(40 + case, num_reqs=37 + 500 * (case - len(META_CASES)), max_len=3000, max_q=9)
+    d = H.upload(b)
+    got = H.run_metadata(d)
+    ref = O.build_metadata(b.seq_lens, b.query_lens)
+    for key in ("cu_seqlens_q", "cu_seqlens_k", "cu_blocks", "row_req", "row_pos"):
+        assert got[key].tolist() == ref[key].tolist(), key
+    L, ql = b.seq_lens.astype(np.int64), b.query_lens.astype(np.int64)
+    units = [0] + np.cumsum(-(-L // 128) * -(-ql // 64)).tolist()
+    assert got["cu_units"].tolist() == units
+
+
+# ---------------------------------------------------------------------------
+# index scores
+# ---------------------------------------------------------------------------
+SCORE_CASES = [
+    dict(L=[2048], ql=[1]),
+    dict(L=[300, 129, 1, 700, 128], ql=[1, 3, 1, 4, 2]),
+    dict(L=[1000, 5000], ql=[70, 33]),                 # several 16-row tiles and row groups
+    dict(L=[4000, 0, 257], ql=[130, 0, 17], max_seq_len=8192),  # empty request, wide ld_s
+]
+
+
+@pytest.mark.parametrize("case", range(len(SCORE_CASES)))
+def test_index_scores(gpu_lib, case):
+    c = SCORE_CASES[case]
+    b = syn.make_batch("score", 60 + case, c["L"], c["ql"], topk=4, num_q_heads=16,
+                       max_seq_len=c.get("max_seq_len"))
+    d = H.upload(b)
+    H.run_metadata(d)
+    gpu = H.run_scores(d)
+    check_scores(b, gpu, list(range(b.num_rows)))
+
+
+def test_index_scores_closed_form(gpu_lib):
+    # all-ones keys and query: every visible token scores exactly 128
+    b = syn.make_batch("ones", 70, [700, 64], [3, 1], topk=2, num_q_heads=16)
+    one = np.uint16(0x3F80)
+    b.index_k[:] = one
+    b.index_q[:] = one
+    d = H.upload(b)
+    H.run_metadata(d)
+    gpu = H.run_scores(d)
+    assert np.all(gpu[:, :1] == 128.0)
+    assert gpu[0, :6].tolist() == [128.0] * 6 and np.isneginf(gpu[0, 6:]).all()
+
+
+# ---------------------------------------------------------------------------
+# top-k, page-16 table, context length
+# ---------------------------------------------------------------------------
+def _crafted_scores(b, mode, seed):
+    rng = syn.SplitMix64(seed)
+    s = rng.normal(b.num_rows * b.ld_s).reshape(b.num_rows, b.ld_s)
+    if mode == "ties":
+        s = np.round(s * 2) / 2
+    elif mode == "zeros":
+        s = np.where(rng.uniform(s.size).reshape(s.shape) < 0.5, 0.0, -0.0)
+    elif mode == "equal":
+        s = np.full_like(s, 3.25)
+    elif mode == "few_distinct":
+        s = np.floor(rng.uniform(s.size).reshape(s.shape) * 3) - 1.0
+    return s.astype(np.float32)
+
+
+@functools.lru_cache(maxsize=1)
+def _topk_batch():
+    L = [128000, 5000, 129, 1, 2047, 640, 0, 77]
+    ql = [1, 2, 1, 1, 4, 3, 0, 77]
+    return syn.make_batch("topk", 80, L, ql, topk=1, num_q_heads=16, max_seq_len=131072, data=False)
+
+
+@pytest.mark.parametrize("mode", ["normal", "ties", "zeros", "equal", "few_distinct"])
+@pytest.mark.parametrize("topk", [1, 3, 16, 64, 1500])
+def test_topk_bitexact(gpu_lib, mode, topk):
+    b = dataclasses.replace(_topk_batch(), topk=topk)
+    d = H.upload(b)
+    H.run_metadata(d)
+    s = _crafted_scores(b, mode, 81 + topk)
+    table, ctx, sel = H.run_topk(d, s)
+    check_selection(b, s, table, ctx, sel, range(b.num_rows))
+
+
+# ---------------------------------------------------------------------------
+# attention on a given table
+# ---------------------------------------------------------------------------
+ATTN_CASES = [
+    dict(kv=syn.KV_BF16, sm=syn.SCALE_NONE, hq=16),
+    dict(kv=syn.KV_BF16, sm=syn.SCALE_NONE, hq=8),
+    dict(kv=syn.KV_BF16, sm=syn.SCALE_NONE, hq=24),
+    dict(kv=syn.KV_FP8, sm=syn.SCALE_SCALAR, hq=16),
+    dict(kv=syn.KV_FP8, sm=syn.SCALE_PER_TOKEN_HEAD, hq=16),
+    dict(kv=syn.KV_BF16, sm=syn.SCALE_PER_TOKEN_HEAD, hq=16),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ATTN_CASES)))
+def test_attention_on_device_table(gpu_lib, case):
+    c = ATTN_CASES[case]
+    L = [9000, 700, 129, 1, 20000, 3000]
+    ql = [1, 2, 1, 1, 1, 3]
+    b = syn.make_batch("attn", 90 + case, L, ql, topk=24, num_q_heads=c["hq"], kv_dtype=c["kv"],
+                       scale_mode=c["sm"])
+    d = H.upload(b)
+    H.run_metadata(d)
+    scores = H.run_scores(d)
+    table, ctx, sel = H.run_topk(d, scores)
+    out = H.run_attn(d, table, ctx, max_ctx=128 * b.topk)
+    check_attention(b, out, table, ctx, list(range(b.num_rows)))
+
+
+def test_attention_zero_context_rows_give_zeros(gpu_lib):
+    b = syn.make_batch("attn0", 99, [500, 300], [1, 1], topk=4, num_q_heads=16)
+    d = H.upload(b)
+    table = np.zeros((2, 32), np.int32)
+    table[1, :8] = np.arange(8) + 8 * int(b.block_table[1, 0])
+    ctx = np.array([0, 100], np.int32)
+    out = H.run_attn(d, table, ctx, max_ctx=512)
+    assert np.all(out[0] == 0.0)
+    check_attention(b, out, table, ctx, [1])
+
+
+# ---------------------------------------------------------------------------
+# the fused decode step
+# ---------------------------------------------------------------------------
+def test_fused_decode_equals_steps_and_oracle(gpu_lib):
+    b = syn.make_batch("fused", 110, [9000, 700, 129, 1, 20000], [1, 2, 1, 1, 4], topk=16, num_q_heads=16)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    out = H.bf16_to_np(o.out)
+    rows = list(range(b.num_rows))
+    ref_scores = check_scores(b, scores, rows)
+    check_selection(b, scores, table, ctx, sel, rows)
+    check_selection_valid(b, ref_scores, sel, rows)
+    check_attention(b, out, table, ctx, rows)
+    # the standalone entry points give the same bits
+    H.run_metadata(d)
+    s2 = H.run_scores(d)
+    assert np.array_equal(s2, scores)
+    t2, c2, sel2 = H.run_topk(d, s2)
+    assert np.array_equal(t2, table) and np.array_equal(c2, ctx) and np.array_equal(sel2, sel)
+    out2 = H.run_attn(d, t2, c2, max_ctx=128 * b.topk)
+    assert np.array_equal(out2, out)
+    # scores kept in the workspace instead of a caller buffer: same outputs
+    o3 = H.alloc_decode(d, with_scores=False)
+    H.run_decode(d, o3, with_scores=False)
+    assert torch.equal(o3.out, o.out) and torch.equal(o3.table, o.table)
+
+
+def test_fused_decode_repeat_and_graph_replay_bitwise(gpu_lib):
+    b = syn.make_batch("graph", 120, [20000, 3000, 7000], [4, 1, 2], topk=16, num_q_heads=16)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o.out, o.table, o.ctx, o.sel, o.scores)]
+    H.run_decode(d, o)
+    for t, r in zip((o.out, o.table, o.ctx, o.sel, o.scores), ref):
+        assert torch.equal(t, r)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        H.run_decode(d, o)           # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        H.run_decode(d, o)
+    for rep in range(3):
+        o.out.zero_()
+        o.table.fill_(-1)
+        o.ws.fill_(0x3F3F3F3F)       # garbage counters: the step resets them in-stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((o.out, o.table, o.ctx, o.sel, o.scores), ref):
+            assert torch.equal(t, r), f"replay {rep}"
+
+
+def _permute_pages(b, seed):
+    P = b.num_pages
+    pi = syn.SplitMix64(seed).permutation(P)
+    nb = syn.Batch(**{f: getattr(b, f) for f in b.__dataclass_fields__})
+    nb.block_table = np.where(b.block_table >= 0, pi[b.block_table], b.block_table).astype(np.int32)
+    nb.index_k = np.empty_like(b.index_k)
+    nb.index_k[pi] = b.index_k
+    sub = (8 * pi[:, None] + np.arange(8)[None, :]).reshape(-1)
+    nb.k_cache = np.empty_like(b.k_cache)
+    nb.k_cache[sub] = b.k_cache
+    nb.v_cache = np.empty_like(b.v_cache)
+    nb.v_cache[sub] = b.v_cache
+    if b.scale_mode == syn.SCALE_PER_TOKEN_HEAD:
+        nb.k_scale = np.empty_like(b.k_scale)
+        nb.k_scale[sub] = b.k_scale
+        nb.v_scale = np.empty_like(b.v_scale)
+        nb.v_scale[sub] = b.v_scale
+    return nb
+
+
+def test_physical_page_permutation_changes_no_output_bit(gpu_lib):
+    b = syn.make_batch("perm", 130, [9000, 3000], [1, 3], topk=8, num_q_heads=16, kv_dtype=syn.KV_FP8,
+                       scale_mode=syn.SCALE_PER_TOKEN_HEAD)
+    outs = []
+    for bb in (b, _permute_pages(b, 131)):
+        d = H.upload(bb)
+        o = H.alloc_decode(d)
+        H.run_decode(d, o)
+        outs.append((o.out.cpu(), o.ctx.cpu(), o.sel.cpu(), o.scores.cpu()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+@functools.lru_cache(maxsize=1)
+def _config(name, scale_mode):
+    return syn.config(name, scale_mode=scale_mode)
+
+
+def _sample_rows(b, k, seed):
+    N = b.num_rows
+    if N <= k:
+        return list(range(N))
+    meta = O.build_metadata(b.seq_lens, b.query_lens)
+    rows = set()
+    for r in range(b.num_reqs):                  # first and last row of each request
+        lo, hi = int(meta["cu_seqlens_q"][r]), int(meta["cu_seqlens_q"][r + 1])
+        if hi > lo:
+            rows.update([lo, hi - 1])
+    rng = syn.SplitMix64(seed)
+    rows.update(int(x) for x in rng.integers(0, N - 1, k))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name,scale_mode", [
+    ("tiny", None), ("bf16_batch", None), ("spec_decode", None),
+    ("fp8_kv", syn.SCALE_PER_TOKEN_HEAD), ("fp8_kv", syn.SCALE_SCALAR), ("mixed_prefill", None),
+])
+def test_workload_parity(gpu_lib, name, scale_mode):
+    b = _config(name, scale_mode)
+    print(f"[workload] {name} scale_mode={scale_mode} rows={b.num_rows} pages={b.num_pages}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    meta = H.run_metadata(d)
+    ref_meta = O.build_metadata(b.seq_lens, b.query_lens)
+    for key in ("cu_seqlens_q", "cu_seqlens_k", "cu_blocks", "row_req", "row_pos"):
+        assert meta[key].tolist() == ref_meta[key].tolist(), key
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    out = H.bf16_to_np(o.out)
+    # selection, tables and context lengths: every row, bit-exact on device scores
+    check_selection(b, scores, table, ctx, sel, range(b.num_rows))
+    rows = _sample_rows(b, 12, 7)
+    ref_scores = check_scores(b, scores, rows)
+    check_selection_valid(b, ref_scores, sel, rows)
+    err = check_attention(b, out, table, ctx, rows)
+    print(f"[workload] {name}: max attention err {err:.3e} over rows {rows[:8]}...", flush=True)
+    # every row that selected anything produced a finite output
+    assert np.isfinite(out).all()
