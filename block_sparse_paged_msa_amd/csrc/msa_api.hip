@@ -32,9 +32,10 @@ int cu_count() {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Attention split policy: the smallest split (a multiple of 128 tokens) whose
-// workgroup count stays within two workgroups per compute unit, so that short
-// batches still spread over the whole chip while long ones keep few partials.
+// Attention split policy: the smallest split (128 tokens times a power of two,
+// at most kMaxSplitTokens) whose workgroup count stays within two workgroups
+// per compute unit, so that short batches still spread over the whole chip
+// while long ones keep few partials.
 struct AttnPlan {
   int hgroups;
   int split_tok;
@@ -47,22 +48,24 @@ AttnPlan attn_plan(int num_rows, int num_q_heads, int max_ctx) {
   const int64_t ctx = max_ctx < 1 ? 1 : max_ctx;
   const int64_t target = 2LL * cu_count();
   int64_t split = 128;
-  while (split < ctx && static_cast<int64_t>(num_rows) * p.hgroups * ceil_div(ctx, split) > target) split *= 2;
+  while (split < ctx && split < kMaxSplitTokens &&
+         static_cast<int64_t>(num_rows) * p.hgroups * ceil_div(ctx, split) > target)
+    split *= 2;
   p.split_tok = static_cast<int>(split);
   p.nsplit = static_cast<int>(ceil_div(ctx, split));
   return p;
 }
 
 struct WsLayout {
-  size_t counters, partials, scores, total;
+  size_t partials, scores, total;
 };
 
+// Workspace: split partials (rows with several splits) then, for the fused
+// step without a caller score buffer, the block scores.
 WsLayout ws_layout(int num_rows, int num_q_heads, int max_ctx, int ld_s) {
   const AttnPlan p = attn_plan(num_rows, num_q_heads, max_ctx);
   WsLayout w;
   size_t off = 0;
-  w.counters = off;
-  off += align256(sizeof(int32_t) * static_cast<size_t>(num_rows) * p.hgroups);
   w.partials = off;
   if (p.nsplit > 1)
     off += align256(sizeof(float) * static_cast<size_t>(num_rows) * p.hgroups * p.nsplit *
@@ -78,7 +81,7 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
 msa_status check_batch(const msa_batch* b, bool need_meta_outputs) {
   if (!b) return MSA_ERR_INVALID_ARG;
   if (b->num_reqs < 0 || b->num_rows < 0 || b->max_seq_len < 0) return MSA_ERR_INVALID_ARG;
-  if (b->num_reqs > MSA_MAX_REQS) return MSA_ERR_UNSUPPORTED;
+  if (b->num_reqs > MSA_MAX_REQS || b->max_seq_len > MSA_MAX_SEQ_LEN) return MSA_ERR_UNSUPPORTED;
   if (b->num_rows > 0 && b->num_reqs == 0) return MSA_ERR_INVALID_ARG;
   if (b->num_reqs == 0) return MSA_OK;
   if (b->ld_bt < 1 || b->num_pages < 1) return MSA_ERR_INVALID_ARG;
@@ -103,7 +106,12 @@ msa_status check_kv(const msa_kv* kv) {
   return MSA_OK;
 }
 
-MsaMetaArgs meta_args(const msa_batch* b, int32_t* zero_ptr, int64_t zero_count) {
+int32_t len_cap(const msa_batch* b) {
+  const int64_t cap = static_cast<int64_t>(kPage) * b->ld_bt;
+  return static_cast<int32_t>(cap < b->max_seq_len ? cap : b->max_seq_len);
+}
+
+MsaMetaArgs meta_args(const msa_batch* b) {
   MsaMetaArgs m;
   m.seq_lens = b->seq_lens;
   m.query_lens = b->query_lens;
@@ -113,30 +121,34 @@ MsaMetaArgs meta_args(const msa_batch* b, int32_t* zero_ptr, int64_t zero_count)
   m.cu_units = b->cu_units;
   m.row_req = b->row_req;
   m.row_pos = b->row_pos;
-  m.zero_ptr = zero_ptr;
-  m.zero_count = zero_count;
   m.num_reqs = b->num_reqs;
   m.num_rows = b->num_rows;
-  const int64_t cap = static_cast<int64_t>(kPage) * b->ld_bt;
-  m.len_cap = static_cast<int32_t>(cap < b->max_seq_len ? cap : b->max_seq_len);
+  m.len_cap = len_cap(b);
   return m;
 }
 
 msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, const void* index_k,
-                        float* scores, int32_t ld_s) {
+                        float* scores, int32_t ld_s, bool write_meta) {
   MsaScoreArgs a;
   a.index_q = static_cast<const uint16_t*>(index_q);
   a.index_k = static_cast<const uint16_t*>(index_k);
   a.block_table = b->block_table;
+  a.seq_lens = b->seq_lens;
+  a.query_lens = b->query_lens;
+  a.scores = scores;
   a.cu_q = b->cu_seqlens_q;
   a.cu_k = b->cu_seqlens_k;
+  a.cu_blocks = b->cu_blocks;
   a.cu_units = b->cu_units;
-  a.scores = scores;
+  a.row_req = b->row_req;
+  a.row_pos = b->row_pos;
   a.ld_s = ld_s;
   a.ld_bt = b->ld_bt;
   a.num_reqs = b->num_reqs;
   a.num_rows = b->num_rows;
   a.num_pages = b->num_pages;
+  a.len_cap = len_cap(b);
+  a.write_meta = write_meta ? 1 : 0;
   // units <= blocks_bound * sum_r ceil(ql_r/64) <= blocks_bound * (R + ceil(N/64))
   const int64_t units = static_cast<int64_t>(blocks_bound(b)) * (b->num_reqs + ceil_div(b->num_rows, kRowsPerUnit));
   int64_t wgs = ceil_div(units, 4);
@@ -164,36 +176,34 @@ msa_status launch_topk(hipStream_t s, const msa_batch* b, const float* scores, i
   return hip_status(msa_launch_topk(a, s));
 }
 
-msa_status launch_attn(hipStream_t s, const void* q, int32_t num_rows, int32_t num_q_heads, const msa_kv* kv,
-                       const int32_t* table, int32_t ld_table, const int32_t* ctx, int32_t max_ctx,
-                       float sm_scale, void* out, void* ws, bool zero_counters) {
+MsaAttnArgs attn_args(const void* q, int32_t num_rows, int32_t num_q_heads, const msa_kv* kv, int32_t ld_table,
+                      int32_t max_ctx, float sm_scale, void* out, void* ws) {
   const AttnPlan p = attn_plan(num_rows, num_q_heads, max_ctx);
   const WsLayout w = ws_layout(num_rows, num_q_heads, max_ctx, 0);
-  MsaAttnArgs a;
+  MsaAttnArgs a = {};
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = kv->k_cache;
   a.v_cache = kv->v_cache;
   a.k_scale = kv->k_scale;
   a.v_scale = kv->v_scale;
-  a.table = table;
-  a.ctx = ctx;
   a.out = static_cast<uint16_t*>(out);
   a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + w.partials);
-  a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + w.counters);
+  a.ld_table = ld_table;
   a.num_rows = num_rows;
   a.num_q_heads = num_q_heads;
   a.num_hgroups = p.hgroups;
-  a.ld_table = ld_table;
   a.max_ctx = max_ctx;
   a.split_tok = p.split_tok;
   a.nsplit = p.nsplit;
   a.num_subpages = kv->num_pages * msa::kSubsPerPage;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  if (zero_counters && p.nsplit > 1) {
-    hipError_t e = msa_launch_zero(a.counters, static_cast<int64_t>(num_rows) * p.hgroups, s);
-    if (e != hipSuccess) return MSA_ERR_HIP;
-  }
-  return hip_status(msa_launch_attn(a, kv->kv_dtype, kv->scale_mode, s));
+  return a;
+}
+
+msa_status launch_attn_and_merge(hipStream_t s, const MsaAttnArgs& a, const msa_kv* kv) {
+  msa_status st = hip_status(msa_launch_attn(a, kv->kv_dtype, kv->scale_mode, s));
+  if (st != MSA_OK) return st;
+  return hip_status(msa_launch_merge(a, s));
 }
 
 }  // namespace
@@ -204,17 +214,17 @@ msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch) {
   msa_status st = check_batch(batch, true);
   if (st != MSA_OK) return st;
   if (batch->num_reqs == 0) return MSA_OK;
-  return hip_status(msa_launch_meta(meta_args(batch, nullptr, 0), static_cast<hipStream_t>(stream)));
+  return hip_status(msa_launch_meta(meta_args(batch), static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_index_score(msa_stream_t stream, const msa_batch* batch, const void* index_q, const void* index_k,
                            float* block_scores, int32_t ld_s) {
-  msa_status st = check_batch(batch, true);
+  msa_status st = check_batch(batch, false);
   if (st != MSA_OK) return st;
   if (batch->num_rows == 0) return MSA_OK;
   if (!index_q || !index_k || !block_scores) return MSA_ERR_INVALID_ARG;
   if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
-  return launch_score(static_cast<hipStream_t>(stream), batch, index_q, index_k, block_scores, ld_s);
+  return launch_score(static_cast<hipStream_t>(stream), batch, index_q, index_k, block_scores, ld_s, false);
 }
 
 msa_status msa_topk_block_table(msa_stream_t stream, const msa_batch* batch, const float* block_scores,
@@ -244,9 +254,11 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
   if (!q || !sparse_table || !ctx_lens || !out) return MSA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(ld_table) * kSub < max_ctx || ld_table < 1) return MSA_ERR_INVALID_ARG;
   const WsLayout w = ws_layout(num_rows, num_q_heads, max_ctx, 0);
-  if (!workspace || workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
-  return launch_attn(static_cast<hipStream_t>(stream), q, num_rows, num_q_heads, kv, sparse_table, ld_table,
-                     ctx_lens, max_ctx, sm_scale, out, workspace, true);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MSA_ERR_WORKSPACE;
+  MsaAttnArgs a = attn_args(q, num_rows, num_q_heads, kv, ld_table, max_ctx, sm_scale, out, workspace);
+  a.table_in = sparse_table;
+  a.ctx_in = ctx_lens;
+  return launch_attn_and_merge(static_cast<hipStream_t>(stream), a, kv);
 }
 
 msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q, const void* index_k,
@@ -265,22 +277,25 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
   if (kv->num_pages != batch->num_pages) return MSA_ERR_INVALID_ARG;
   const int32_t max_ctx = kPage * topk;
   const WsLayout w = ws_layout(batch->num_rows, num_q_heads, max_ctx, block_scores ? 0 : ld_s);
-  if (!workspace || workspace_bytes < w.total) return MSA_ERR_WORKSPACE;
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* scores = block_scores ? block_scores : reinterpret_cast<float*>(ws + w.scores);
-  const AttnPlan p = attn_plan(batch->num_rows, num_q_heads, max_ctx);
-  // metadata + zeroed split counters, in one launch
-  st = hip_status(msa_launch_meta(
-      meta_args(batch, reinterpret_cast<int32_t*>(ws + w.counters), static_cast<int64_t>(batch->num_rows) * p.hgroups),
-      s));
+  float* scores = block_scores ? block_scores : reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores);
+  // 1) metadata + index scores, 2) per-row selection + attention, 3) split merge
+  st = launch_score(s, batch, index_q, index_k, scores, ld_s, true);
   if (st != MSA_OK) return st;
-  st = launch_score(s, batch, index_q, index_k, scores, ld_s);
-  if (st != MSA_OK) return st;
-  st = launch_topk(s, batch, scores, ld_s, topk, sparse_table, ctx_lens, sel_blocks);
-  if (st != MSA_OK) return st;
-  return launch_attn(s, q, batch->num_rows, num_q_heads, kv, sparse_table, 8 * topk, ctx_lens, max_ctx, sm_scale,
-                     out, workspace, false);
+  MsaAttnArgs a = attn_args(q, batch->num_rows, num_q_heads, kv, 8 * topk, max_ctx, sm_scale, out, workspace);
+  a.scores = scores;
+  a.ld_s = ld_s;
+  a.block_table = batch->block_table;
+  a.ld_bt = batch->ld_bt;
+  a.row_req = batch->row_req;
+  a.row_pos = batch->row_pos;
+  a.num_reqs = batch->num_reqs;
+  a.topk = topk;
+  a.table_out = sparse_table;
+  a.ctx_out = ctx_lens;
+  a.sel_out = sel_blocks;
+  return launch_attn_and_merge(s, a, kv);
 }
 
 size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ctx, int32_t ld_s) {

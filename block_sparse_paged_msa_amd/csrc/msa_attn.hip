@@ -5,7 +5,8 @@
 // page-128 cache).
 //
 // Workgroup = (row, group of 16 query heads, split of split_tok tokens), four
-// waves that each walk a contiguous run of 16-token sub-pages:
+// waves that each walk a contiguous run of 16-token sub-pages, two at a time,
+// with the next two sub-pages' loads in flight while the current pair is used:
 //   S^T[token][head] = K_sub (16x128) . Q^T (128x16)   v_mfma_f32_16x16x32_bf16
 //   O^T[dim][head]  += V_sub^T (128x16) . P^T (16x16)  v_mfma_f32_16x16x16_bf16
 // The S^T output layout (lane = head, four tokens per lane) is exactly the
@@ -14,10 +15,17 @@
 // bytes. FP8 codes are widened to bf16 in registers (exact); a per-token K
 // scale multiplies the logit, a per-token V scale multiplies the probability
 // fed to the PV product; scalar scales fold into the logit scale and the final
-// normalisation. The four waves merge through LDS; splits of one row merge in
-// the last-arriving workgroup (log2-domain LSE weights), so the result does
-// not depend on arrival order.
-#include "msa_internal.h"
+// normalisation. The four waves merge through LDS. A row split over several
+// workgroups leaves one partial (max, sum, unnormalised output) per split;
+// msa_merge_kernel combines them after the kernel boundary, in split order.
+//
+// In the fused decode step (vLLM PR #54682 page, 实现拆解 items 1-3: the
+// indexer's selection feeds attention in the same step) every workgroup
+// selects its row's blocks from the block scores itself (msa_select.h): the
+// selection is deterministic, so all workgroups of a row agree, and no
+// workgroup waits for another. The first workgroup of each row also writes the
+// page-16 table, the context length and the selected block ids.
+#include "msa_select.h"
 
 using namespace msa;
 
@@ -25,66 +33,160 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kPartStride = 2 * kHeadTile + kHeadTile * kDim;  // m[16], l[16], acc[16][128]
-
-template <int KV_FP8>
-__device__ __forceinline__ void load_k(const void* cache, int sub, int lane, bf16x8 (&ka)[4]) {
-  if constexpr (!KV_FP8) {
-    const uint16_t* kp = static_cast<const uint16_t*>(cache) + static_cast<size_t>(sub) * (kSub * kDim) +
-                         (lane & 15) * kDim + (lane >> 4) * 8;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) ka[kc] = *reinterpret_cast<const bf16x8*>(kp + kc * 32);
-  } else {
-    const uint8_t* kp = static_cast<const uint8_t*>(cache) + static_cast<size_t>(sub) * (kSub * kDim) +
-                        (lane & 15) * kDim + (lane >> 4) * 8;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(kp + kc * 32);
-      const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
-      ka[kc] = __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
-    }
-  }
-}
-
-template <int KV_FP8>
-__device__ __forceinline__ void load_v(const void* cache, int sub, int lane, i16x4 (&va)[8]) {
-  if constexpr (!KV_FP8) {
-    const uint16_t* vp = static_cast<const uint16_t*>(cache) + static_cast<size_t>(sub) * (kDim * kSub) +
-                         (lane & 15) * kSub + (lane >> 4) * 4;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) va[dt] = *reinterpret_cast<const i16x4*>(vp + dt * 16 * kSub);
-  } else {
-    const uint8_t* vp = static_cast<const uint8_t*>(cache) + static_cast<size_t>(sub) * (kDim * kSub) +
-                        (lane & 15) * kSub + (lane >> 4) * 4;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      va[dt] = __builtin_bit_cast(i16x4, fp8x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vp + dt * 16 * kSub)));
-  }
-}
+constexpr int kLdsRow = kDim + 4;                               // padded [head][dim] rows
+constexpr int kMaxSplitBlocks = kMaxSplitTokens / kPage;
 
 template <int KV_FP8, int SCALE_MODE>
-__global__ __launch_bounds__(kAttnThreads) void msa_attn_kernel(MsaAttnArgs a) {
-  __shared__ float s_m[4][kHeadTile];
-  __shared__ float s_l[4][kHeadTile];
-  __shared__ float s_o[4][kDim][kHeadTile + 1];
-  __shared__ int s_last;
+struct SubPage {
+  bf16x8 k[4];   // A operand of S^T: token lane%16, dims kc*32 + 8*(lane/16)..+7
+  i16x4 v[8];    // A operand of O^T: dim dt*16 + lane%16, tokens 4*(lane/16)..+3
+  f32x4 ks, vs;  // per-token scales of tokens 4*(lane/16)..+3
+};
 
+template <int KV_FP8, int SCALE_MODE>
+__device__ __forceinline__ void load_sub(const MsaAttnArgs& a, int sub, int lane, SubPage<KV_FP8, SCALE_MODE>& s) {
+  const size_t base = static_cast<size_t>(sub) * (kSub * kDim);
+  // K sub-pages are shuffled tiles [4][4][16][8]: operand kc of lane l is the
+  // 8 elements at (kc*64 + l)*8, so every operand load is one contiguous run.
+  if constexpr (!KV_FP8) {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k_cache) + base + lane * 8;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) s.k[kc] = *reinterpret_cast<const bf16x8*>(kp + kc * 512);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v_cache) + base + (lane & 15) * kSub + (lane >> 4) * 4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) s.v[dt] = *reinterpret_cast<const i16x4*>(vp + dt * 16 * kSub);
+  } else {
+    const uint8_t* kp = static_cast<const uint8_t*>(a.k_cache) + base + lane * 8;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(kp + kc * 512);
+      const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
+      s.k[kc] = __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
+    }
+    const uint8_t* vp = static_cast<const uint8_t*>(a.v_cache) + base + (lane & 15) * kSub + (lane >> 4) * 4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      s.v[dt] = __builtin_bit_cast(i16x4, fp8x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vp + dt * 16 * kSub)));
+  }
+  if constexpr (SCALE_MODE == 2) {
+    s.ks = *reinterpret_cast<const f32x4*>(a.k_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
+    s.vs = *reinterpret_cast<const f32x4*>(a.v_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
+  } else {
+    s.ks = f32x4{1.f, 1.f, 1.f, 1.f};
+    s.vs = f32x4{1.f, 1.f, 1.f, 1.f};
+  }
+}
+
+// Per-wave online-softmax state: O^T accumulators, running max (log2 domain,
+// equal in the four lanes of a head) and this lane's partial denominator.
+struct WaveState {
+  f32x4 o[8];
+  float m;
+  float l;
+};
+
+// One or two consecutive sub-pages: logits, one max update, PV products.
+template <int KV_FP8, int SCALE_MODE>
+__device__ __forceinline__ void attend_pair(WaveState& st, SubPage<KV_FP8, SCALE_MODE> (&sp)[2], int nval0, int nval1,
+                                            const bf16x8 (&qb)[4], float zscale, int lane) {
+  const int tok0 = 4 * (lane >> 4);
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) s0 = mfma_16x16x32(sp[0].k[kc], qb[kc], s0);
+  if (nval1 > 0) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) s1 = mfma_16x16x32(sp[1].k[kc], qb[kc], s1);
+  }
+  float z0[4], z1[4], mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z0[i] = (tok0 + i < nval0) ? s0[i] * zscale * sp[0].ks[i] : -INFINITY;
+    z1[i] = (tok0 + i < nval1) ? s1[i] * zscale * sp[1].ks[i] : -INFINITY;
+    mloc = fmaxf(mloc, fmaxf(z0[i], z1[i]));
+  }
+  const float m_new = fmaxf(st.m, max_across_rows(mloc));  // finite: token 0 of sub-page 0 is valid
+  const float alpha = fast_exp2(st.m - m_new);
+  float psum = 0.f;
+  i16x4 p0, p1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float e0 = fast_exp2(z0[i] - m_new);
+    const float e1 = fast_exp2(z1[i] - m_new);
+    psum += e0 + e1;
+    p0[i] = static_cast<short>(f32_to_bf16(e0 * sp[0].vs[i]));
+    p1[i] = static_cast<short>(f32_to_bf16(e1 * sp[1].vs[i]));
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  // V slots past the context can hold anything (even NaN codes): zero them so
+  // that a zero probability cannot meet a NaN in the product.
+  if (nval0 < kSub) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tok0 + i >= nval0) sp[0].v[dt][i] = 0;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16(sp[0].v[dt], p0, st.o[dt] * alpha);
+  if (nval1 > 0) {
+    if (nval1 < kSub) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + i >= nval1) sp[1].v[dt][i] = 0;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16(sp[1].v[dt], p1, st.o[dt]);
+  }
+}
+
+struct MergeLds {
+  float m[4][kHeadTile];
+  float l[4][kHeadTile];
+  __attribute__((aligned(16))) float o[4][kHeadTile][kLdsRow];
+};
+
+__device__ __forceinline__ u32x4 pack_bf16x8(f32x4 a, f32x4 b, float s) {
+  u32x4 pk;
+  pk.x = f32_to_bf16(a.x * s) | (static_cast<uint32_t>(f32_to_bf16(a.y * s)) << 16);
+  pk.y = f32_to_bf16(a.z * s) | (static_cast<uint32_t>(f32_to_bf16(a.w * s)) << 16);
+  pk.z = f32_to_bf16(b.x * s) | (static_cast<uint32_t>(f32_to_bf16(b.y * s)) << 16);
+  pk.w = f32_to_bf16(b.z * s) | (static_cast<uint32_t>(f32_to_bf16(b.w * s)) << 16);
+  return pk;
+}
+
+// Attention of (row n, head group hgi, split) over tokens
+// [split*split_tok, min(ctx, (split+1)*split_tok)); get_sub(sp) gives the
+// physical sub-page of the row's sp-th sub-page. Writes the output when the
+// row has one split, else this split's partial.
+// Q^T as the B operand of S^T: column = head lane%16, K entries = dims
+// kc*32 + 8*(lane/16)..+7 (heads past the group's end read as zero).
+__device__ __forceinline__ void load_q(const MsaAttnArgs& a, int n, int hgi, bf16x8 (&qb)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
+  if ((lane & 15) < nheads) {
+    const uint16_t* qp =
+        a.q + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + (lane & 15)) * kDim + (lane >> 4) * 8;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qb[kc] = *reinterpret_cast<const bf16x8*>(qp + kc * 32);
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qb[kc] = bf16x8{};
+  }
+}
+
+template <int KV_FP8, int SCALE_MODE, typename GetSub>
+__device__ __forceinline__ void attend_split(const MsaAttnArgs& a, MergeLds& ml, int n, int hgi, int split, int ctx,
+                                             const bf16x8 (&qb)[4], GetSub get_sub) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x % a.nsplit;
-  const int rest = blockIdx.x / a.nsplit;
-  const int hgi = rest % a.num_hgroups;
-  const int n = rest / a.num_hgroups;
-  const int ctx = clampi(a.ctx[n], 0, min(a.max_ctx, kSub * a.ld_table));
   const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
   const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
   uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile) * kDim;
-
-  if (ctx == 0) {  // nothing selected: zeros
-    if (split == 0)
-      for (int i = tid; i < nheads * kDim; i += kAttnThreads) orow[i] = 0;
-    return;
-  }
-  if (split >= nsplit_n) return;
+  const int th = tid >> 4;         // output / partial mapping: head th, dims td .. td+7
+  const int td = (tid & 15) * 8;
 
   float kscal = 1.f, vscal = 1.f;
   if constexpr (SCALE_MODE == 1) {
@@ -93,149 +195,229 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_kernel(MsaAttnArgs a) {
   }
   const float zscale = a.scale_log2 * kscal;
 
-  // Q^T as the B operand: column = head lane%16, K entries = dims kc*32 + 8*(lane/16)..
-  const int h = lane & 15;
-  bf16x8 qb[4];
-  if (h < nheads) {
-    const uint16_t* qp = a.q + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + h) * kDim + (lane >> 4) * 8;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qb[kc] = *reinterpret_cast<const bf16x8*>(qp + kc * 32);
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qb[kc] = bf16x8{};
-  }
-
   const int sp_per_wave = a.split_tok / (4 * kSub);
   const int sp_begin = split * (a.split_tok / kSub) + wave * sp_per_wave;
   const int sp_end = min(sp_begin + sp_per_wave, (ctx + kSub - 1) / kSub);
-  const int32_t* trow = a.table + static_cast<size_t>(n) * a.ld_table;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[8];
+  WaveState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int sp = sp_begin; sp < sp_end; ++sp) {
-    const int sub = clampi(trow[sp], 0, a.num_subpages - 1);
-    const int nval = min(kSub, ctx - sp * kSub);
-    bf16x8 ka[4];
-    i16x4 va[8];
-    load_k<KV_FP8>(a.k_cache, sub, lane, ka);
-    load_v<KV_FP8>(a.v_cache, sub, lane, va);
-    f32x4 ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (SCALE_MODE == 2) {
-      ks4 = *reinterpret_cast<const f32x4*>(a.k_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
-      vs4 = *reinterpret_cast<const f32x4*>(a.v_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
+  auto nval = [&](int sp) { return sp < sp_end ? min(kSub, ctx - sp * kSub) : 0; };
+  SubPage<KV_FP8, SCALE_MODE> A[2], B[2];
+  int sp = sp_begin;
+  if (sp < sp_end) {
+    load_sub(a, get_sub(sp), lane, A[0]);
+    if (sp + 1 < sp_end) load_sub(a, get_sub(sp + 1), lane, A[1]);
+  }
+  while (sp < sp_end) {
+    if (sp + 2 < sp_end) {
+      load_sub(a, get_sub(sp + 2), lane, B[0]);
+      if (sp + 3 < sp_end) load_sub(a, get_sub(sp + 3), lane, B[1]);
     }
-
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) s = mfma_16x16x32(ka[kc], qb[kc], s);
-
-    float z[4], mloc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 4 * (lane >> 4) + i;
-      z[i] = (tok < nval) ? s[i] * zscale * ks4[i] : -INFINITY;
-      mloc = fmaxf(mloc, z[i]);
+    attend_pair(st, A, nval(sp), nval(sp + 1), qb, zscale, lane);
+    sp += 2;
+    if (sp >= sp_end) break;
+    if (sp + 2 < sp_end) {
+      load_sub(a, get_sub(sp + 2), lane, A[0]);
+      if (sp + 3 < sp_end) load_sub(a, get_sub(sp + 3), lane, A[1]);
     }
-    const float m_new = fmaxf(m_run, max_across_rows(mloc));
-    const float alpha = fast_exp2(m_run - m_new);
-    float psum = 0.f;
-    i16x4 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(z[i] - m_new);
-      psum += p;
-      pb[i] = static_cast<short>(f32_to_bf16(p * vs4[i]));
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_16x16x16(va[dt], pb, o[dt] * alpha);
+    attend_pair(st, B, nval(sp), nval(sp + 1), qb, zscale, lane);
+    sp += 2;
   }
 
-  // ---- merge the four waves through LDS ----
-  const float l_w = sum_across_rows(l_run);
+  // ---- merge the four waves through LDS ([head][dim] rows) ----
+  const float l_w = sum_across_rows(st.l);
   if (lane < kHeadTile) {
-    s_m[wave][lane] = m_run;
-    s_l[wave][lane] = l_w;
+    ml.m[wave][lane] = st.m;
+    ml.l[wave][lane] = l_w;
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[wave][dt * 16 + 4 * (lane >> 4) + i][lane & 15] = o[dt][i];
+    for (int i = 0; i < 4; ++i) ml.o[wave][lane & 15][dt * 16 + 4 * (lane >> 4) + i] = st.o[dt][i];
   __syncthreads();
 
-  const int hh = tid & 15;
-  const int d0 = tid >> 4;  // dims d0 + 16k
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][hh]);
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-  float wt[4], Lsum = 0.f;
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml.m[w][th]);
+  float Lsum = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    wt[w] = (s_m[w][hh] == -INFINITY) ? 0.f : fast_exp2(s_m[w][hh] - Ms);
-    Lsum += wt[w] * s_l[w][hh];
-  }
-  float acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int d = d0 + 16 * k;
-    acc[k] = wt[0] * s_o[0][d][hh] + wt[1] * s_o[1][d][hh] + wt[2] * s_o[2][d][hh] + wt[3] * s_o[3][d][hh];
+    const float wt = (ml.m[w][th] == -INFINITY) ? 0.f : fast_exp2(ml.m[w][th] - M);
+    Lsum += wt * ml.l[w][th];
+    acc0 += wt * *reinterpret_cast<const f32x4*>(&ml.o[w][th][td]);
+    acc1 += wt * *reinterpret_cast<const f32x4*>(&ml.o[w][th][td + 4]);
   }
 
   if (nsplit_n == 1) {
     const float inv = (Lsum > 0.f) ? vscal / Lsum : 0.f;
-    if (hh < nheads) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) orow[hh * kDim + d0 + 16 * k] = f32_to_bf16(acc[k] * inv);
-    }
+    if (th < nheads) *reinterpret_cast<u32x4*>(orow + th * kDim + td) = pack_bf16x8(acc0, acc1, inv);
     return;
   }
+  // partial: a scalar V scale is folded in here (the merge is linear in acc)
+  float* part = a.partials + ((static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit + split) * kPartStride;
+  if ((tid & 15) == 0) {
+    part[th] = M;
+    part[kHeadTile + th] = Lsum;
+  }
+  *reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td) = acc0 * vscal;
+  *reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td + 4) = acc1 * vscal;
+}
 
-  // ---- several splits: publish the partial, the last arriver merges ----
-  const size_t slot0 = (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit;
-  float* part = a.partials + (slot0 + split) * kPartStride;
-  if (tid < kHeadTile) {
-    part[tid] = M;
-    part[kHeadTile + tid] = Lsum;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) part[2 * kHeadTile + hh * kDim + d0 + 16 * k] = acc[k];
-  __threadfence();
-  __syncthreads();
-  int32_t* counter = a.counters + static_cast<size_t>(n) * a.num_hgroups + hgi;
-  if (tid == 0) s_last = (atomicAdd(counter, 1) == nsplit_n - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+__device__ __forceinline__ void write_zero_row(const MsaAttnArgs& a, int n, int hgi) {
+  const int th = threadIdx.x >> 4, td = (threadIdx.x & 15) * 8;
+  const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
+  uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile) * kDim;
+  if (th < nheads) *reinterpret_cast<u32x4*>(orow + th * kDim + td) = u32x4{0u, 0u, 0u, 0u};
+}
 
-  const float* base = a.partials + slot0 * kPartStride;
-  float Mg = -INFINITY;
-  for (int sidx = 0; sidx < nsplit_n; ++sidx) Mg = fmaxf(Mg, base[sidx * kPartStride + hh]);
-  float Lg = 0.f, og[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sidx = 0; sidx < nsplit_n; ++sidx) {
-    const float* ps = base + sidx * kPartStride;
-    const float w = fast_exp2(ps[hh] - Mg);
-    Lg += w * ps[kHeadTile + hh];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) og[k] += w * ps[2 * kHeadTile + hh * kDim + d0 + 16 * k];
+// Table mode: the row's sub-pages and context length come from the caller.
+// Q and the split's table entries are fetched together at the start.
+template <int KV_FP8, int SCALE_MODE>
+__global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArgs a) {
+  __shared__ MergeLds ml;
+  __shared__ int s_sub[kMaxSplitTokens / kSub];
+  const int split = blockIdx.x % a.nsplit;
+  const int rest = blockIdx.x / a.nsplit;
+  const int hgi = rest % a.num_hgroups;
+  const int n = rest / a.num_hgroups;
+  const int ctx = clampi(a.ctx_in[n], 0, min(a.max_ctx, kSub * a.ld_table));
+  if (ctx == 0) {
+    if (split == 0) write_zero_row(a, n, hgi);
+    return;
   }
-  const float inv = (Lg > 0.f) ? vscal / Lg : 0.f;
-  if (hh < nheads) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) orow[hh * kDim + d0 + 16 * k] = f32_to_bf16(og[k] * inv);
+  if (split * a.split_tok >= ctx) return;
+  bf16x8 qb[4];
+  load_q(a, n, hgi, qb);
+  const int sp0 = split * (a.split_tok / kSub);
+  const int nsp = min(a.split_tok / kSub, (ctx + kSub - 1) / kSub - sp0);
+  const int32_t* trow = a.table_in + static_cast<size_t>(n) * a.ld_table + sp0;
+  for (int i = threadIdx.x; i < nsp; i += kAttnThreads) s_sub[i] = clampi(trow[i], 0, a.num_subpages - 1);
+  __syncthreads();
+  attend_split<KV_FP8, SCALE_MODE>(a, ml, n, hgi, split, ctx, qb, [&](int sp) { return s_sub[sp - sp0]; });
+}
+
+// Fused mode: select the row's blocks from its scores, then attend. The
+// row's scores (as keys) and block-table entries go to dynamic LDS, read in
+// the same round as Q; the merge buffers reuse that LDS after the selection.
+template <int KV_FP8, int SCALE_MODE>
+__global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // keys[nbmax], pages[nbmax] | MergeLds
+  __shared__ SelectLds sl;
+  __shared__ int s_pages[kMaxSplitBlocks];
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x % a.nsplit;
+  const int rest = blockIdx.x / a.nsplit;
+  const int hgi = rest % a.num_hgroups;
+  const int n = rest / a.num_hgroups;
+  const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
+  const int r = clampi(a.row_req[n], 0, a.num_reqs - 1);
+  const int v = a.row_pos[n] + 1;
+  const int nb = clampi((v + kPage - 1) / kPage, 0, nbmax);
+  const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
+  const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
+  uint32_t* keys = s_dyn;
+  int* pages = reinterpret_cast<int*>(s_dyn + nbmax);
+  for (int e = tid; e < nb; e += kAttnThreads) {
+    keys[e] = order_key(srow[e]);
+    pages[e] = bt[e];
   }
-  if (tid == 0) atomicExch(counter, 0);  // leave the counter at zero for the next call
+  bf16x8 qb[4];
+  load_q(a, n, hgi, qb);
+  __syncthreads();
+
+  const int nblk = a.split_tok / kPage;
+  const int blk0 = split * nblk;
+  const bool writer = split == 0 && hgi == 0;
+  int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
+  int32_t* selrow = a.sel_out ? a.sel_out + static_cast<size_t>(n) * a.topk : nullptr;
+  const int pmax = a.num_subpages / kSubsPerPage - 1;
+  int ctx = 0;
+  const int kk = select_row(keys, nb, a.topk, v, sl, [&](int pos, int e) {
+    const int page = pages[e];
+    if (pos >= blk0 && pos < blk0 + nblk) s_pages[pos - blk0] = clampi(page, 0, pmax);
+    if (writer) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) trow[8 * pos + i] = 8 * page + i;
+      if (selrow) selrow[pos] = e;
+    }
+  }, &ctx);
+  if (writer) {
+    for (int m = 8 * kk + tid; m < 8 * a.topk; m += kAttnThreads) trow[m] = 0;
+    if (selrow)
+      for (int m = kk + tid; m < a.topk; m += kAttnThreads) selrow[m] = -1;
+    if (tid == 0) a.ctx_out[n] = ctx;
+  }
+  __syncthreads();  // s_pages complete; keys and pages are dead from here on
+  ctx = min(ctx, a.max_ctx);
+  if (ctx == 0) {
+    if (split == 0) write_zero_row(a, n, hgi);
+    return;
+  }
+  if (split * a.split_tok >= ctx) return;
+  attend_split<KV_FP8, SCALE_MODE>(a, *reinterpret_cast<MergeLds*>(s_dyn), n, hgi, split, ctx, qb,
+                                   [&](int sp) { return 8 * s_pages[(sp >> 3) - blk0] + (sp & 7); });
+}
+
+// Combines the split partials of rows that needed more than one split, in
+// split order (log2-domain weights 2^(m_s - max)).
+__global__ __launch_bounds__(kAttnThreads) void msa_merge_kernel(MsaAttnArgs a, const int32_t* ctxp) {
+  const int tid = threadIdx.x;
+  const int hgi = blockIdx.x % a.num_hgroups;
+  const int n = blockIdx.x / a.num_hgroups;
+  const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
+  const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
+  if (nsplit_n <= 1) return;
+  const int th = tid >> 4, td = (tid & 15) * 8;
+  const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kPartStride;
+  float Mg = -INFINITY, Lg = 0.f;
+  f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit_n; s0 += 16) {  // sixteen splits' loads in flight at a time
+    float ms[16], ls[16];
+    f32x4 x0[16], x1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float* ps = base + static_cast<size_t>(min(s0 + j, nsplit_n - 1)) * kPartStride;
+      ms[j] = ps[th];
+      ls[j] = ps[kHeadTile + th];
+      x0[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td);
+      x1[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (s0 + j < nsplit_n) {
+        const float mn = fmaxf(Mg, ms[j]);
+        const float c_old = fast_exp2(Mg - mn);  // 0 on the first split (Mg = -inf)
+        const float c_new = fast_exp2(ms[j] - mn);
+        Lg = Lg * c_old + ls[j] * c_new;
+        g0 = g0 * c_old + x0[j] * c_new;
+        g1 = g1 * c_old + x1[j] * c_new;
+        Mg = mn;
+      }
+    }
+  }
+  const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
+  uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile) * kDim;
+  const float inv = (Lg > 0.f) ? 1.f / Lg : 0.f;
+  if (th < nheads) *reinterpret_cast<u32x4*>(orow + th * kDim + td) = pack_bf16x8(g0, g1, inv);
 }
 
 template <int KV_FP8, int SCALE_MODE>
 hipError_t launch(const MsaAttnArgs& a, hipStream_t s) {
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups * a.nsplit;
-  hipLaunchKernelGGL((msa_attn_kernel<KV_FP8, SCALE_MODE>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kAttnThreads), 0, s, a);
+  if (a.scores) {
+    const size_t nbmax = static_cast<size_t>(min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow));
+    const size_t lds = max(2 * nbmax * sizeof(uint32_t), sizeof(MergeLds));
+    hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kAttnThreads), lds, s, a);
+  }
+  else
+    hipLaunchKernelGGL((msa_attn_table_kernel<KV_FP8, SCALE_MODE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -249,4 +431,12 @@ hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, h
   }
   if (scale_mode == 1) return launch<1, 1>(a, s);
   return launch<1, 2>(a, s);
+}
+
+hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {
+  if (a.nsplit <= 1) return hipSuccess;
+  const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups;
+  hipLaunchKernelGGL(msa_merge_kernel, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, s, a,
+                     a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in);
+  return hipGetLastError();
 }

@@ -14,7 +14,7 @@ constexpr int kSubsPerPage = 8;   // sub-pages per page
 constexpr int kDim = 128;         // head dim and index dim
 constexpr int kRowsPerUnit = 64;  // query rows of one request per score unit
 constexpr int kHeadTile = 16;     // query heads per attention MFMA tile
-constexpr int kMaxReqs = 8192;    // requests per batch (LDS-resident prefix)
+constexpr int kMaxReqs = 4096;    // requests per batch (LDS-resident prefix)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -120,28 +120,33 @@ struct MsaMetaArgs {
   int32_t* cu_units;
   int32_t* row_req;
   int32_t* row_pos;
-  int32_t* zero_ptr;   // optional int32 region cleared by the same launch
-  int64_t zero_count;
   int32_t num_reqs;
   int32_t num_rows;
   int32_t len_cap;     // seq_lens are clamped to [0, len_cap]
 };
 hipError_t msa_launch_meta(const MsaMetaArgs& a, hipStream_t s);
-hipError_t msa_launch_zero(int32_t* p, int64_t count, hipStream_t s);
 
 struct MsaScoreArgs {
   const uint16_t* index_q;
   const uint16_t* index_k;
   const int32_t* block_table;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  const int32_t* cu_units;
+  const int32_t* seq_lens;
+  const int32_t* query_lens;
   float* scores;
+  // batch metadata, written by workgroup 0 when write_meta != 0
+  int32_t* cu_q;
+  int32_t* cu_k;
+  int32_t* cu_blocks;
+  int32_t* cu_units;
+  int32_t* row_req;
+  int32_t* row_pos;
   int32_t ld_s;
   int32_t ld_bt;
   int32_t num_reqs;
   int32_t num_rows;
   int32_t num_pages;
+  int32_t len_cap;
+  int32_t write_meta;
 };
 hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s);
 
@@ -161,25 +166,41 @@ struct MsaTopkArgs {
 };
 hipError_t msa_launch_topk(const MsaTopkArgs& a, hipStream_t s);
 
+// Attention over a page-16 table. Table mode: table_in / ctx_in give each
+// row's sub-pages. Fused mode (scores != null): every workgroup selects its
+// row's blocks from the block scores itself; the (split 0, head group 0)
+// workgroup of a row writes table_out / ctx_out / sel_out.
 struct MsaAttnArgs {
   const uint16_t* q;
   const void* k_cache;
   const void* v_cache;
   const float* k_scale;
   const float* v_scale;
-  const int32_t* table;
-  const int32_t* ctx;
+  const int32_t* table_in;
+  const int32_t* ctx_in;
+  const float* scores;
+  const int32_t* block_table;
+  const int32_t* row_req;
+  const int32_t* row_pos;
+  int32_t* table_out;
+  int32_t* ctx_out;
+  int32_t* sel_out;    // may be null
   uint16_t* out;
   float* partials;     // [rows][hgroups][nsplit][16*2 + 16*128]
-  int32_t* counters;   // [rows][hgroups], zero on entry, zero on exit
+  int32_t ld_table;    // row stride of the table (8*topk in fused mode)
+  int32_t ld_s;
+  int32_t ld_bt;
+  int32_t num_reqs;
+  int32_t topk;
   int32_t num_rows;
   int32_t num_q_heads;
   int32_t num_hgroups;
-  int32_t ld_table;
   int32_t max_ctx;
-  int32_t split_tok;   // tokens per workgroup, a multiple of 64
+  int32_t split_tok;   // tokens per workgroup, a multiple of 128
   int32_t nsplit;      // ceil(max_ctx / split_tok)
   int32_t num_subpages;
   float scale_log2;    // sm_scale * log2(e)
 };
+constexpr int kMaxSplitTokens = 8192;
 hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, hipStream_t s);
+hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s);

@@ -2,8 +2,7 @@
 // 关键源码片段): cumulative query / KV lengths start with a zero written on the
 // device, each query row gets its request id and absolute position
 // (context_len + i, context_len = seq_len - query_len), all without a host
-// round trip. The same launch also clears the completion counters that later
-// kernels of a step use, so a replayed graph starts from zero.
+// round trip.
 #include "msa_internal.h"
 
 using namespace msa;
@@ -92,32 +91,14 @@ __global__ __launch_bounds__(kMetaThreads) void msa_meta_kernel(MsaMetaArgs a) {
     a.row_req[n] = lo;
     a.row_pos[n] = clampi(L - ql + (n - s_cuq[lo]), -1, L - 1);
   }
-
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kMetaThreads + tid; i < a.zero_count;
-       i += static_cast<int64_t>(gridDim.x) * kMetaThreads)
-    a.zero_ptr[i] = 0;
-}
-
-__global__ __launch_bounds__(256) void msa_zero_kernel(int32_t* p, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    p[i] = 0;
 }
 
 }  // namespace
 
 hipError_t msa_launch_meta(const MsaMetaArgs& a, hipStream_t s) {
-  int64_t work = a.num_rows > a.zero_count ? a.num_rows : a.zero_count;
-  int64_t g = (work + kMetaThreads - 1) / kMetaThreads;
+  int64_t g = (static_cast<int64_t>(a.num_rows) + kMetaThreads - 1) / kMetaThreads;
   int grid = static_cast<int>(g < 1 ? 1 : (g > 64 ? 64 : g));
   hipLaunchKernelGGL(msa_meta_kernel, dim3(grid), dim3(kMetaThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t msa_launch_zero(int32_t* p, int64_t count, hipStream_t s) {
-  if (count <= 0) return hipSuccess;
-  int64_t g = (count + 255) / 256;
-  int grid = static_cast<int>(g > 1024 ? 1024 : g);
-  hipLaunchKernelGGL(msa_zero_kernel, dim3(grid), dim3(256), 0, s, p, count);
-  return hipGetLastError();
-}

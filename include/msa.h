@@ -71,9 +71,10 @@ enum {
   MSA_SUBPAGE_TOKENS = 16,
   MSA_HEAD_DIM = 128,
   MSA_INDEX_DIM = 128,
-  MSA_MAX_REQS = 8192,      /* requests per batch */
+  MSA_MAX_REQS = 4096,      /* requests per batch */
   MSA_MAX_Q_HEADS = 128,    /* query heads sharing the one KV head */
   MSA_MAX_TOPK = 8192,      /* selected blocks per row */
+  MSA_MAX_SEQ_LEN = 1048576, /* tokens per request (8192 blocks) */
   MSA_SCORE_ROWS_PER_UNIT = 64 /* query rows of one request scored per work unit */
 };
 
@@ -120,7 +121,8 @@ typedef struct msa_kv {
  * get a request id and an absolute position).
  * Writes cu_seqlens_q, cu_seqlens_k, cu_blocks, cu_units, row_req, row_pos.
  * Errors: INVALID_ARG for null pointers or num_reqs/num_rows < 0;
- * UNSUPPORTED for num_reqs > MSA_MAX_REQS.
+ * UNSUPPORTED for num_reqs > MSA_MAX_REQS or max_seq_len > MSA_MAX_SEQ_LEN
+ * (every call taking a batch checks the same).
  */
 msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch);
 

@@ -23,8 +23,11 @@ scales. Everything is a pure function of ``(config, seed)``.
 
 Buffer layouts (see ``include/msa.h``)
 --------------------------------------
-* ``index_k``  [P][128][128] bf16 bits (uint16): page, token slot, dim.
-* ``k_cache``  [P*8][16][Hkv][128]: token-major inside each 16-token sub-page.
+A 16-token tile of 128-dim rows is stored "MFMA-shuffled" as [4][4][16][8]:
+(32-dim chunk, 8-dim group, token, element); dim d of a token is at chunk d//32,
+group (d%32)//8, element d%8.
+* ``index_k``  [P][8][4][4][16][8] bf16 bits (uint16): page, 16-token tile, shuffled tile.
+* ``k_cache``  [P*8][Hkv][4][4][16][8]: sub-page, KV head, shuffled tile.
 * ``v_cache``  [P*8][Hkv][128][16]: dim-major inside each 16-token sub-page.
 * per-token-head scales [P*8][16][Hkv] fp32; scalar scales are a [1] array.
 """
@@ -44,6 +47,9 @@ PAGE = 128      # tokens per physical KV / index-K page
 SUB = 16        # tokens per sub-page of the page-16 view
 HEAD_DIM = 128
 INDEX_DIM = 128
+
+TILE_SHAPE = (4, 4, SUB, 8)                 # shuffled 16-token x 128-dim tile
+INDEX_PAGE_SHAPE = (PAGE // SUB,) + TILE_SHAPE
 
 KV_BF16 = 0
 KV_FP8 = 1
@@ -158,9 +164,9 @@ class Batch:
     scale_mode: int
     sm_scale: float
     index_q: np.ndarray         # [N][128] uint16 (bf16 bits)
-    index_k: np.ndarray         # [P][128][128] uint16
+    index_k: np.ndarray         # [P][8][4][4][16][8] uint16
     q: np.ndarray               # [N][Hq][128] uint16
-    k_cache: np.ndarray         # [8P][16][Hkv][128] uint16 or uint8
+    k_cache: np.ndarray         # [8P][Hkv][4][4][16][8] uint16 or uint8
     v_cache: np.ndarray         # [8P][Hkv][128][16] uint16 or uint8
     k_scale: np.ndarray | None  # [1] or [8P][16][Hkv] float32
     v_scale: np.ndarray | None
@@ -224,13 +230,13 @@ def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
                      k_cache=e16 if kv_dtype == KV_BF16 else e8,
                      v_cache=e16 if kv_dtype == KV_BF16 else e8, k_scale=None, v_scale=None)
     index_q = bf16_normal(rng, (N, INDEX_DIM))
-    index_k = bf16_normal(rng, (P, PAGE, INDEX_DIM))
+    index_k = bf16_normal(rng, (P,) + INDEX_PAGE_SHAPE)
     q = bf16_normal(rng, (N, hq, HEAD_DIM))
     if kv_dtype == KV_BF16:
-        k_cache = bf16_normal(rng, (P * 8, SUB, hkv, HEAD_DIM))
+        k_cache = bf16_normal(rng, (P * 8, hkv) + TILE_SHAPE)
         v_cache = bf16_normal(rng, (P * 8, hkv, HEAD_DIM, SUB))
     else:
-        k_cache = fp8_normal(rng, (P * 8, SUB, hkv, HEAD_DIM))
+        k_cache = fp8_normal(rng, (P * 8, hkv) + TILE_SHAPE)
         v_cache = fp8_normal(rng, (P * 8, hkv, HEAD_DIM, SUB))
     k_scale = v_scale = None
     if scale_mode == SCALE_SCALAR:

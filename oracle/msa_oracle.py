@@ -118,13 +118,24 @@ def num_blocks(v: int) -> int:
 # ---------------------------------------------------------------------------
 # Step 2: index scores and per-block pooling
 # ---------------------------------------------------------------------------
+def tile_row(tile: np.ndarray, tok: int) -> np.ndarray:
+    """The 128 values of token `tok` of a stored 16-token tile. Tiles are kept
+    as [4][4][16][8] (32-dim chunk, 8-dim group, token, element): dim d of the
+    token is at [d // 32][(d % 32) // 8][tok][d % 8]."""
+    return tile[:, :, tok, :].reshape(-1)
+
+
 def index_keys_of_request(index_k_bits: np.ndarray, bt_row: np.ndarray, ntok: int) -> np.ndarray:
     """Logical index keys [ntok][128] of one request: token t lives in physical
-    page bt_row[t // 128], slot t % 128 (the page-128 cache, [P1] 实现拆解 item 3)."""
-    out = np.empty((ntok, index_k_bits.shape[-1]), dtype=np.float64)
+    page bt_row[t // 128], slot s = t % 128 (the page-128 cache, [P1] 实现拆解
+    item 3), i.e. in 16-token tile s // 16 of the page, as token s % 16."""
+    out = np.empty((ntok, 128), dtype=np.float64)
     for j in range(num_blocks(ntok)):
         lo, hi = j * PAGE, min((j + 1) * PAGE, ntok)
-        out[lo:hi] = bf16_to_f64(index_k_bits[int(bt_row[j]), : hi - lo])
+        page = index_k_bits[int(bt_row[j])]               # [8][4][4][16][8]
+        # (tile, chunk, group, token, element) -> (tile, token, chunk, group, element)
+        rows = page.transpose(0, 3, 1, 2, 4).reshape(PAGE, 128)
+        out[lo:hi] = bf16_to_f64(rows[: hi - lo])
     return out
 
 
@@ -230,12 +241,12 @@ def kv_token(cache: np.ndarray, bt_row: np.ndarray, t: int, hkv: int, kv_dtype: 
              plane: str) -> np.ndarray:
     """Raw stored values of one token for KV head hkv, addressed logically:
     physical page P = bt_row[t // 128], sub-page 8P + (t % 128) // 16, slot t % 16.
-    K sub-pages are token-major [16][Hkv][128]; V sub-pages are dim-major
-    [Hkv][128][16]."""
+    K sub-pages are shuffled tiles [Hkv][4][4][16][8] (see tile_row); V
+    sub-pages are dim-major [Hkv][128][16]."""
     page = int(bt_row[t // PAGE])
     sub = SUBS_PER_PAGE * page + (t % PAGE) // SUB
     slot = t % SUB
-    raw = cache[sub, slot, hkv, :] if plane == "k" else cache[sub, hkv, :, slot]
+    raw = tile_row(cache[sub, hkv], slot) if plane == "k" else cache[sub, hkv, :, slot]
     return bf16_to_f64(raw) if kv_dtype == 0 else e4m3fn_to_f64(raw)
 
 
@@ -255,8 +266,7 @@ def token_scale(scale: np.ndarray | None, scale_mode: int, bt_row: np.ndarray, t
 
 def dequant_tokens(cache, scale, scale_mode, kv_dtype, bt_row, tokens, hkv, plane):
     """K-hat / V-hat rows: scale x stored value, float64."""
-    out = np.empty((len(tokens), cache.shape[-1] if plane == "k" else cache.shape[-2]),
-                   dtype=np.float64)
+    out = np.empty((len(tokens), 128), dtype=np.float64)
     for i, t in enumerate(tokens):
         out[i] = token_scale(scale, scale_mode, bt_row, t, hkv) * \
             kv_token(cache, bt_row, t, hkv, kv_dtype, plane)
@@ -284,7 +294,7 @@ def sparse_attention_row(q_row_bits: np.ndarray, k_cache, v_cache, kv_dtype: int
     table, so that the GPU's table walk is checked against the definition.
     Query head h reads KV head h // (Hq / Hkv)."""
     hq = q_row_bits.shape[0]
-    hkv_n = k_cache.shape[2]
+    hkv_n = k_cache.shape[1]
     group = hq // hkv_n
     tokens = [t for b in sel for t in range(PAGE * int(b), min(PAGE * (int(b) + 1), v))]
     q = bf16_to_f64(q_row_bits)
@@ -300,7 +310,7 @@ def dense_causal_attention_row(q_row_bits, k_cache, v_cache, kv_dtype, scale_mod
                                v_scale, bt_row, v, sm_scale) -> np.ndarray:
     """Textbook causal attention of one row over every visible key t < v."""
     hq = q_row_bits.shape[0]
-    hkv_n = k_cache.shape[2]
+    hkv_n = k_cache.shape[1]
     group = hq // hkv_n
     q = bf16_to_f64(q_row_bits)
     out = np.zeros((hq, q.shape[1]), dtype=np.float64)
@@ -365,14 +375,14 @@ def attention_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows) -> np.
     token u, slot u % 16). Used to check the device's attention on the device's
     own table, so selection near-ties do not mix into attention error."""
     out = np.zeros((len(rows), batch.num_q_heads, batch.q.shape[-1]), dtype=np.float64)
-    hkv_n = batch.k_cache.shape[2]
+    hkv_n = batch.k_cache.shape[1]
     group = batch.num_q_heads // hkv_n
     for i, n in enumerate(rows):
         c = int(ctx[n])
         q = bf16_to_f64(batch.q[n])
         for g in range(hkv_n):
-            kh = np.empty((c, batch.k_cache.shape[-1]))
-            vh = np.empty((c, batch.v_cache.shape[-2]))
+            kh = np.empty((c, 128))
+            vh = np.empty((c, 128))
             for u in range(c):
                 sub = int(table[n][u // SUB])
                 slot = u % SUB
@@ -384,7 +394,7 @@ def attention_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows) -> np.
                     ks = float(batch.k_scale[sub, slot, g])
                     vs = float(batch.v_scale[sub, slot, g])
                 dec = bf16_to_f64 if batch.kv_dtype == 0 else e4m3fn_to_f64
-                kh[u] = ks * dec(batch.k_cache[sub, slot, g, :])
+                kh[u] = ks * dec(tile_row(batch.k_cache[sub, g], slot))
                 vh[u] = vs * dec(batch.v_cache[sub, g, :, slot])
             out[i, g * group:(g + 1) * group] = softmax_attention(
                 q[g * group:(g + 1) * group], kh, vh, batch.sm_scale)

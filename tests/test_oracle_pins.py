@@ -33,18 +33,24 @@ def fp8_codes(x):
     return t.view(torch.uint8).numpy().copy()
 
 
+def shuffle_into(tile, tok, row):
+    # token `tok` of a [4][4][16][8] tile: dim d -> [d // 32][(d % 32) // 8][tok][d % 8]
+    for d in range(128):
+        tile[d // 32, (d % 32) // 8, tok, d % 8] = row[d]
+
+
 def write_paged(logical_k, logical_v, page_of_block, num_pages, dtype=np.uint16):
     """Scatter logical K [T][Hkv][D] and V [T][Hkv][D] (already encoded) into
-    K sub-pages [8P][16][Hkv][D] (token-major) and V sub-pages [8P][Hkv][D][16]
-    (dim-major)."""
+    K sub-pages [8P][Hkv][4][4][16][8] (shuffled tiles) and V sub-pages
+    [8P][Hkv][D][16] (dim-major)."""
     T, hkv, D = logical_k.shape
-    kc = np.zeros((num_pages * 8, 16, hkv, D), dtype=dtype)
+    kc = np.zeros((num_pages * 8, hkv, 4, 4, 16, 8), dtype=dtype)
     vc = np.zeros((num_pages * 8, hkv, D, 16), dtype=dtype)
     for t in range(T):
         page = page_of_block[t // 128]
         sub = page * 8 + (t % 128) // 16
-        kc[sub, t % 16] = logical_k[t]
         for h in range(hkv):
+            shuffle_into(kc[sub, h], t % 16, logical_k[t, h])
             vc[sub, h, :, t % 16] = logical_v[t, h]
     return kc, vc
 
@@ -60,9 +66,10 @@ def write_scales(logical_s, page_of_block, num_pages):
 
 def write_index_pages(logical_ik, page_of_block, num_pages):
     T, D = logical_ik.shape
-    out = np.zeros((num_pages, 128, D), dtype=np.uint16)
+    out = np.zeros((num_pages, 8, 4, 4, 16, 8), dtype=np.uint16)
     for t in range(T):
-        out[page_of_block[t // 128], t % 128] = logical_ik[t]
+        s = t % 128
+        shuffle_into(out[page_of_block[t // 128], s // 16], s % 16, logical_ik[t])
     return out
 
 
@@ -179,7 +186,7 @@ def test_scores_one_hot_query_reads_one_coordinate():
 
 def test_scores_all_ones_equal_dim():
     L = 200
-    ik = np.full((2, 128, 128), bf16_bits([1.0])[0], np.uint16)
+    ik = np.full((2, 8, 4, 4, 16, 8), bf16_bits([1.0])[0], np.uint16)
     keys = O.index_keys_of_request(ik, np.array([1, 0]), L)
     s = O.token_scores(bf16_bits(np.ones(128)), keys, L)
     assert np.all(s == 128.0)
@@ -194,8 +201,9 @@ def test_scores_brute_force_tiny():
     s = O.token_scores(q, keys, L)
     qf = [float(x) for x in torch.from_numpy(q.view(np.int16).copy()).view(torch.bfloat16).float()]
     for t in range(L):
-        page = int(pages[t // 128])
-        row = torch.from_numpy(ik[page, t % 128].view(np.int16).copy()).view(torch.bfloat16).float()
+        page, slot = int(pages[t // 128]), t % 128
+        raw = np.array([ik[page, slot // 16, d // 32, (d % 32) // 8, slot % 16, d % 8] for d in range(128)], np.uint16)
+        row = torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).float()
         ref = math.fsum(qf[d] * float(row[d]) for d in range(128))
         assert abs(s[t] - ref) <= 1e-12 * max(1.0, abs(ref))
 
@@ -218,6 +226,7 @@ def test_pool_planted_maxima_and_partial_block():
     L = 3 * 128 + 10           # 4 blocks, the last one partial
     rng = syn.SplitMix64(7)
     logical = bf16_bits(0.01 * O.bf16_to_f64(syn.bf16_normal(rng, (L + 118, 128))))
+    logical = logical.reshape(L + 118, 128)
     q = np.zeros(128, np.float32)
     q[5] = 1.0
     # values at block edges catch a pooled range that is off by one at either end
