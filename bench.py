@@ -44,8 +44,18 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="cache copies cycled (0: enough for 768 MB)")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--counters", action="store_true",
+                   help="counter pass: 8 plain copies of 256 MiB, then 8 index-score launches, no timing")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of --counters into "
+                        "the traffic summary under profiles/")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="turn a rocprofv3 --kernel-trace --stats csv output into a summary under profiles/")
     return p.parse_args()
+
+
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = "index_score_traffic_{}.json"
 
 
 def algorithmic_bytes(b, ctx):
@@ -65,18 +75,24 @@ def algorithmic_bytes(b, ctx):
     return {"step": idx_k + N * 256 + kv + qo + small, "score": score_launch, "attn": kv + qo + N * 8 * topk * 4}
 
 
-def cpu_baseline(b, rows):
-    """The oracle as it stands, single-threaded, on `rows` of the workload."""
+def cpu_baseline(b, rows, budget_s=10.0):
+    """The oracle as it stands, single-threaded, on `rows` of the workload,
+    repeated until about budget_s seconds of CPU work."""
     from threadpoolctl import threadpool_limits
 
     from oracle import msa_oracle as O
+    passes = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        O.decode_step(b, rows=rows)
-        dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(rows)} of {b.num_rows} rows of the {b.name} workload, full step "
-                      f"(metadata, scores, pooling, selection, table, attention) in {dt:.1f} s"}
+        while True:
+            O.decode_step(b, rows=rows)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+    return {"value": passes * len(rows) / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over {len(rows)} of {b.num_rows} rows of the {b.name} workload, "
+                      f"full step (metadata, scores, pooling, selection, table, attention), {dt:.1f} s"}
 
 
 def main():
@@ -85,6 +101,13 @@ def main():
         print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_counters:
+        summarize_counters(args.workload, *args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.workload, args.summarize_trace)
+        return
 
     import numpy as np
     import torch
@@ -147,6 +170,20 @@ def main():
     for c in range(copies):
         step(c)
     torch.cuda.synchronize()
+    if args.counters:
+        # counter pass: plain copies of known size, then the dominant kernel
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(8):
+            torch.mul(src, 1, out=dst)   # an elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        for i in range(8):
+            msa.msa_index_score(batches[i % copies], index_q, index_k, scores, ld_s)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_pass": args.workload, "copy_bytes": COPY_BYTES,
+                          "score_algorithmic_bytes": algorithmic_bytes(b, ctx.cpu().numpy())["score"]}))
+        return
     ctx_host = ctx.cpu().numpy()
     nbytes = algorithmic_bytes(b, ctx_host)
 
@@ -179,32 +216,40 @@ def main():
     print(f"[bench] {args.workload}: {sec * 1e6:.2f} us/step over {args.steps} steps, {copies} copies",
           file=sys.stderr, flush=True)
 
-    # per-entry-point times with events on the launching stream (eager launches)
+    # Dominant kernel: back-to-back msa_index_score launches (cycling the cache
+    # copies) captured in one graph and bracketed by HIP events on the
+    # launching stream, so the per-launch figure is the kernel's own duration
+    # plus the small gap between graph nodes.
+    reps = 32
     stream = torch.cuda.current_stream()
-
-    def time_calls(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i in range(reps):
-            evs[i][0].record(stream)
-            fn(i % copies)
-            evs[i][1].record(stream)
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    g_score = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        msa.msa_index_score(batches[0], index_q, index_k, scores, ld_s)
+        with torch.cuda.graph(g_score, stream=gs):
+            for i in range(reps):
+                msa.msa_index_score(batches[i % copies], index_q, index_k, scores, ld_s)
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_score_runs = []
+    for _ in range(5):
+        e0.record(stream)
+        g_score.replay()
+        e1.record(stream)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(e) for a, e in evs) / reps * 1e3   # us
-
-    reps = max(args.steps, 20)
-    t_meta = time_calls(lambda c: msa.msa_build_metadata(batches[c]), reps)
-    t_score = time_calls(lambda c: msa.msa_index_score(batches[c], index_q, index_k, scores, ld_s), reps)
-    t_topk = time_calls(lambda c: msa.msa_topk_block_table(batches[c], scores, ld_s, topk, table, ctx, None), reps)
-    t_attn = time_calls(lambda c: msa.msa_sparse_paged_attn(q, N, hq, kv, table, 8 * topk, ctx, 128 * topk,
-                                                            b.sm_scale, out, ws, wsb), reps)
+        t_score_runs.append(e0.elapsed_time(e1) * 1e3 / reps)
+    t_score = sorted(t_score_runs)[len(t_score_runs) // 2]
 
     score_gbps = nbytes["score"] / (t_score * 1e-6) / 1e9
     traffic = None
-    if os.path.exists(args.traffic_json):
+    tpath = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(args.workload))
+    if os.path.exists(tpath):
         try:
-            tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == args.workload and tj.get("kernel_source_hash") == source_hash():
-                traffic = tj.get("score_bytes_per_launch")
+            tj = json.load(open(tpath))
+            if tj.get("kernel_source_hash") == source_hash():
+                traffic = tj.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
 
@@ -227,14 +272,108 @@ def main():
         "step_hbm_gbps": nbytes["step"] / sec / 1e9,
         "step_hbm_frac": nbytes["step"] / sec / 1e9 / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": nbytes["step"],
-        "kernel_us": {"metadata": t_meta, "index_score": t_score, "topk_table": t_topk, "attention": t_attn},
         "roofline": {"kernel": "msa_score_kernel (msa_index_score)", "bound": "hbm", "achieved": score_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},
     }
     if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, list(range(min(N, 8))))
     print(json.dumps(res), flush=True)
+
+
+def _counter_rows(d):
+    """(kernel name, counter name, value) rows of a rocprofv3 --pmc csv output."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for rec in csv.DictReader(fh):
+                rows.append((rec.get("Kernel_Name", ""), rec.get("Counter_Name", ""),
+                             float(rec.get("Counter_Value", "nan"))))
+    return rows
+
+
+PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <out> -o run -- "
+           "python3 -u bench.py --workload {workload} --counters")
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- "
+             "python3 -u bench.py --workload {workload} --steps 50 --warmup 10 --no-cpu-baseline")
+
+
+def _short(name):
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def summarize_counters(workload, fetch_dir, write_dir):
+    """Scale every kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what
+    the same counter reads for the calibration kernel of the --counters pass
+    (an elementwise multiply that reads and writes COPY_BYTES bytes). Writes
+    the index-score kernel's traffic for bench.py and a per-kernel table."""
+    import statistics
+    out = {"workload": workload, "kernel": "msa_score_kernel", "copy_bytes": COPY_BYTES,
+           "kernel_source_hash": source_hash()}
+    table = {}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r[1] == counter]
+        copy = [v for k, _, v in rows if "MulFunctor" in k]
+        if not copy:
+            raise SystemExit(f"no calibration-kernel {counter} rows in {d}")
+        c_kib = statistics.median(copy)
+        factor = COPY_BYTES / (c_kib * 1024.0)
+        per = {}
+        for k, _, v in rows:
+            if "msa_" in k:
+                per.setdefault(_short(k), []).append(v)
+        for k, vals in per.items():
+            table.setdefault(k, {})[counter] = statistics.median(vals) * 1024.0 * factor
+        s_kib = statistics.median(per["msa_score_kernel"])
+        out[counter] = {"calibration_kib_per_dispatch": c_kib, "score_kib_per_dispatch": s_kib,
+                        "scale_factor": factor, "score_bytes": s_kib * 1024.0 * factor}
+        total += s_kib * 1024.0 * factor
+    out["bytes_per_launch"] = total
+    prof = os.path.join(ROOT, "profiles")
+    with open(os.path.join(prof, TRAFFIC_FILE.format(workload)), "w") as fh:
+        json.dump(out, fh, indent=1)
+    lines = [f"# HBM traffic per dispatch, {workload} workload", "",
+             "Commands (one counter per run, outputs in <out>):", "",
+             "    " + PMC_CMD.format(counter="FETCH_SIZE", workload=workload),
+             "    " + PMC_CMD.format(counter="WRITE_SIZE", workload=workload),
+             "    python3 bench.py --workload {} --summarize-counters <fetch-out> <write-out>".format(workload), "",
+             "Calibration: an elementwise multiply over {} MiB reads FETCH_SIZE {:.0f} KiB and WRITE_SIZE "
+             "{:.0f} KiB per dispatch, so the counters are scaled by {:.3f} (fetch) and {:.3f} (write)."
+             .format(COPY_BYTES >> 20, out["FETCH_SIZE"]["calibration_kib_per_dispatch"],
+                     out["WRITE_SIZE"]["calibration_kib_per_dispatch"], out["FETCH_SIZE"]["scale_factor"],
+                     out["WRITE_SIZE"]["scale_factor"]), "",
+             "| kernel | fetched MB | written MB |", "|---|---|---|"]
+    for k, v in sorted(table.items()):
+        lines.append(f"| {k} | {v.get('FETCH_SIZE', float('nan')) / 1e6:.3f} | {v.get('WRITE_SIZE', float('nan')) / 1e6:.3f} |")
+    lines += ["", f"Kernel source hash (msa_score.hip + msa_internal.h): {out['kernel_source_hash']}"]
+    with open(os.path.join(prof, f"counters_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(json.dumps(out))
+
+
+def summarize_trace(workload, trace_dir):
+    """Per-kernel duration table from a rocprofv3 --stats csv output."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    lines = [f"# Kernel durations, {workload} workload", "", "Command:", "",
+             "    " + TRACE_CMD.format(workload=workload), "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    with open(f[0]) as fh:
+        for rec in csv.DictReader(fh):
+            if "msa_" not in rec["Name"]:
+                continue
+            lines.append(f"| {_short(rec['Name'])} | {rec['Calls']} | {float(rec['AverageNs']) / 1e3:.2f} | "
+                         f"{float(rec['MinNs']) / 1e3:.2f} | {float(rec['MaxNs']) / 1e3:.2f} |")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def source_hash() -> str:

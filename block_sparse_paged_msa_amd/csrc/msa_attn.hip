@@ -302,8 +302,8 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArg
 }
 
 // Fused mode: select the row's blocks from its scores, then attend. The
-// row's scores (as keys) and block-table entries go to dynamic LDS, read in
-// the same round as Q; the merge buffers reuse that LDS after the selection.
+// row's scores (as keys) and block-table entries go to dynamic LDS; the merge
+// buffers reuse that LDS after the selection.
 template <int KV_FP8, int SCALE_MODE>
 __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // keys[nbmax], pages[nbmax] | MergeLds
@@ -315,19 +315,26 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
   const int hgi = rest % a.num_hgroups;
   const int n = rest / a.num_hgroups;
   const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
-  const int r = clampi(a.row_req[n], 0, a.num_reqs - 1);
-  const int v = a.row_pos[n] + 1;
-  const int nb = clampi((v + kPage - 1) / kPage, 0, nbmax);
+  // round 1: the row's whole score row (nb <= nbmax is not known yet), its
+  // request and position, and Q; round 2: the request's block-table entries,
+  // held in registers until the selection needs them
   const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
-  const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
   uint32_t* keys = s_dyn;
   int* pages = reinterpret_cast<int*>(s_dyn + nbmax);
-  for (int e = tid; e < nb; e += kAttnThreads) {
-    keys[e] = order_key(srow[e]);
-    pages[e] = bt[e];
-  }
+  for (int e = tid; e < nbmax; e += kAttnThreads) keys[e] = order_key(srow[e]);
+  const int r = clampi(a.row_req[n], 0, a.num_reqs - 1);
+  const int v = a.row_pos[n] + 1;
   bf16x8 qb[4];
   load_q(a, n, hgi, qb);
+  const int nb = clampi((v + kPage - 1) / kPage, 0, nbmax);
+  const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
+  constexpr int kRegBlocks = 4;  // block-table entries held per thread
+  int btreg[kRegBlocks];
+#pragma unroll
+  for (int i = 0; i < kRegBlocks; ++i) {
+    const int e = tid + i * kAttnThreads;
+    btreg[i] = e < nb ? bt[e] : 0;
+  }
   __syncthreads();
 
   const int nblk = a.split_tok / kPage;
@@ -345,7 +352,12 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
       for (int i = 0; i < 8; ++i) trow[8 * pos + i] = 8 * page + i;
       if (selrow) selrow[pos] = e;
     }
-  }, &ctx);
+  }, &ctx, [&] {
+#pragma unroll
+    for (int i = 0; i < kRegBlocks; ++i)
+      if (tid + i * kAttnThreads < nb) pages[tid + i * kAttnThreads] = btreg[i];
+    for (int e = tid + kRegBlocks * kAttnThreads; e < nb; e += kAttnThreads) pages[e] = bt[e];
+  });
   if (writer) {
     for (int m = 8 * kk + tid; m < 8 * a.topk; m += kAttnThreads) trow[m] = 0;
     if (selrow)
@@ -369,26 +381,33 @@ __global__ __launch_bounds__(kAttnThreads) void msa_merge_kernel(MsaAttnArgs a, 
   const int tid = threadIdx.x;
   const int hgi = blockIdx.x % a.num_hgroups;
   const int n = blockIdx.x / a.num_hgroups;
-  const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
-  const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
-  if (nsplit_n <= 1) return;
   const int th = tid >> 4, td = (tid & 15) * 8;
   const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kPartStride;
-  float Mg = -INFINITY, Lg = 0.f;
-  f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit_n; s0 += 16) {  // sixteen splits' loads in flight at a time
-    float ms[16], ls[16];
-    f32x4 x0[16], x1[16];
+  // the first sixteen partials are requested in the same round as ctx (every
+  // slot below nsplit exists in the workspace; unused ones are ignored)
+  constexpr int kBatch = 16;
+  float ms[kBatch], ls[kBatch];
+  f32x4 x0[kBatch], x1[kBatch];
+  auto fetch = [&](int s0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float* ps = base + static_cast<size_t>(min(s0 + j, nsplit_n - 1)) * kPartStride;
+    for (int j = 0; j < kBatch; ++j) {
+      const float* ps = base + static_cast<size_t>(min(s0 + j, a.nsplit - 1)) * kPartStride;
       ms[j] = ps[th];
       ls[j] = ps[kHeadTile + th];
       x0[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td);
       x1[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4);
     }
+  };
+  fetch(0);
+  const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
+  const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
+  if (nsplit_n <= 1) return;
+  float Mg = -INFINITY, Lg = 0.f;
+  f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit_n; s0 += kBatch) {
+    if (s0 > 0) fetch(s0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < nsplit_n) {
         const float mn = fmaxf(Mg, ms[j]);
         const float c_old = fast_exp2(Mg - mn);  // 0 on the first split (Mg = -inf)

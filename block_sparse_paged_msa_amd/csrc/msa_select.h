@@ -35,13 +35,16 @@ struct SelectLds {
 
 // Keeps K' = min(topk, nb) of the nb keys; calls emit(rank, block) for each
 // kept block (ranks 0..K'-1 in ascending block order, any thread may emit).
+// before_compaction() runs in every thread after the threshold is known and
+// before the first emit(); emit(rank, block) runs in the thread that owns
+// block = base + threadIdx.x of one 256-block chunk.
 // Returns K'; *ctx_out gets sum over kept blocks of min(128, v - 128*block)
 // in every thread: every block but the last (nb-1) holds 128 visible tokens,
 // so the sum is 128*K' minus the last block's invisible tail when it is kept.
 // All 256 threads must call it.
-template <typename Emit>
+template <typename Emit, typename BeforeCompaction>
 __device__ __forceinline__ int select_row(const uint32_t* keys, int nb, int topk, int v, SelectLds& sl, Emit emit,
-                                          int* ctx_out) {
+                                          int* ctx_out, BeforeCompaction before_compaction) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kk = min(topk, nb);
   const bool partial = kk < nb;
@@ -93,6 +96,8 @@ __device__ __forceinline__ int select_row(const uint32_t* keys, int nb, int topk
     T = prefix;
     eq_total = sl.eq_total;  // keys equal to T (the last pass bins them exactly)
   }
+
+  before_compaction();  // caller hook: per-thread data that emit() reads (same thread, no barrier)
 
   // every key equal to T is kept unless the tie straddles the cut
   const bool all_eq_kept = !partial || need == eq_total;

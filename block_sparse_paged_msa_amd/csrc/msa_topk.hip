@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kSelectThreads) void msa_topk_kernel(MsaTopkArgs a)
 #pragma unroll
     for (int i = 0; i < 8; ++i) trow[8 * pos + i] = sub0 + i;
     if (selrow) selrow[pos] = e;
-  }, &ctx);
+  }, &ctx, [] {});
 
   // zero tail of the table row, -1 tail of the selection, never past 8*topk
   for (int m = 8 * kk + tid; m < 8 * a.topk; m += kSelectThreads) trow[m] = 0;
