@@ -26,17 +26,22 @@
  *     head and one index head.
  *
  * Data layouts (all row-major, innermost last)
+ *   A "tile" is 16 tokens x 128 dims stored MFMA-shuffled as [4][4][16][8]:
+ *   (32-dim chunk, 8-dim group, token, element); dim d of token t is at
+ *   [d/32][(d%32)/8][t][d%8], so each 64-lane MFMA operand is one contiguous
+ *   run in memory.
  *   index_q      [N][128]                bf16
- *   index_k      [P][128][128]           bf16   page, token slot, dim
+ *   index_k      [P][8][4][4][16][8]     bf16   page, 16-token tile, shuffled tile
  *   q, out       [N][Hq][128]            bf16
- *   k_cache      [8P][16][Hkv][128]      bf16 | fp8 e4m3fn   token-major sub-pages
+ *   k_cache      [8P][Hkv][4][4][16][8]  bf16 | fp8 e4m3fn   one shuffled tile per sub-page
  *   v_cache      [8P][Hkv][128][16]      bf16 | fp8 e4m3fn   dim-major sub-pages
  *   k/v_scale    scalar: [1] fp32;  per-token-head: [8P][16][Hkv] fp32
  *   block_table  [R][ld_bt]              int32  physical page-128 ids
  *   block_scores [N][ld_s]               fp32
  *   sparse_table [N][ld_table]           int32  page-16 sub-page ids
  *   Sub-page i of physical page p is 8*p + i. Token t of a request lives in
- *   page block_table[r][t / 128], slot t % 128.
+ *   page block_table[r][t / 128], slot s = t % 128: tile s / 16 of the index-K
+ *   page, sub-page 8*page + s / 16 of the K/V caches, token s % 16 there.
  */
 #ifndef MSA_H_
 #define MSA_H_
@@ -104,7 +109,7 @@ typedef struct msa_batch {
 
 /* K/V cache description (host struct with device pointers). */
 typedef struct msa_kv {
-  const void* k_cache;   /* [8P][16][Hkv][128] */
+  const void* k_cache;   /* [8P][Hkv][4][4][16][8] */
   const void* v_cache;   /* [8P][Hkv][128][16] */
   const float* k_scale;  /* NULL (MSA_SCALE_NONE), [1] or [8P][16][Hkv] */
   const float* v_scale;
@@ -134,8 +139,9 @@ msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch);
  *   block_scores[n][b] = max over visible tokens t of block b (t <= row_pos[n])
  *                        of dot(index_q[n], index_k[token t]),  b < nb_n
  *   block_scores[n][b] = -inf for nb_n <= b < ld_s,  nb_n = ceil((row_pos[n]+1)/128)
- * Requires msa_build_metadata on the same batch earlier on the stream.
- * index_q [N][128] bf16, index_k [P][128][128] bf16, block_scores [N][ld_s] fp32.
+ * Reads seq_lens / query_lens directly (the metadata arrays are not needed).
+ * index_q [N][128] bf16, index_k [P][8][4][4][16][8] bf16 (see the layouts
+ * above), block_scores [N][ld_s] fp32.
  * Errors: INVALID_ARG for null pointers; UNSUPPORTED if ld_s < ceil(max_seq_len/128).
  */
 msa_status msa_index_score(msa_stream_t stream, const msa_batch* batch, const void* index_q,
@@ -145,6 +151,7 @@ msa_status msa_index_score(msa_stream_t stream, const msa_batch* batch, const vo
  * msa_topk_block_table — fused top-k selection, page-16 sparse block table and
  * context lengths (#54682 page, 实现拆解 items 1 and 4; #47287 page, 实现拆解
  * item 3 and 评论区精华 on keeping the zero padding inside the row).
+ * Requires row_req / row_pos from msa_build_metadata (or msa_sparse_decode).
  * For each row n with nb_n eligible blocks, K' = min(topk, nb_n) blocks are kept
  * under the total order (score descending, block id ascending, -0 == +0) and
  * listed by ascending block id b_0 < ... < b_{K'-1}:
@@ -175,7 +182,8 @@ msa_status msa_topk_block_table(msa_stream_t stream, const msa_batch* batch,
  *   max_ctx (host): upper bound of ctx_lens; larger device values are clamped.
  *   ld_table: row stride of sparse_table, >= ceil(max_ctx/16).
  *   workspace: >= msa_workspace_bytes(num_rows, num_q_heads, max_ctx, 0) bytes,
- *   256-byte aligned; its contents need no initialisation.
+ *   256-byte aligned; its contents need no initialisation; may be NULL when
+ *   that size is 0 (every row fits one split).
  * Errors: INVALID_ARG for null required pointers or sizes < 0; UNSUPPORTED for
  * num_kv_heads != 1, num_q_heads > MSA_MAX_Q_HEADS, bad dtype/scale pairing
  * (MSA_SCALE_NONE with fp8); WORKSPACE if the workspace is too small.
@@ -190,15 +198,16 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  * msa_sparse_decode — the whole decode step on one stream with no host
  * synchronisation: metadata, index score + pooling, top-k + page-16 table +
  * context lengths, sparse paged attention and the split merge (#54682 page,
- * 实现拆解 items 2-3: the indexer writes the sparse table that attention then
- * consumes; completion counters are reset in-stream so the step can be
- * replayed from a HIP graph).
+ * 实现拆解 items 2-3: the indexer's selection and sparse table feed attention
+ * in the same step). Three launches; no state is carried between calls, so the
+ * step can be captured in a HIP graph and replayed. Also writes the batch
+ * metadata arrays (as msa_build_metadata does).
  *   sparse_table [N][8*topk], ctx_lens [N]: written (outputs of the top-k step).
  *   sel_blocks [N][topk]: optional (NULL skips it).
  *   block_scores [N][ld_s]: optional; when NULL the scores live in the
  *   workspace. ld_s >= ceil(max_seq_len/128).
  *   workspace: >= msa_workspace_bytes(num_rows, num_q_heads, 128*topk,
- *   block_scores ? 0 : ld_s) bytes.
+ *   block_scores ? 0 : ld_s) bytes (NULL allowed when that is 0).
  * Errors: union of the errors of the steps.
  */
 msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q,
