@@ -7,8 +7,8 @@ sparse paged attention + split merge (msa_sparse_decode) over one batch of the
 named synthetic workload (default: 8 requests x 1 row, L ~ U{8192..32768},
 top-k 16, 16 query heads, bf16). The step's inputs live in HBM; several copies
 of the caches at different addresses are cycled so that no step finds the
-previous step's data in the 256 MB Infinity Cache. Steps are replayed from HIP
-graphs (one per copy). Prints one JSON line.
+previous step's data in the 256 MB Infinity Cache. Steps are replayed from a
+HIP graph holding one step per copy. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -187,12 +187,21 @@ def main():
     ctx_host = ctx.cpu().numpy()
     nbytes = algorithmic_bytes(b, ctx_host)
 
-    run = step
-    if not args.eager:
+    if args.eager:
+        def run_steps(k0, k):
+            for i in range(k0, k0 + k):
+                step(i % copies)
+    else:
+        # one graph holding one step per cache copy, plus one graph per copy for
+        # a remainder, so that exactly the requested number of steps is replayed
         graphs = []
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
+            g_all = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_all, stream=s):
+                for c in range(copies):
+                    step(c)
             for c in range(copies):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s):
@@ -201,15 +210,17 @@ def main():
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
 
-        def run(c):
-            graphs[c].replay()
+        def run_steps(k0, k):
+            full, rem = divmod(k, copies)
+            for _ in range(full):
+                g_all.replay()
+            for i in range(rem):
+                graphs[i].replay()
 
-    for i in range(args.warmup):
-        run(i % copies)
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i % copies)
+    run_steps(0, args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec = (t1 - t0) / args.steps

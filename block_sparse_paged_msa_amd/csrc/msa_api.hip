@@ -149,8 +149,11 @@ msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, 
   a.num_pages = b->num_pages;
   a.len_cap = len_cap(b);
   a.write_meta = write_meta ? 1 : 0;
-  // units <= blocks_bound * sum_r ceil(ql_r/64) <= blocks_bound * (R + ceil(N/64))
-  const int64_t units = static_cast<int64_t>(blocks_bound(b)) * (b->num_reqs + ceil_div(b->num_rows, kRowsPerUnit));
+  // first-group slots r*S + j, S = ceil(len_cap/128); extra row groups are at
+  // most S * floor(N/64) (sum_r (ceil(ql_r/64) - 1) <= N/64)
+  const int64_t S = ceil_div(a.len_cap, kPage) > 0 ? ceil_div(a.len_cap, kPage) : 1;
+  a.blocks_per_req = static_cast<int32_t>(S);
+  const int64_t units = S * b->num_reqs + S * (b->num_rows / kRowsPerUnit);
   int64_t wgs = ceil_div(units, 4);
   const int64_t cap = 8LL * cu_count();
   if (wgs > cap) wgs = cap;

@@ -302,22 +302,25 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArg
 }
 
 // Fused mode: select the row's blocks from its scores, then attend. The
-// row's scores (as keys) and block-table entries go to dynamic LDS; the merge
-// buffers reuse that LDS after the selection.
+// row's keys and block-table entries sit in dynamic LDS; every wave runs the
+// selection itself (wave_select / wave_compact) and keeps only the pages of
+// its own sub-pages, so the waves need no barrier between selection and
+// attention. The merge buffers reuse the key area afterwards.
 template <int KV_FP8, int SCALE_MODE>
 __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // keys[nbmax], pages[nbmax] | MergeLds
-  __shared__ SelectLds sl;
-  __shared__ int s_pages[kMaxSplitBlocks];
-  const int tid = threadIdx.x;
+  __shared__ int s_hist[4][256];
+  __shared__ int s_wpage[4][kMaxSplitBlocks];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x % a.nsplit;
   const int rest = blockIdx.x / a.nsplit;
   const int hgi = rest % a.num_hgroups;
   const int n = rest / a.num_hgroups;
   const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
-  // round 1: the row's whole score row (nb <= nbmax is not known yet), its
-  // request and position, and Q; round 2: the request's block-table entries,
-  // held in registers until the selection needs them
+  // round 1: the whole score row (nb <= nbmax is not known yet), the row's
+  // request and position, and Q; round 2: the block-table entries, held in
+  // registers while the waves run the radix passes
   const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
   uint32_t* keys = s_dyn;
   int* pages = reinterpret_cast<int*>(s_dyn + nbmax);
@@ -328,43 +331,45 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
   load_q(a, n, hgi, qb);
   const int nb = clampi((v + kPage - 1) / kPage, 0, nbmax);
   const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
-  constexpr int kRegBlocks = 4;  // block-table entries held per thread
+  constexpr int kRegBlocks = 4;  // block-table entries held per thread during the selection
   int btreg[kRegBlocks];
 #pragma unroll
-  for (int i = 0; i < kRegBlocks; ++i) {
-    const int e = tid + i * kAttnThreads;
-    btreg[i] = e < nb ? bt[e] : 0;
-  }
-  __syncthreads();
+  for (int i = 0; i < kRegBlocks; ++i) btreg[i] = (tid + i * kAttnThreads < nb) ? bt[tid + i * kAttnThreads] : 0;
+  __syncthreads();  // keys visible
 
-  const int nblk = a.split_tok / kPage;
-  const int blk0 = split * nblk;
-  const bool writer = split == 0 && hgi == 0;
+  WaveKeys wk;
+  wave_load_keys(keys, nb, wk);
+  const WaveSelection ws = wave_select(keys, wk, nb, a.topk, s_hist[wave]);
+#pragma unroll
+  for (int i = 0; i < kRegBlocks; ++i)
+    if (tid + i * kAttnThreads < nb) pages[tid + i * kAttnThreads] = btreg[i];
+  for (int e = tid + kRegBlocks * kAttnThreads; e < nb; e += kAttnThreads) pages[e] = bt[e];
+  __syncthreads();  // pages visible
+  // this wave's sub-pages and the blocks they fall in
+  const int sp_per_wave = a.split_tok / (4 * kSub);
+  const int sp_begin = split * (a.split_tok / kSub) + wave * sp_per_wave;
+  const int wblk0 = sp_begin >> 3;
+  const int wnblk = max(1, sp_per_wave >> 3);
+  const bool writer = split == 0 && hgi == 0 && wave == 0;
   int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
   int32_t* selrow = a.sel_out ? a.sel_out + static_cast<size_t>(n) * a.topk : nullptr;
   const int pmax = a.num_subpages / kSubsPerPage - 1;
-  int ctx = 0;
-  const int kk = select_row(keys, nb, a.topk, v, sl, [&](int pos, int e) {
+  int ctx = wave_compact(keys, wk, nb, v, ws, [&](int pos, int e) {
     const int page = pages[e];
-    if (pos >= blk0 && pos < blk0 + nblk) s_pages[pos - blk0] = clampi(page, 0, pmax);
+    if (pos >= wblk0 && pos < wblk0 + wnblk) s_wpage[wave][pos - wblk0] = clampi(page, 0, pmax);
     if (writer) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) trow[8 * pos + i] = 8 * page + i;
       if (selrow) selrow[pos] = e;
     }
-  }, &ctx, [&] {
-#pragma unroll
-    for (int i = 0; i < kRegBlocks; ++i)
-      if (tid + i * kAttnThreads < nb) pages[tid + i * kAttnThreads] = btreg[i];
-    for (int e = tid + kRegBlocks * kAttnThreads; e < nb; e += kAttnThreads) pages[e] = bt[e];
   });
   if (writer) {
-    for (int m = 8 * kk + tid; m < 8 * a.topk; m += kAttnThreads) trow[m] = 0;
+    for (int m = 8 * ws.kk + lane; m < 8 * a.topk; m += 64) trow[m] = 0;
     if (selrow)
-      for (int m = kk + tid; m < a.topk; m += kAttnThreads) selrow[m] = -1;
-    if (tid == 0) a.ctx_out[n] = ctx;
+      for (int m = ws.kk + lane; m < a.topk; m += 64) selrow[m] = -1;
+    if (lane == 0) a.ctx_out[n] = ctx;
   }
-  __syncthreads();  // s_pages complete; keys and pages are dead from here on
+  __syncthreads();  // keys / pages are dead; the merge buffers may reuse them
   ctx = min(ctx, a.max_ctx);
   if (ctx == 0) {
     if (split == 0) write_zero_row(a, n, hgi);
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
   }
   if (split * a.split_tok >= ctx) return;
   attend_split<KV_FP8, SCALE_MODE>(a, *reinterpret_cast<MergeLds*>(s_dyn), n, hgi, split, ctx, qb,
-                                   [&](int sp) { return 8 * s_pages[(sp >> 3) - blk0] + (sp & 7); });
+                                   [&](int sp) { return 8 * s_wpage[wave][(sp >> 3) - wblk0] + (sp & 7); });
 }
 
 // Combines the split partials of rows that needed more than one split, in

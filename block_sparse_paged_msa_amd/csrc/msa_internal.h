@@ -59,37 +59,54 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float max16(float v) {  // max over the 16 lanes of a row
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
+// Max over the 16 lanes of each DPP row, in every lane of the row: quad swaps,
+// then half-row and row mirrors pair up the remaining groups.
+__device__ __forceinline__ float max16(float v) {
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false))));
+  return __int_as_float(x);
 }
 
-__device__ __forceinline__ float max_across_rows(float v) {  // lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Lanes l, l^16, l^32, l^48 (the same lane of the four rows): gfx950's
+// permlane swaps exchange rows 0<->1, 2<->3 and halves 0-31 <-> 32-63; with
+// both operands equal, the two results hold the value and its partner.
+__device__ __forceinline__ float max_across_rows(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 __device__ __forceinline__ float sum_across_rows(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then the row totals are carried forward
+// (lane 15 into row 1 and row 3, then lane 31 into rows 2 and 3). Lanes whose
+// source is outside the row or whose row is masked add the `old` value 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Exclusive prefix sum over a 256-thread block; `scratch` holds 4 ints.
 __device__ __forceinline__ int block256_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -146,6 +163,7 @@ struct MsaScoreArgs {
   int32_t num_rows;
   int32_t num_pages;
   int32_t len_cap;
+  int32_t blocks_per_req;  // host bound S on any request's blocks: slot r*S + j
   int32_t write_meta;
 };
 hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s);

@@ -41,13 +41,7 @@ __global__ __launch_bounds__(kMetaThreads) void msa_meta_kernel(MsaMetaArgs a) {
     const int nb = (L + kPage - 1) / kPage;
     int x[4] = {ql, L, nb, nb * ((ql + kRowsPerUnit - 1) / kRowsPerUnit)};
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int y = __shfl_up(x[c], o);
-        if (lane >= o) x[c] += y;
-      }
-    }
+    for (int c = 0; c < 4; ++c) x[c] = wave_inclusive_scan(x[c]);
     if (lane == 63) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) s_tot[wave][c] = x[c];

@@ -2,21 +2,25 @@
 // 实现拆解 item 1: the per-row decode scorer with work mapped to each request's
 // real block count, index-K tiles shared by all query rows of a request).
 //
-// Work unit = (request r, page j, group of up to 64 query rows of r). Every
-// workgroup first forms the running sums of query rows and units over the
-// requests in LDS (from seq_lens / query_lens, one coalesced read), so a unit
-// finds its request with an LDS binary search and the persistent grid covers
-// exactly the real pages of the batch. In the fused decode step workgroup 0
-// also writes the batch metadata (cu_seqlens_q/k, cu_blocks, cu_units, row
-// request ids and positions: vLLM PR #56170 page, 实现拆解 items 1-3) so that
-// no separate metadata launch is needed.
+// Work unit = (request r, page j, group g of up to 64 query rows of r).
+// Units with g = 0 are numbered by a fixed stride, slot = r*S + j with S the
+// host bound on a request's blocks, so a wave knows its page from its slot
+// alone and requests the page before anything else; slots with j past the
+// request's real block count are skipped. Units with g >= 1 (only requests
+// with more than 64 query rows, i.e. prefill) follow, numbered by a device
+// prefix over the requests. Every workgroup forms the running sums of query
+// rows (and of the g >= 1 units) in LDS from seq_lens / query_lens while its
+// first pages are in flight. In the fused decode step workgroup 0 also writes
+// the batch metadata (cu_seqlens_q/k, cu_blocks, cu_units, row request ids and
+// positions: vLLM PR #56170 page, 实现拆解 items 1-3), so no separate metadata
+// launch is needed.
 //
 // One wave owns one unit: it streams the 32 KiB index-K page into registers
 // once, in 1 KiB fully coalesced runs thanks to the shuffled tile layout (the
-// B operand of v_mfma_f32_16x16x32_bf16, token = column) and
-// multiplies it with every 16-row tile of the group's index queries (the A
-// operand), so the page is shared by all of the request's rows in the group.
-// The max over the block's visible tokens is taken on the MFMA output, per row.
+// B operand of v_mfma_f32_16x16x32_bf16, token = column), and multiplies it
+// with every 16-row tile of the group's index queries (the A operand), so the
+// page is shared by all of the request's rows in the group. The max over the
+// block's visible tokens is taken on the MFMA output, per row.
 #include "msa_internal.h"
 
 using namespace msa;
@@ -26,39 +30,37 @@ namespace {
 constexpr int kScoreThreads = 256;
 constexpr int kWavesPerWg = kScoreThreads / 64;
 
-__device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const int* s_units, const int* s_cuq, int u,
-                                           int lane) {
-  int lo = 0, hi = a.num_reqs;  // request of this unit: last r with cu_units[r] <= u
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_units[mid] <= u) lo = mid; else hi = mid;
-  }
-  const int r = lo;
-  const int q0 = s_cuq[r];
-  const int ql = s_cuq[r + 1] - q0;
-  const int ngroups = (ql + kRowsPerUnit - 1) / kRowsPerUnit;
-  const int local = u - s_units[r];
-  const int j = local / ngroups;                 // page (block) index inside the request
-  const int g0 = (local - j * ngroups) * kRowsPerUnit;
-  const int nrows = min(kRowsPerUnit, ql - g0);
-  const int row0 = q0 + g0;                      // first query row of the group
-  const int L = clampi(a.seq_lens[r], 0, a.len_cap);
-  const int page = clampi(a.block_table[static_cast<size_t>(r) * a.ld_bt + j], 0, a.num_pages - 1);
-  const int pos0 = L - ql + g0;                  // absolute position of the group's first row
-  const int nb_r = (L + kPage - 1) / kPage;
-  const uint16_t* kp = a.index_k + static_cast<size_t>(page) * (kPage * kDim);
+struct Unit {
+  int r, j, g;   // request, page inside the request, 64-row group
+  int L, ql;     // request length and query rows (clamped)
+  bool valid;
+};
 
-  // B operand: column = token tt*16 + lane%16, K entries = dims kc*32 + 8*(lane/16) .. +7.
-  // A page is 8 shuffled 16-token tiles [4][4][16][8], so each (tt, kc) operand
-  // is one contiguous 1 KiB run read by the 64 lanes in order.
-  bf16x8 kb[8][4];
+// B operand of the page: column = token tt*16 + lane%16, K entries = dims
+// kc*32 + 8*(lane/16) .. +7. A page is 8 shuffled 16-token tiles
+// [4][4][16][8], so each (tt, kc) operand is one contiguous 1 KiB run.
+__device__ __forceinline__ void load_page(const MsaScoreArgs& a, int page, int lane, bf16x8 (&kb)[8][4]) {
+  const uint16_t* kp = a.index_k + static_cast<size_t>(page) * (kPage * kDim);
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
       kb[tt][kc] = *reinterpret_cast<const bf16x8*>(kp + tt * (kSub * kDim) + (kc * 64 + lane) * 8);
+}
 
-  const int t_base = j * kPage + (lane & 15);
+__device__ __forceinline__ int page_of(const MsaScoreArgs& a, const Unit& w) {
+  return clampi(a.block_table[static_cast<size_t>(w.r) * a.ld_bt + w.j], 0, a.num_pages - 1);
+}
+
+// Scores of one unit once its page is in registers; q0 is the request's first row.
+__device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const Unit& w, int q0, const bf16x8 (&kb)[8][4],
+                                           int lane) {
+  const int g0 = w.g * kRowsPerUnit;
+  const int nrows = min(kRowsPerUnit, w.ql - g0);
+  const int row0 = q0 + g0;                 // first query row of the group
+  const int pos0 = w.L - w.ql + g0;         // its absolute position
+  const int nb_r = (w.L + kPage - 1) / kPage;
+  const int t_base = w.j * kPage + (lane & 15);
   for (int mt = 0; mt * 16 < nrows; ++mt) {
     const int mrow = mt * 16 + (lane & 15);
     bf16x8 qa[4];
@@ -91,13 +93,12 @@ __device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const int* s_u
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + 4 * (lane >> 4) + i;
         if (m < nrows && row0 + m < a.num_rows)
-          a.scores[static_cast<size_t>(row0 + m) * a.ld_s + j] = mx[i];
+          a.scores[static_cast<size_t>(row0 + m) * a.ld_s + w.j] = mx[i];
       }
     }
   }
-
   // the unit of the request's last page also writes the -inf tail of its rows
-  if (j == nb_r - 1) {
+  if (w.j == nb_r - 1) {
     const int width = a.ld_s - nb_r;
     for (int idx = lane; idx < nrows * width; idx += 64) {
       const int m = idx / width;
@@ -107,19 +108,64 @@ __device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const int* s_u
   }
 }
 
+// Fixed-stride slot r*S + j (first row group), from global memory only.
+__device__ __forceinline__ Unit slot_unit(const MsaScoreArgs& a, int u) {
+  Unit w;
+  w.r = u / a.blocks_per_req;
+  w.j = u - w.r * a.blocks_per_req;
+  w.g = 0;
+  w.L = clampi(a.seq_lens[w.r], 0, a.len_cap);
+  w.ql = clampi(a.query_lens[w.r], 0, w.L);
+  w.valid = w.ql > 0 && w.j * kPage < w.L;
+  return w;
+}
+
+// Extra row groups (g >= 1): the prefix over requests numbers them.
+__device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_extra, const int* s_cuq, int ue) {
+  int lo = 0, hi = a.num_reqs;  // last r with extra[r] <= ue
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_extra[mid] <= ue) lo = mid; else hi = mid;
+  }
+  Unit w;
+  w.r = lo;
+  w.ql = s_cuq[lo + 1] - s_cuq[lo];
+  w.L = clampi(a.seq_lens[lo], 0, a.len_cap);
+  const int more = (w.ql + kRowsPerUnit - 1) / kRowsPerUnit - 1;  // groups 1..more
+  const int local = ue - s_extra[lo];
+  w.j = more > 0 ? local / more : 0;
+  w.g = more > 0 ? 1 + (local - w.j * more) : 0;
+  w.valid = more > 0 && ue < s_extra[a.num_reqs];
+  return w;
+}
+
 __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a) {
-  extern __shared__ int s_dyn[];            // [R+1] unit prefix, [R+1] row prefix
-  __shared__ int s_tot[kWavesPerWg][4];
-  int* s_units = s_dyn;
-  int* s_cuq = s_dyn + a.num_reqs + 1;
+  extern __shared__ int s_dyn[];  // [R+1] row prefix, [R+1] extra-group prefix
+  __shared__ int s_tot[kWavesPerWg][5];
+  int* s_cuq = s_dyn;
+  int* s_extra = s_dyn + a.num_reqs + 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = a.num_reqs;
   const bool writer = a.write_meta && blockIdx.x == 0;
+  const int slots_a = R * a.blocks_per_req;
+  const int nwaves = gridDim.x * kWavesPerWg;
+  int u = blockIdx.x * kWavesPerWg + wave;
 
+  // first unit of this wave: its page is requested before the prefix work
+  Unit w0 = {};
+  bf16x8 kb[8][4];
+  const bool first_is_a = u < slots_a;
+  if (first_is_a) {
+    w0 = slot_unit(a, u);
+    if (w0.valid) load_page(a, page_of(a, w0), lane, kb);
+  }
+
+  // running sums over the requests of (query rows, KV tokens, blocks, score
+  // units, extra row-group units)
   if (tid == 0) {
-    s_units[0] = 0;
     s_cuq[0] = 0;
+    s_extra[0] = 0;
     if (writer) {
       a.cu_q[0] = 0;
       a.cu_k[0] = 0;
@@ -127,8 +173,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
       a.cu_units[0] = 0;
     }
   }
-  // running sums of (query rows, KV tokens, blocks, score units) over requests
-  int carry[4] = {0, 0, 0, 0};
+  int carry[5] = {0, 0, 0, 0, 0};
   for (int base = 0; base < R; base += kScoreThreads) {
     const int r = base + tid;
     int L = 0, ql = 0;
@@ -137,37 +182,32 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
       ql = clampi(a.query_lens[r], 0, L);
     }
     const int nb = (L + kPage - 1) / kPage;
-    int x[4] = {ql, L, nb, nb * ((ql + kRowsPerUnit - 1) / kRowsPerUnit)};
+    const int groups = (ql + kRowsPerUnit - 1) / kRowsPerUnit;
+    int x[5] = {ql, L, nb, nb * groups, nb * max(groups - 1, 0)};
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int y = __shfl_up(x[c], o);
-        if (lane >= o) x[c] += y;
-      }
-    }
+    for (int c = 0; c < 5; ++c) x[c] = wave_inclusive_scan(x[c]);
     if (lane == 63) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s_tot[wave][c] = x[c];
+      for (int c = 0; c < 5; ++c) s_tot[wave][c] = x[c];
     }
     __syncthreads();
-    int pre[4], tot[4];
+    int pre[5], tot[5];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 5; ++c) {
       pre[c] = carry[c];
       tot[c] = 0;
     }
 #pragma unroll
-    for (int w = 0; w < kWavesPerWg; ++w)
+    for (int ww = 0; ww < kWavesPerWg; ++ww)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        pre[c] += (w < wave) ? s_tot[w][c] : 0;
-        tot[c] += s_tot[w][c];
+      for (int c = 0; c < 5; ++c) {
+        pre[c] += (ww < wave) ? s_tot[ww][c] : 0;
+        tot[c] += s_tot[ww][c];
       }
     __syncthreads();
     if (r < R) {
       s_cuq[r + 1] = pre[0] + x[0];
-      s_units[r + 1] = pre[3] + x[3];
+      s_extra[r + 1] = pre[4] + x[4];
       if (writer) {
         a.cu_q[r + 1] = pre[0] + x[0];
         a.cu_k[r + 1] = pre[1] + x[1];
@@ -176,7 +216,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) carry[c] += tot[c];
+    for (int c = 0; c < 5; ++c) carry[c] += tot[c];
   }
   __syncthreads();
 
@@ -194,9 +234,17 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
     }
   }
 
-  const int total = s_units[R];
-  const int nwaves = gridDim.x * kWavesPerWg;
-  for (int u = blockIdx.x * kWavesPerWg + wave; u < total; u += nwaves) score_unit(a, s_units, s_cuq, u, lane);
+  if (first_is_a) {
+    if (w0.valid) score_unit(a, w0, s_cuq[w0.r], kb, lane);
+    u += nwaves;
+  }
+  const int total = slots_a + s_extra[R];
+  for (; u < total; u += nwaves) {
+    const Unit w = u < slots_a ? slot_unit(a, u) : extra_unit(a, s_extra, s_cuq, u - slots_a);
+    if (!w.valid) continue;
+    load_page(a, page_of(a, w), lane, kb);
+    score_unit(a, w, s_cuq[w.r], kb, lane);
+  }
 }
 
 }  // namespace

@@ -71,12 +71,7 @@ __device__ __forceinline__ int select_row(const uint32_t* keys, int nb, int topk
           c[i] = sl.hist[255 - 4 * lane - i];
           local += c[i];
         }
-        int incl = local;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
+        const int incl = wave_inclusive_scan(local);
         int run = incl - local;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -127,6 +122,142 @@ __device__ __forceinline__ int select_row(const uint32_t* keys, int nb, int topk
   __syncthreads();
   *ctx_out = kPage * kk - (sl.last_kept ? kPage * nb - v : 0);
   return kk;
+}
+
+// ---------------------------------------------------------------------------
+// The same selection computed by one wave alone (every wave of a workgroup
+// can run it on the same LDS keys and get the same answer with no
+// workgroup barrier). hist: 256 ints of LDS private to the wave.
+// ---------------------------------------------------------------------------
+struct WaveSelection {
+  uint32_t T;        // keep keys > T, and keys == T among the lowest ids
+  int need;          // keys equal to T that are kept (lowest ids first)
+  int kk;            // K' = min(topk, nb)
+  bool partial;      // kk < nb
+  bool all_eq_kept;  // every key >= T is kept
+};
+
+constexpr int kWaveKeyRegs = 16;  // keys a lane keeps in registers (1024 blocks)
+
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The keys of blocks e = lane + 64*i, i < kWaveKeyRegs, in registers
+// (0 past nb); blocks from 1024 on are read from LDS when needed.
+struct WaveKeys {
+  uint32_t k[kWaveKeyRegs];
+};
+
+__device__ __forceinline__ void wave_load_keys(const uint32_t* keys, int nb, WaveKeys& wk) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kWaveKeyRegs; ++i) wk.k[i] = (lane + 64 * i < nb) ? keys[lane + 64 * i] : 0u;
+}
+
+__device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const WaveKeys& wk, int nb, int topk,
+                                                     int* hist) {
+  const int lane = threadIdx.x & 63;
+  WaveSelection w;
+  w.kk = min(topk, nb);
+  w.partial = w.kk < nb;
+  w.T = 0;
+  w.need = 0;
+  w.all_eq_kept = true;
+  if (!w.partial) return w;
+  uint32_t prefix = 0;
+  int need = w.kk;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
+    wave_lds_order();
+    auto bin = [&](uint32_t k) {
+      const bool match = (shift == 24) || ((k >> (shift + 8)) == (prefix >> (shift + 8)));
+      if (match) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    };
+#pragma unroll
+    for (int i = 0; i < kWaveKeyRegs; ++i)
+      if (lane + 64 * i < nb) bin(wk.k[i]);
+    for (int e = lane + 64 * kWaveKeyRegs; e < nb; e += 64) bin(keys[e]);
+    wave_lds_order();
+    int c[4], local = 0;  // lane owns digits 255-4*lane .. 252-4*lane (descending)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = hist[255 - 4 * lane - i];
+      local += c[i];
+    }
+    const int incl = wave_inclusive_scan(local);
+    int run = incl - local, my_digit = 0, my_need = 0, my_cnt = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run < need && need <= run + c[i]) {
+        found = true;
+        my_digit = 255 - 4 * lane - i;
+        my_need = need - run;
+        my_cnt = c[i];
+      }
+      run += c[i];
+    }
+    // exactly one lane holds the digit: broadcast it with readlane
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(__ballot(found))) - 1);
+    prefix |= static_cast<uint32_t>(__builtin_amdgcn_readlane(my_digit, src)) << shift;
+    need = __builtin_amdgcn_readlane(my_need, src);
+    const int cnt = __builtin_amdgcn_readlane(my_cnt, src);
+    wave_lds_order();
+    if (need == cnt) {
+      // every key sharing the prefix so far is kept: keys >= prefix (lower
+      // bits zero) are exactly the K' largest, no tie straddles the cut
+      w.T = prefix;
+      w.need = 0;
+      w.all_eq_kept = true;
+      return w;
+    }
+  }
+  w.T = prefix;
+  w.need = need;
+  w.all_eq_kept = false;  // keys equal to T straddle the cut: lowest ids first
+  return w;
+}
+
+// Visits the kept blocks in ascending id order: visit(rank, block) in the
+// lane that examined the block. Returns the context length
+// 128*K' - (block nb-1 kept ? 128*nb - v : 0) in every lane.
+template <typename Visit>
+__device__ __forceinline__ int wave_compact(const uint32_t* keys, const WaveKeys& wk, int nb, int v,
+                                            const WaveSelection& w, Visit visit) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int carry = 0, carry_eq = 0;
+  bool last_kept = false;
+  auto step = [&](int e, uint32_t k) {
+    const bool valid = e < nb;
+    bool keep;
+    if (!w.partial) {
+      keep = valid;
+    } else if (w.all_eq_kept) {
+      keep = valid && k >= w.T;
+    } else {
+      const bool eq = valid && k == w.T;
+      const unsigned long long em = __ballot(eq);
+      const int rank_eq = carry_eq + __popcll(em & lt);
+      carry_eq += __popcll(em);
+      keep = valid && (k > w.T || (eq && rank_eq < w.need));
+    }
+    const unsigned long long km = __ballot(keep);
+    if (keep) {
+      visit(carry + __popcll(km & lt), e);
+      if (e == nb - 1) last_kept = true;
+    }
+    carry += __popcll(km);
+  };
+#pragma unroll
+  for (int i = 0; i < kWaveKeyRegs; ++i)
+    if (64 * i < nb) step(lane + 64 * i, wk.k[i]);
+  for (int base = 64 * kWaveKeyRegs; base < nb; base += 64) step(base + lane, base + lane < nb ? keys[base + lane] : 0u);
+  const bool lk = __ballot(last_kept) != 0ull;
+  return kPage * w.kk - (lk ? kPage * nb - v : 0);
 }
 
 }  // namespace msa
