@@ -305,8 +305,9 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArg
 // row's keys and block-table entries sit in dynamic LDS; every wave runs the
 // selection itself (wave_select / wave_compact) and keeps only the pages of
 // its own sub-pages, so the waves need no barrier between selection and
-// attention. The merge buffers reuse the key area afterwards.
-template <int KV_FP8, int SCALE_MODE>
+// attention. The merge buffers reuse the key area afterwards. KEY_REGS keys
+// per lane stay in registers during the selection (64*KEY_REGS blocks).
+template <int KV_FP8, int SCALE_MODE, int KEY_REGS>
 __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // keys[nbmax], pages[nbmax] | MergeLds
   __shared__ int s_hist[4][256];
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
   for (int i = 0; i < kRegBlocks; ++i) btreg[i] = (tid + i * kAttnThreads < nb) ? bt[tid + i * kAttnThreads] : 0;
   __syncthreads();  // keys visible
 
-  WaveKeys wk;
+  WaveKeys<KEY_REGS> wk;
   wave_load_keys(keys, nb, wk);
   const WaveSelection ws = wave_select(keys, wk, nb, a.topk, s_hist[wave]);
 #pragma unroll
@@ -411,18 +412,26 @@ __global__ __launch_bounds__(kAttnThreads) void msa_merge_kernel(MsaAttnArgs a, 
   f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit_n; s0 += kBatch) {
     if (s0 > 0) fetch(s0);
+    // batch max first, so the sixteen weights are independent of each other
+    float mb = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j < nsplit_n) mb = fmaxf(mb, ms[j]);
+    const float mn = fmaxf(Mg, mb);
+    const float c_old = fast_exp2(Mg - mn);  // 0 on the first batch (Mg = -inf)
+    float lb = 0.f;
+    f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j < nsplit_n) {
-        const float mn = fmaxf(Mg, ms[j]);
-        const float c_old = fast_exp2(Mg - mn);  // 0 on the first split (Mg = -inf)
-        const float c_new = fast_exp2(ms[j] - mn);
-        Lg = Lg * c_old + ls[j] * c_new;
-        g0 = g0 * c_old + x0[j] * c_new;
-        g1 = g1 * c_old + x1[j] * c_new;
-        Mg = mn;
-      }
+      const float wj = (s0 + j < nsplit_n) ? fast_exp2(ms[j] - mn) : 0.f;
+      lb += ls[j] * wj;
+      b0 += x0[j] * wj;
+      b1 += x1[j] * wj;
     }
+    Lg = Lg * c_old + lb;
+    g0 = g0 * c_old + b0;
+    g1 = g1 * c_old + b1;
+    Mg = mn;
   }
   const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
   uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile) * kDim;
@@ -436,8 +445,12 @@ hipError_t launch(const MsaAttnArgs& a, hipStream_t s) {
   if (a.scores) {
     const size_t nbmax = static_cast<size_t>(min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow));
     const size_t lds = max(2 * nbmax * sizeof(uint32_t), sizeof(MergeLds));
-    hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kAttnThreads), lds, s, a);
+    if (nbmax <= 256)
+      hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE, 4>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kAttnThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE, 16>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kAttnThreads), lds, s, a);
   }
   else
     hipLaunchKernelGGL((msa_attn_table_kernel<KV_FP8, SCALE_MODE>), dim3(static_cast<unsigned>(grid)),

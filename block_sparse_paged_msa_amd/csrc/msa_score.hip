@@ -10,10 +10,12 @@
 // with more than 64 query rows, i.e. prefill) follow, numbered by a device
 // prefix over the requests. Every workgroup forms the running sums of query
 // rows (and of the g >= 1 units) in LDS from seq_lens / query_lens while its
-// first pages are in flight. In the fused decode step workgroup 0 also writes
-// the batch metadata (cu_seqlens_q/k, cu_blocks, cu_units, row request ids and
-// positions: vLLM PR #56170 page, 实现拆解 items 1-3), so no separate metadata
-// launch is needed.
+// first pages are in flight; in a launch of at most 64 rows there are no
+// g >= 1 units, and the waves of every workgroup but the metadata writer sum
+// the rows below their request themselves instead. In the fused decode step
+// workgroup 0 also writes the batch metadata (cu_seqlens_q/k, cu_blocks,
+// cu_units, row request ids and positions: vLLM PR #56170 page, 实现拆解
+// items 1-3), so no separate metadata launch is needed.
 //
 // One wave owns one unit: it streams the 32 KiB index-K page into registers
 // once, in 1 KiB fully coalesced runs thanks to the shuffled tile layout (the
@@ -152,9 +154,25 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   const int nwaves = gridDim.x * kWavesPerWg;
   int u = blockIdx.x * kWavesPerWg + wave;
 
+  // Decode-only launches (at most 64 rows in all, so no request has a row
+  // group past the first) with no metadata to write need no prefix: a wave
+  // sums query_lens below its request itself and never waits on a barrier.
+  bf16x8 kb[8][4];
+  if (!writer && a.num_rows <= kRowsPerUnit) {
+    for (; u < slots_a; u += nwaves) {
+      const Unit w = slot_unit(a, u);
+      if (!w.valid) continue;
+      int q0 = 0;
+      for (int r = lane; r < w.r; r += 64) q0 += clampi(a.query_lens[r], 0, clampi(a.seq_lens[r], 0, a.len_cap));
+      load_page(a, page_of(a, w), lane, kb);
+      q0 = __builtin_amdgcn_readlane(wave_inclusive_scan(q0), 63);
+      score_unit(a, w, q0, kb, lane);
+    }
+    return;
+  }
+
   // first unit of this wave: its page is requested before the prefix work
   Unit w0 = {};
-  bf16x8 kb[8][4];
   const bool first_is_a = u < slots_a;
   if (first_is_a) {
     w0 = slot_unit(a, u);

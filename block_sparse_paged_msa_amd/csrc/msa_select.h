@@ -137,26 +137,27 @@ struct WaveSelection {
   bool all_eq_kept;  // every key >= T is kept
 };
 
-constexpr int kWaveKeyRegs = 16;  // keys a lane keeps in registers (1024 blocks)
-
 __device__ __forceinline__ void wave_lds_order() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
-// The keys of blocks e = lane + 64*i, i < kWaveKeyRegs, in registers
-// (0 past nb); blocks from 1024 on are read from LDS when needed.
+// The keys of blocks e = lane + 64*i, i < KR, in registers (0 past nb);
+// blocks from 64*KR on are read from LDS when needed.
+template <int KR>
 struct WaveKeys {
-  uint32_t k[kWaveKeyRegs];
+  uint32_t k[KR];
 };
 
-__device__ __forceinline__ void wave_load_keys(const uint32_t* keys, int nb, WaveKeys& wk) {
+template <int KR>
+__device__ __forceinline__ void wave_load_keys(const uint32_t* keys, int nb, WaveKeys<KR>& wk) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < kWaveKeyRegs; ++i) wk.k[i] = (lane + 64 * i < nb) ? keys[lane + 64 * i] : 0u;
+  for (int i = 0; i < KR; ++i) wk.k[i] = (lane + 64 * i < nb) ? keys[lane + 64 * i] : 0u;
 }
 
-__device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const WaveKeys& wk, int nb, int topk,
+template <int KR>
+__device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const WaveKeys<KR>& wk, int nb, int topk,
                                                      int* hist) {
   const int lane = threadIdx.x & 63;
   WaveSelection w;
@@ -177,9 +178,9 @@ __device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const
       if (match) atomicAdd(&hist[(k >> shift) & 255u], 1);
     };
 #pragma unroll
-    for (int i = 0; i < kWaveKeyRegs; ++i)
+    for (int i = 0; i < KR; ++i)
       if (lane + 64 * i < nb) bin(wk.k[i]);
-    for (int e = lane + 64 * kWaveKeyRegs; e < nb; e += 64) bin(keys[e]);
+    for (int e = lane + 64 * KR; e < nb; e += 64) bin(keys[e]);
     wave_lds_order();
     int c[4], local = 0;  // lane owns digits 255-4*lane .. 252-4*lane (descending)
 #pragma unroll
@@ -224,8 +225,8 @@ __device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const
 // Visits the kept blocks in ascending id order: visit(rank, block) in the
 // lane that examined the block. Returns the context length
 // 128*K' - (block nb-1 kept ? 128*nb - v : 0) in every lane.
-template <typename Visit>
-__device__ __forceinline__ int wave_compact(const uint32_t* keys, const WaveKeys& wk, int nb, int v,
+template <int KR, typename Visit>
+__device__ __forceinline__ int wave_compact(const uint32_t* keys, const WaveKeys<KR>& wk, int nb, int v,
                                             const WaveSelection& w, Visit visit) {
   const int lane = threadIdx.x & 63;
   const unsigned long long lt = (1ull << lane) - 1ull;
@@ -253,9 +254,9 @@ __device__ __forceinline__ int wave_compact(const uint32_t* keys, const WaveKeys
     carry += __popcll(km);
   };
 #pragma unroll
-  for (int i = 0; i < kWaveKeyRegs; ++i)
+  for (int i = 0; i < KR; ++i)
     if (64 * i < nb) step(lane + 64 * i, wk.k[i]);
-  for (int base = 64 * kWaveKeyRegs; base < nb; base += 64) step(base + lane, base + lane < nb ? keys[base + lane] : 0u);
+  for (int base = 64 * KR; base < nb; base += 64) step(base + lane, base + lane < nb ? keys[base + lane] : 0u);
   const bool lk = __ballot(last_kept) != 0ull;
   return kPage * w.kk - (lk ? kPage * nb - v : 0);
 }
