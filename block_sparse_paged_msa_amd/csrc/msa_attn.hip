@@ -301,17 +301,18 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArg
   attend_split<KV_FP8, SCALE_MODE>(a, ml, n, hgi, split, ctx, qb, [&](int sp) { return s_sub[sp - sp0]; });
 }
 
-// Fused mode: select the row's blocks from its scores, then attend. The
-// row's keys and block-table entries sit in dynamic LDS; every wave runs the
-// selection itself (wave_select / wave_compact) and keeps only the pages of
-// its own sub-pages, so the waves need no barrier between selection and
-// attention. The merge buffers reuse the key area afterwards. KEY_REGS keys
-// per lane stay in registers during the selection (64*KEY_REGS blocks).
+// Fused mode: select the row's blocks from its scores, then attend. Every
+// wave loads the row's keys and block-table entries into registers and runs
+// the selection itself (wave_select / wave_compact), keeping only the pages
+// of its own sub-pages, so nothing before the attention's own merge needs a
+// workgroup barrier. KEY_REGS keys per lane sit in registers (64*KEY_REGS
+// blocks); keys and pages past them are read from global memory.
 template <int KV_FP8, int SCALE_MODE, int KEY_REGS>
 __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // keys[nbmax], pages[nbmax] | MergeLds
-  __shared__ int s_hist[4][256];
-  __shared__ int s_wpage[4][kMaxSplitBlocks];
+  __shared__ MergeLds ml;
+  __shared__ __attribute__((aligned(16))) int s_hist[4][kWaveRadixPasses][256];
+  __shared__ int s_wpage[4][kMaxSplitBlocks];  // raw page of each of the wave's ranks
+  __shared__ int s_wsel[4][kMaxSplitBlocks];   // and its block id
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x % a.nsplit;
@@ -319,85 +320,128 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
   const int hgi = rest % a.num_hgroups;
   const int n = rest / a.num_hgroups;
   const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
-  // round 1: the whole score row (nb <= nbmax is not known yet), the row's
-  // request and position, and Q; round 2: the block-table entries, held in
-  // registers while the waves run the radix passes
+  // round 1: the row's keys (nb <= nbmax is not known yet), its request and
+  // position, and Q; round 2: the block-table entries, which arrive while the
+  // radix passes run
   const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
-  uint32_t* keys = s_dyn;
-  int* pages = reinterpret_cast<int*>(s_dyn + nbmax);
-  for (int e = tid; e < nbmax; e += kAttnThreads) keys[e] = order_key(srow[e]);
+  // (indices clamped so that every load is issued unconditionally, in one
+  // round; slots at or past nb are ignored by the selection)
+  WaveKeys<KEY_REGS> wk;
+  float kraw[KEY_REGS];
+#pragma unroll
+  for (int i = 0; i < KEY_REGS; ++i) kraw[i] = srow[min(lane + 64 * i, max(nbmax, 1) - 1)];
   const int r = clampi(a.row_req[n], 0, a.num_reqs - 1);
   const int v = a.row_pos[n] + 1;
   bf16x8 qb[4];
   load_q(a, n, hgi, qb);
+  wave_clear_hist(s_hist[wave]);
   const int nb = clampi((v + kPage - 1) / kPage, 0, nbmax);
   const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
-  constexpr int kRegBlocks = 4;  // block-table entries held per thread during the selection
-  int btreg[kRegBlocks];
+  int pg[KEY_REGS];
 #pragma unroll
-  for (int i = 0; i < kRegBlocks; ++i) btreg[i] = (tid + i * kAttnThreads < nb) ? bt[tid + i * kAttnThreads] : 0;
-  __syncthreads();  // keys visible
-
-  WaveKeys<KEY_REGS> wk;
-  wave_load_keys(keys, nb, wk);
-  const WaveSelection ws = wave_select(keys, wk, nb, a.topk, s_hist[wave]);
+  for (int i = 0; i < KEY_REGS; ++i) pg[i] = bt[min(lane + 64 * i, max(nb, 1) - 1)];
 #pragma unroll
-  for (int i = 0; i < kRegBlocks; ++i)
-    if (tid + i * kAttnThreads < nb) pages[tid + i * kAttnThreads] = btreg[i];
-  for (int e = tid + kRegBlocks * kAttnThreads; e < nb; e += kAttnThreads) pages[e] = bt[e];
-  __syncthreads();  // pages visible
-  // this wave's sub-pages and the blocks they fall in
+  for (int i = 0; i < KEY_REGS; ++i) wk.k[i] = order_key(kraw[i]);
+  auto tail_key = [&](int e) { return order_key(srow[e]); };
+  auto tail_page = [&](int e) { return bt[e]; };
+  wave_lds_order();  // histograms cleared
+  const WaveSelection ws = wave_select(wk, nb, a.topk, s_hist[wave], tail_key);
+  // this wave's sub-pages and the blocks (ranks) they fall in
   const int sp_per_wave = a.split_tok / (4 * kSub);
   const int sp_begin = split * (a.split_tok / kSub) + wave * sp_per_wave;
   const int wblk0 = sp_begin >> 3;
   const int wnblk = max(1, sp_per_wave >> 3);
-  const bool writer = split == 0 && hgi == 0 && wave == 0;
-  int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
-  int32_t* selrow = a.sel_out ? a.sel_out + static_cast<size_t>(n) * a.topk : nullptr;
-  const int pmax = a.num_subpages / kSubsPerPage - 1;
-  int ctx = wave_compact(keys, wk, nb, v, ws, [&](int pos, int e) {
-    const int page = pages[e];
-    if (pos >= wblk0 && pos < wblk0 + wnblk) s_wpage[wave][pos - wblk0] = clampi(page, 0, pmax);
-    if (writer) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) trow[8 * pos + i] = 8 * page + i;
-      if (selrow) selrow[pos] = e;
+  int ctx = wave_locate(wk, pg, nb, v, ws, wblk0, wblk0 + wnblk, tail_key, tail_page, [&](int q, int e, int page) {
+    if (lane == 0) {
+      s_wpage[wave][q - wblk0] = page;
+      s_wsel[wave][q - wblk0] = e;
     }
   });
-  if (writer) {
-    for (int m = 8 * ws.kk + lane; m < 8 * a.topk; m += 64) trow[m] = 0;
-    if (selrow)
-      for (int m = ws.kk + lane; m < a.topk; m += 64) selrow[m] = -1;
-    if (lane == 0) a.ctx_out[n] = ctx;
-  }
-  __syncthreads();  // keys / pages are dead; the merge buffers may reuse them
+  wave_lds_order();  // this wave's pages
+  const int pmax = a.num_subpages / kSubsPerPage - 1;
+  const int ctx_row = ctx;
   ctx = min(ctx, a.max_ctx);
-  if (ctx == 0) {
-    if (split == 0) write_zero_row(a, n, hgi);
-    return;
+  if (ctx > 0 && split * a.split_tok < ctx)
+    attend_split<KV_FP8, SCALE_MODE>(a, ml, n, hgi, split, ctx, qb, [&](int sp) {
+      return 8 * clampi(s_wpage[wave][(sp >> 3) - wblk0], 0, pmax) + (sp & 7);
+    });
+  else if (ctx == 0 && split == 0)
+    write_zero_row(a, n, hgi);
+
+  // The selection's outputs, written once the attention's loads are out so
+  // that no wait for these stores holds them back. Rank q is written by the
+  // wave whose sub-pages start its block, in head group 0 (every rank lies in
+  // a split that attends, since 128*q < ctx).
+  if (hgi == 0 && (sp_begin & 7) == 0) {
+    int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
+    const int nq = min(wblk0 + wnblk, ws.kk) - wblk0;
+    for (int idx = lane; idx < 8 * nq; idx += 64) trow[8 * wblk0 + idx] = 8 * s_wpage[wave][idx >> 3] + (idx & 7);
+    if (a.sel_out)
+      for (int m = lane; m < nq; m += 64) a.sel_out[static_cast<size_t>(n) * a.topk + wblk0 + m] = s_wsel[wave][m];
   }
-  if (split * a.split_tok >= ctx) return;
-  attend_split<KV_FP8, SCALE_MODE>(a, *reinterpret_cast<MergeLds*>(s_dyn), n, hgi, split, ctx, qb,
-                                   [&](int sp) { return 8 * s_wpage[wave][(sp >> 3) - wblk0] + (sp & 7); });
+  if (split == 0 && hgi == 0 && wave == 0) {  // context length and the zero tail past K'
+    int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
+    for (int m = 8 * ws.kk + lane; m < 8 * a.topk; m += 64) trow[m] = 0;
+    if (a.sel_out)
+      for (int m = ws.kk + lane; m < a.topk; m += 64) a.sel_out[static_cast<size_t>(n) * a.topk + m] = -1;
+    if (lane == 0) a.ctx_out[n] = ctx_row;
+  }
 }
 
-// Combines the split partials of rows that needed more than one split, in
-// split order (log2-domain weights 2^(m_s - max)).
-__global__ __launch_bounds__(kAttnThreads) void msa_merge_kernel(MsaAttnArgs a, const int32_t* ctxp) {
-  const int tid = threadIdx.x;
-  const int hgi = blockIdx.x % a.num_hgroups;
-  const int n = blockIdx.x / a.num_hgroups;
-  const int th = tid >> 4, td = (tid & 15) * 8;
+// Combines the split partials of rows that needed more than one split. One
+// wave per (row, query head): lane group g = lane/16 takes splits g, g+4,
+// g+8, ... and eight dims (lane%16)*8.. of each, so one round of loads
+// fetches sixteen splits of 512 B. The four groups are then combined through
+// row and half swaps. All weights are log2-domain 2^(m_s - max).
+constexpr int kMergeThreads = 64;
+
+struct MergeState {
+  float m, l;
+  f32x4 o0, o1;
+};
+
+// Both lanes of a swapped pair receive the same combination: the two
+// operands are ordered (even row or half first) before they are added.
+template <bool HALVES>
+__device__ __forceinline__ MergeState merge_partner(const MergeState& x) {
+  auto swap = [](float v) {
+    const uint32_t u = __float_as_uint(v);
+    auto p = HALVES ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                    : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return float2{__uint_as_float(p[0]), __uint_as_float(p[1])};
+  };
+  const float2 m = swap(x.m), l = swap(x.l);
+  const float mn = fmaxf(m.x, m.y);
+  const float ca = (m.x == -INFINITY) ? 0.f : fast_exp2(m.x - mn);
+  const float cb = (m.y == -INFINITY) ? 0.f : fast_exp2(m.y - mn);
+  MergeState r;
+  r.m = mn;
+  r.l = l.x * ca + l.y * cb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2 p = swap(x.o0[i]), q = swap(x.o1[i]);
+    r.o0[i] = p.x * ca + p.y * cb;
+    r.o1[i] = q.x * ca + q.y * cb;
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a, const int32_t* ctxp) {
+  const int lane = threadIdx.x;
+  const int head = blockIdx.x % a.num_q_heads;
+  const int n = blockIdx.x / a.num_q_heads;
+  const int hgi = head / kHeadTile, th = head % kHeadTile;
+  const int sg = lane >> 4, td = (lane & 15) * 8;
   const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kPartStride;
   // the first sixteen partials are requested in the same round as ctx (every
   // slot below nsplit exists in the workspace; unused ones are ignored)
-  constexpr int kBatch = 16;
-  float ms[kBatch], ls[kBatch];
-  f32x4 x0[kBatch], x1[kBatch];
+  constexpr int kPer = 4;  // splits per lane per round
+  float ms[kPer], ls[kPer];
+  f32x4 x0[kPer], x1[kPer];
   auto fetch = [&](int s0) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float* ps = base + static_cast<size_t>(min(s0 + j, a.nsplit - 1)) * kPartStride;
+    for (int j = 0; j < kPer; ++j) {
+      const float* ps = base + static_cast<size_t>(min(s0 + sg + 4 * j, a.nsplit - 1)) * kPartStride;
       ms[j] = ps[th];
       ls[j] = ps[kHeadTile + th];
       x0[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td);
@@ -408,49 +452,50 @@ __global__ __launch_bounds__(kAttnThreads) void msa_merge_kernel(MsaAttnArgs a, 
   const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
   const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
   if (nsplit_n <= 1) return;
-  float Mg = -INFINITY, Lg = 0.f;
-  f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit_n; s0 += kBatch) {
+  MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < nsplit_n; s0 += 4 * kPer) {
     if (s0 > 0) fetch(s0);
-    // batch max first, so the sixteen weights are independent of each other
     float mb = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (s0 + j < nsplit_n) mb = fmaxf(mb, ms[j]);
-    const float mn = fmaxf(Mg, mb);
-    const float c_old = fast_exp2(Mg - mn);  // 0 on the first batch (Mg = -inf)
+    for (int j = 0; j < kPer; ++j)
+      if (s0 + sg + 4 * j < nsplit_n) mb = fmaxf(mb, ms[j]);
+    if (mb == -INFINITY) continue;  // no split of this lane group in the round
+    const float mn = fmaxf(st.m, mb);
+    const float c_old = fast_exp2(st.m - mn);  // 0 while st.m = -inf
     float lb = 0.f;
     f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float wj = (s0 + j < nsplit_n) ? fast_exp2(ms[j] - mn) : 0.f;
+    for (int j = 0; j < kPer; ++j) {
+      const float wj = (s0 + sg + 4 * j < nsplit_n) ? fast_exp2(ms[j] - mn) : 0.f;
       lb += ls[j] * wj;
       b0 += x0[j] * wj;
       b1 += x1[j] * wj;
     }
-    Lg = Lg * c_old + lb;
-    g0 = g0 * c_old + b0;
-    g1 = g1 * c_old + b1;
-    Mg = mn;
+    st.l = st.l * c_old + lb;
+    st.o0 = st.o0 * c_old + b0;
+    st.o1 = st.o1 * c_old + b1;
+    st.m = mn;
   }
-  const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
-  uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile) * kDim;
-  const float inv = (Lg > 0.f) ? 1.f / Lg : 0.f;
-  if (th < nheads) *reinterpret_cast<u32x4*>(orow + th * kDim + td) = pack_bf16x8(g0, g1, inv);
+  st = merge_partner<false>(st);
+  st = merge_partner<true>(st);
+  if (sg == 0) {
+    uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + head) * kDim;
+    const float inv = (st.l > 0.f) ? 1.f / st.l : 0.f;
+    *reinterpret_cast<u32x4*>(orow + td) = pack_bf16x8(st.o0, st.o1, inv);
+  }
 }
 
 template <int KV_FP8, int SCALE_MODE>
 hipError_t launch(const MsaAttnArgs& a, hipStream_t s) {
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups * a.nsplit;
   if (a.scores) {
-    const size_t nbmax = static_cast<size_t>(min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow));
-    const size_t lds = max(2 * nbmax * sizeof(uint32_t), sizeof(MergeLds));
+    const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
     if (nbmax <= 256)
       hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE, 4>), dim3(static_cast<unsigned>(grid)),
-                         dim3(kAttnThreads), lds, s, a);
+                         dim3(kAttnThreads), 0, s, a);
     else
       hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE, 16>), dim3(static_cast<unsigned>(grid)),
-                         dim3(kAttnThreads), lds, s, a);
+                         dim3(kAttnThreads), 0, s, a);
   }
   else
     hipLaunchKernelGGL((msa_attn_table_kernel<KV_FP8, SCALE_MODE>), dim3(static_cast<unsigned>(grid)),
@@ -472,8 +517,8 @@ hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, h
 
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {
   if (a.nsplit <= 1) return hipSuccess;
-  const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups;
-  hipLaunchKernelGGL(msa_merge_kernel, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, s, a,
+  const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_q_heads;
+  hipLaunchKernelGGL(msa_merge_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMergeThreads), 0, s, a,
                      a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in);
   return hipGetLastError();
 }

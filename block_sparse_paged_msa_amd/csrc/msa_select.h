@@ -125,10 +125,16 @@ __device__ __forceinline__ int select_row(const uint32_t* keys, int nb, int topk
 }
 
 // ---------------------------------------------------------------------------
-// The same selection computed by one wave alone (every wave of a workgroup
-// can run it on the same LDS keys and get the same answer with no
-// workgroup barrier). hist: 256 ints of LDS private to the wave.
+// The same selection computed by one wave alone, from keys held in registers
+// (every wave of a workgroup can run it on the same row and get the same
+// answer with no workgroup barrier). It is the same MSB-first radix select,
+// with two changes that cut its passes: the bits above the highest bit where
+// the largest and smallest keys differ are shared by every key, so the first
+// 8-bit window starts at that bit; and each pass has its own histogram in
+// the wave's LDS, cleared once up front.
 // ---------------------------------------------------------------------------
+constexpr int kWaveRadixPasses = 4;
+
 struct WaveSelection {
   uint32_t T;        // keep keys > T, and keys == T among the lowest ids
   int need;          // keys equal to T that are kept (lowest ids first)
@@ -137,28 +143,45 @@ struct WaveSelection {
   bool all_eq_kept;  // every key >= T is kept
 };
 
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// The keys of blocks e = lane + 64*i, i < KR, in registers (0 past nb);
-// blocks from 64*KR on are read from LDS when needed.
+// The keys of blocks e = lane + 64*i, i < KR, in registers; slots at or
+// past nb are ignored. Blocks from 64*KR on come from tail_key(e).
 template <int KR>
 struct WaveKeys {
   uint32_t k[KR];
 };
 
-template <int KR>
-__device__ __forceinline__ void wave_load_keys(const uint32_t* keys, int nb, WaveKeys<KR>& wk) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < KR; ++i) wk.k[i] = (lane + 64 * i < nb) ? keys[lane + 64 * i] : 0u;
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-template <int KR>
-__device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const WaveKeys<KR>& wk, int nb, int topk,
-                                                     int* hist) {
+// Clears a wave's kWaveRadixPasses x 256 histogram counters.
+__device__ __forceinline__ void wave_clear_hist(int (*hist)[256]) {
+  const int lane = threadIdx.x & 63;
+  i32x4* h = reinterpret_cast<i32x4*>(&hist[0][0]);
+#pragma unroll
+  for (int i = 0; i < kWaveRadixPasses; ++i) h[i * 64 + lane] = i32x4{0, 0, 0, 0};
+}
+
+// Max / min of an unsigned value over the wave, in every lane (DPP inside
+// each 16-lane row, then the row and half swaps).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t x) {
+  auto op = [](uint32_t p, uint32_t q) { return MAX ? max(p, q) : min(p, q); };
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xB1, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x4E, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x141, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x140, 0xf, 0xf, false)));
+  auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(p[0], p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(q[0], q[1]);
+}
+
+// hist: this wave's kWaveRadixPasses x 256 counters, all zero on entry.
+template <int KR, typename TailKey>
+__device__ __forceinline__ WaveSelection wave_select(const WaveKeys<KR>& wk, int nb, int topk, int (*hist)[256],
+                                                     TailKey tail_key) {
   const int lane = threadIdx.x & 63;
   WaveSelection w;
   w.kk = min(topk, nb);
@@ -167,27 +190,50 @@ __device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const
   w.need = 0;
   w.all_eq_kept = true;
   if (!w.partial) return w;
-  uint32_t prefix = 0;
-  int need = w.kk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
-    wave_lds_order();
+  for (int i = 0; i < KR; ++i)
+    if (lane + 64 * i < nb) {
+      kmax = max(kmax, wk.k[i]);
+      kmin = min(kmin, wk.k[i]);
+    }
+  for (int e = lane + 64 * KR; e < nb; e += 64) {
+    const uint32_t k = tail_key(e);
+    kmax = max(kmax, k);
+    kmin = min(kmin, k);
+  }
+  // uniform after the reductions
+  kmax = __builtin_amdgcn_readfirstlane(wave_extreme_u32<true>(kmax));
+  kmin = __builtin_amdgcn_readfirstlane(wave_extreme_u32<false>(kmin));
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0u) {  // every key is equal: the lowest K' ids
+    w.T = kmax;
+    w.need = w.kk;
+    w.all_eq_kept = false;
+    return w;
+  }
+  int top = 31 - __clz(diff);                                       // highest bit still open
+  uint32_t prefix = (top == 31) ? 0u : (kmax & (~0u << (top + 1)));  // bits fixed so far
+  int need = w.kk;
+#pragma unroll 1
+  for (int pass = 0; pass < kWaveRadixPasses; ++pass) {
+    const int width = min(8, top + 1);
+    const int shift = top + 1 - width;
+    const uint32_t fixed = (top == 31) ? 0u : (~0u << (top + 1));
+    const uint32_t dmask = (1u << width) - 1u;
+    int* h = hist[pass];
     auto bin = [&](uint32_t k) {
-      const bool match = (shift == 24) || ((k >> (shift + 8)) == (prefix >> (shift + 8)));
-      if (match) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      if ((k & fixed) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1);
     };
 #pragma unroll
     for (int i = 0; i < KR; ++i)
       if (lane + 64 * i < nb) bin(wk.k[i]);
-    for (int e = lane + 64 * KR; e < nb; e += 64) bin(keys[e]);
+    for (int e = lane + 64 * KR; e < nb; e += 64) bin(tail_key(e));
     wave_lds_order();
-    int c[4], local = 0;  // lane owns digits 255-4*lane .. 252-4*lane (descending)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = hist[255 - 4 * lane - i];
-      local += c[i];
-    }
+    // lane owns digits 255-4*lane .. 252-4*lane (descending)
+    const i32x4 h4 = *reinterpret_cast<const i32x4*>(&h[252 - 4 * lane]);
+    const int c[4] = {h4[3], h4[2], h4[1], h4[0]};
+    const int local = c[0] + c[1] + c[2] + c[3];
     const int incl = wave_inclusive_scan(local);
     int run = incl - local, my_digit = 0, my_need = 0, my_cnt = 0;
     bool found = false;
@@ -206,15 +252,15 @@ __device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const
     prefix |= static_cast<uint32_t>(__builtin_amdgcn_readlane(my_digit, src)) << shift;
     need = __builtin_amdgcn_readlane(my_need, src);
     const int cnt = __builtin_amdgcn_readlane(my_cnt, src);
-    wave_lds_order();
     if (need == cnt) {
       // every key sharing the prefix so far is kept: keys >= prefix (lower
       // bits zero) are exactly the K' largest, no tie straddles the cut
       w.T = prefix;
-      w.need = 0;
       w.all_eq_kept = true;
       return w;
     }
+    if (shift == 0) break;
+    top = shift - 1;
   }
   w.T = prefix;
   w.need = need;
@@ -222,43 +268,56 @@ __device__ __forceinline__ WaveSelection wave_select(const uint32_t* keys, const
   return w;
 }
 
-// Visits the kept blocks in ascending id order: visit(rank, block) in the
-// lane that examined the block. Returns the context length
-// 128*K' - (block nb-1 kept ? 128*nb - v : 0) in every lane.
-template <int KR, typename Visit>
-__device__ __forceinline__ int wave_compact(const uint32_t* keys, const WaveKeys<KR>& wk, int nb, int v,
-                                            const WaveSelection& w, Visit visit) {
+// Walks the kept blocks in ascending id order, 64 blocks at a time, keeping
+// only population counts of the keep ballots, and calls found(rank, block,
+// payload) for every rank in [q0, q1) (all arguments uniform, every lane
+// calls it). payload is pay[i] of the lane holding the block in register
+// slot i, or tail_pay(e) past the register slots. Returns the context
+// length 128*K' - (block nb-1 kept ? 128*nb - v : 0) in every lane.
+template <int KR, typename TailKey, typename TailPay, typename Found>
+__device__ __forceinline__ int wave_locate(const WaveKeys<KR>& wk, const int (&pay)[KR], int nb, int v,
+                                           const WaveSelection& w, int q0, int q1, TailKey tail_key,
+                                           TailPay tail_pay, Found found) {
   const int lane = threadIdx.x & 63;
   const unsigned long long lt = (1ull << lane) - 1ull;
-  int carry = 0, carry_eq = 0;
+  int carry = 0, carry_eq = 0, q = q0;
   bool last_kept = false;
-  auto step = [&](int e, uint32_t k) {
-    const bool valid = e < nb;
-    bool keep;
-    if (!w.partial) {
-      keep = valid;
-    } else if (w.all_eq_kept) {
-      keep = valid && k >= w.T;
-    } else {
-      const bool eq = valid && k == w.T;
-      const unsigned long long em = __ballot(eq);
-      const int rank_eq = carry_eq + __popcll(em & lt);
-      carry_eq += __popcll(em);
-      keep = valid && (k > w.T || (eq && rank_eq < w.need));
-    }
+  q1 = min(q1, w.kk);
+  auto keep_of = [&](bool valid, uint32_t k) {
+    if (!w.partial) return valid;
+    if (w.all_eq_kept) return valid && k >= w.T;
+    const bool eq = valid && k == w.T;
+    const unsigned long long em = __ballot(eq);
+    const int rank_eq = carry_eq + __popcll(em & lt);
+    carry_eq += __popcll(em);
+    return valid && (k > w.T || (eq && rank_eq < w.need));
+  };
+  // one chunk of 64 blocks starting at base; get_pay() gives the lane's payload
+  auto chunk = [&](int base, uint32_t k, auto get_pay) {
+    const bool keep = keep_of(base + lane < nb, k);
     const unsigned long long km = __ballot(keep);
-    if (keep) {
-      visit(carry + __popcll(km & lt), e);
-      if (e == nb - 1) last_kept = true;
+    const int c = __popcll(km);
+    if (nb - 1 - base < 64) last_kept = (km >> (nb - 1 - base)) & 1ull;
+    if (q < q1 && q < carry + c) {
+      const int below = __popcll(km & lt);
+      const int p = get_pay();
+      do {
+        const unsigned long long hit = __ballot(keep && below == q - carry);
+        const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(hit)) - 1);
+        found(q, base + src, __builtin_amdgcn_readlane(p, src));
+        ++q;
+      } while (q < q1 && q < carry + c);
     }
-    carry += __popcll(km);
+    carry += c;
   };
 #pragma unroll
   for (int i = 0; i < KR; ++i)
-    if (64 * i < nb) step(lane + 64 * i, wk.k[i]);
-  for (int base = 64 * KR; base < nb; base += 64) step(base + lane, base + lane < nb ? keys[base + lane] : 0u);
-  const bool lk = __ballot(last_kept) != 0ull;
-  return kPage * w.kk - (lk ? kPage * nb - v : 0);
+    if (64 * i < nb) chunk(64 * i, wk.k[i], [&] { return pay[i]; });
+  for (int base = 64 * KR; base < nb; base += 64) {
+    const int e = min(base + lane, nb - 1);
+    chunk(base, tail_key(e), [&] { return tail_pay(e); });
+  }
+  return kPage * w.kk - (last_kept ? kPage * nb - v : 0);
 }
 
 }  // namespace msa

@@ -247,6 +247,39 @@ def test_fused_decode_equals_steps_and_oracle(gpu_lib):
     assert torch.equal(o3.out, o.out) and torch.equal(o3.table, o.table)
 
 
+@pytest.mark.parametrize("topk", [1, 5, 16, 64])
+def test_fused_selection_with_tied_scores(gpu_lib, topk):
+    """Index queries and keys in {-1, 0, 1}: every token score is an integer,
+    so many blocks share their pooled maximum and the cut falls inside a tie
+    (the lowest block ids are kept). The lengths span rows whose keys all sit
+    in registers and a row past 1024 blocks whose last keys are re-read from
+    LDS during the selection."""
+    L = [140000, 33000, 9000, 129, 1, 2047]
+    ql = [1, 1, 2, 1, 1, 3]
+    b = syn.make_batch("ties", 130 + topk, L, ql, topk=topk, num_q_heads=16, max_seq_len=140032)
+    tern = lambda x: syn.to_bf16_bits(np.clip(np.round(O.bf16_to_f64(x)), -1.0, 1.0))
+    b = dataclasses.replace(b, index_q=tern(b.index_q), index_k=tern(b.index_k))
+    print(f"[ties] topk={topk} rows={b.num_rows} pages={b.num_pages}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    rows = list(range(b.num_rows))
+    ref = check_scores(b, scores, rows)
+    meta = O.build_metadata(b.seq_lens, b.query_lens)
+    straddled = 0
+    for n in rows:
+        nb = O.num_blocks(O.visible_keys(meta["row_pos"][n]))
+        assert np.array_equal(scores[n][:nb], ref[n][:nb].astype(np.float32)), f"row {n}: integer scores differ"
+        if topk < nb:
+            srt = np.sort(ref[n][:nb])[::-1]
+            straddled += int(srt[topk - 1] == srt[topk])
+    assert straddled >= 2, "the crafted inputs should put the cut inside a tie on several rows"
+    check_selection(b, scores, table, ctx, sel, rows)
+    check_attention(b, H.bf16_to_np(o.out), table, ctx, rows)
+
+
 def test_fused_decode_repeat_and_graph_replay_bitwise(gpu_lib):
     b = syn.make_batch("graph", 120, [20000, 3000, 7000], [4, 1, 2], topk=16, num_q_heads=16)
     d = H.upload(b)
