@@ -51,22 +51,22 @@ __device__ __forceinline__ void load_sub(const MsaAttnArgs& a, int sub, int lane
   if constexpr (!KV_FP8) {
     const uint16_t* kp = static_cast<const uint16_t*>(a.k_cache) + base + lane * 8;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) s.k[kc] = *reinterpret_cast<const bf16x8*>(kp + kc * 512);
+    for (int kc = 0; kc < 4; ++kc) s.k[kc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + kc * 512));
     const uint16_t* vp = static_cast<const uint16_t*>(a.v_cache) + base + (lane & 15) * kSub + (lane >> 4) * 4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) s.v[dt] = *reinterpret_cast<const i16x4*>(vp + dt * 16 * kSub);
+    for (int dt = 0; dt < 8; ++dt) s.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const i16x4*>(vp + dt * 16 * kSub));
   } else {
     const uint8_t* kp = static_cast<const uint8_t*>(a.k_cache) + base + lane * 8;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(kp + kc * 512);
+      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kp + kc * 512));
       const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
       s.k[kc] = __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
     }
     const uint8_t* vp = static_cast<const uint8_t*>(a.v_cache) + base + (lane & 15) * kSub + (lane >> 4) * 4;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      s.v[dt] = __builtin_bit_cast(i16x4, fp8x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vp + dt * 16 * kSub)));
+      s.v[dt] = __builtin_bit_cast(i16x4, fp8x4_to_bf16x4(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + dt * 16 * kSub))));
   }
   if constexpr (SCALE_MODE == 2) {
     s.ks = *reinterpret_cast<const f32x4*>(a.k_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);

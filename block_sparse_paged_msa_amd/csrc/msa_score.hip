@@ -47,7 +47,7 @@ __device__ __forceinline__ void load_page(const MsaScoreArgs& a, int page, int l
   for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
-      kb[tt][kc] = *reinterpret_cast<const bf16x8*>(kp + tt * (kSub * kDim) + (kc * 64 + lane) * 8);
+      kb[tt][kc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + tt * (kSub * kDim) + (kc * 64 + lane) * 8));
 }
 
 __device__ __forceinline__ int page_of(const MsaScoreArgs& a, const Unit& w) {
