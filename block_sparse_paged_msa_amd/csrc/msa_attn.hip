@@ -25,6 +25,8 @@
 // selection is deterministic, so all workgroups of a row agree, and no
 // workgroup waits for another. The first workgroup of each row also writes the
 // page-16 table, the context length and the selected block ids.
+#include <type_traits>
+
 #include "msa_select.h"
 
 using namespace msa;
@@ -36,38 +38,48 @@ constexpr int kPartStride = 2 * kHeadTile + kHeadTile * kDim;  // m[16], l[16], 
 constexpr int kLdsRow = kDim + 4;                               // padded [head][dim] rows
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / kPage;
 
+// One 16-token sub-page of K and V in registers, as loaded: bf16 operands, or
+// the raw e4m3fn codes (half the registers), widened to bf16 at use.
 template <int KV_FP8, int SCALE_MODE>
 struct SubPage {
-  bf16x8 k[4];   // A operand of S^T: token lane%16, dims kc*32 + 8*(lane/16)..+7
-  i16x4 v[8];    // A operand of O^T: dim dt*16 + lane%16, tokens 4*(lane/16)..+3
+  using KRaw = typename std::conditional<KV_FP8 != 0, u32x2, bf16x8>::type;
+  using VRaw = typename std::conditional<KV_FP8 != 0, uint32_t, i16x4>::type;
+  KRaw k[4];     // A operand of S^T: token lane%16, dims kc*32 + 8*(lane/16)..+7
+  VRaw v[8];     // A operand of O^T: dim dt*16 + lane%16, tokens 4*(lane/16)..+3
   f32x4 ks, vs;  // per-token scales of tokens 4*(lane/16)..+3
+
+  __device__ __forceinline__ bf16x8 k_op(int kc) const {
+    if constexpr (KV_FP8 != 0) {
+      const u32x2 lo = fp8x4_to_bf16x4(k[kc].x), hi = fp8x4_to_bf16x4(k[kc].y);
+      return __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
+    } else {
+      return k[kc];
+    }
+  }
+  __device__ __forceinline__ i16x4 v_op(int dt) const {
+    if constexpr (KV_FP8 != 0)
+      return __builtin_bit_cast(i16x4, fp8x4_to_bf16x4(v[dt]));
+    else
+      return v[dt];
+  }
 };
 
 template <int KV_FP8, int SCALE_MODE>
 __device__ __forceinline__ void load_sub(const MsaAttnArgs& a, int sub, int lane, SubPage<KV_FP8, SCALE_MODE>& s) {
-  const size_t base = static_cast<size_t>(sub) * (kSub * kDim);
+  using SP = SubPage<KV_FP8, SCALE_MODE>;
+  using KRaw = typename SP::KRaw;
+  using VRaw = typename SP::VRaw;
+  constexpr int elt = KV_FP8 ? 1 : 2;  // bytes per element
+  const size_t base = static_cast<size_t>(sub) * (kSub * kDim) * elt;
   // K sub-pages are shuffled tiles [4][4][16][8]: operand kc of lane l is the
   // 8 elements at (kc*64 + l)*8, so every operand load is one contiguous run.
-  if constexpr (!KV_FP8) {
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k_cache) + base + lane * 8;
+  const char* kp = static_cast<const char*>(a.k_cache) + base + lane * 8 * elt;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) s.k[kc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + kc * 512));
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v_cache) + base + (lane & 15) * kSub + (lane >> 4) * 4;
+  for (int kc = 0; kc < 4; ++kc) s.k[kc] = __builtin_nontemporal_load(reinterpret_cast<const KRaw*>(kp + kc * 512 * elt));
+  const char* vp = static_cast<const char*>(a.v_cache) + base + ((lane & 15) * kSub + (lane >> 4) * 4) * elt;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) s.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const i16x4*>(vp + dt * 16 * kSub));
-  } else {
-    const uint8_t* kp = static_cast<const uint8_t*>(a.k_cache) + base + lane * 8;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kp + kc * 512));
-      const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
-      s.k[kc] = __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
-    }
-    const uint8_t* vp = static_cast<const uint8_t*>(a.v_cache) + base + (lane & 15) * kSub + (lane >> 4) * 4;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      s.v[dt] = __builtin_bit_cast(i16x4, fp8x4_to_bf16x4(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + dt * 16 * kSub))));
-  }
+  for (int dt = 0; dt < 8; ++dt)
+    s.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const VRaw*>(vp + dt * 16 * kSub * elt));
   if constexpr (SCALE_MODE == 2) {
     s.ks = *reinterpret_cast<const f32x4*>(a.k_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
     s.vs = *reinterpret_cast<const f32x4*>(a.v_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
@@ -92,10 +104,10 @@ __device__ __forceinline__ void attend_pair(WaveState& st, SubPage<KV_FP8, SCALE
   const int tok0 = 4 * (lane >> 4);
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) s0 = mfma_16x16x32(sp[0].k[kc], qb[kc], s0);
+  for (int kc = 0; kc < 4; ++kc) s0 = mfma_16x16x32(sp[0].k_op(kc), qb[kc], s0);
   if (nval1 > 0) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) s1 = mfma_16x16x32(sp[1].k[kc], qb[kc], s1);
+    for (int kc = 0; kc < 4; ++kc) s1 = mfma_16x16x32(sp[1].k_op(kc), qb[kc], s1);
   }
   float z0[4], z1[4], mloc = -INFINITY;
 #pragma unroll
@@ -120,25 +132,20 @@ __device__ __forceinline__ void attend_pair(WaveState& st, SubPage<KV_FP8, SCALE
   st.m = m_new;
   // V slots past the context can hold anything (even NaN codes): zero them so
   // that a zero probability cannot meet a NaN in the product.
-  if (nval0 < kSub) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+  auto v_masked = [&](const SubPage<KV_FP8, SCALE_MODE>& x, int dt, int nval) {
+    i16x4 op = x.v_op(dt);
+    if (nval < kSub) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (tok0 + i >= nval0) sp[0].v[dt][i] = 0;
-  }
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16(sp[0].v[dt], p0, st.o[dt] * alpha);
-  if (nval1 > 0) {
-    if (nval1 < kSub) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tok0 + i >= nval1) sp[1].v[dt][i] = 0;
+        if (tok0 + i >= nval) op[i] = 0;
     }
+    return op;
+  };
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16(sp[1].v[dt], p1, st.o[dt]);
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16(v_masked(sp[0], dt, nval0), p0, st.o[dt] * alpha);
+  if (nval1 > 0) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = mfma_16x16x16(v_masked(sp[1], dt, nval1), p1, st.o[dt]);
   }
 }
 
@@ -278,7 +285,7 @@ __device__ __forceinline__ void write_zero_row(const MsaAttnArgs& a, int n, int 
 // Table mode: the row's sub-pages and context length come from the caller.
 // Q and the split's table entries are fetched together at the start.
 template <int KV_FP8, int SCALE_MODE>
-__global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void msa_attn_table_kernel(MsaAttnArgs a) {
   __shared__ MergeLds ml;
   __shared__ int s_sub[kMaxSplitTokens / kSub];
   const int split = blockIdx.x % a.nsplit;
@@ -308,7 +315,7 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_table_kernel(MsaAttnArg
 // workgroup barrier. KEY_REGS keys per lane sit in registers (64*KEY_REGS
 // blocks); keys and pages past them are read from global memory.
 template <int KV_FP8, int SCALE_MODE, int KEY_REGS>
-__global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void msa_attn_select_kernel(MsaAttnArgs a) {
   __shared__ MergeLds ml;
   __shared__ __attribute__((aligned(16))) int s_hist[4][kWaveRadixPasses][256];
   __shared__ int s_wpage[4][kMaxSplitBlocks];  // raw page of each of the wave's ranks
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(kAttnThreads) void msa_attn_select_kernel(MsaAttnAr
 // Combines the split partials of rows that needed more than one split. One
 // wave per (row, query head): lane group g = lane/16 takes splits g, g+4,
 // g+8, ... and eight dims (lane%16)*8.. of each, so one round of loads
-// fetches sixteen splits of 512 B. The four groups are then combined through
+// fetches thirty-two splits of 512 B. The four groups are then combined through
 // row and half swaps. All weights are log2-domain 2^(m_s - max).
 constexpr int kMergeThreads = 64;
 
@@ -433,9 +440,9 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   const int hgi = head / kHeadTile, th = head % kHeadTile;
   const int sg = lane >> 4, td = (lane & 15) * 8;
   const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kPartStride;
-  // the first sixteen partials are requested in the same round as ctx (every
-  // slot below nsplit exists in the workspace; unused ones are ignored)
-  constexpr int kPer = 4;  // splits per lane per round
+  // the first thirty-two partials are requested in the same round as ctx
+  // (every slot below nsplit exists in the workspace; unused ones are ignored)
+  constexpr int kPer = 8;  // splits per lane per round
   float ms[kPer], ls[kPer];
   f32x4 x0[kPer], x1[kPer];
   auto fetch = [&](int s0) {

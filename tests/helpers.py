@@ -79,6 +79,14 @@ def upload(b: syn.Batch, device="cuda") -> DeviceBatch:
     return d
 
 
+def read_metadata(d: DeviceBatch) -> dict:
+    """The batch metadata arrays as they are on the device (no launch)."""
+    N = d.host.num_rows
+    return {"cu_seqlens_q": d.cu_q.cpu().numpy(), "cu_seqlens_k": d.cu_k.cpu().numpy(),
+            "cu_blocks": d.cu_blocks.cpu().numpy(), "cu_units": d.cu_units.cpu().numpy(),
+            "row_req": d.row_req[:N].cpu().numpy(), "row_pos": d.row_pos[:N].cpu().numpy()}
+
+
 def run_metadata(d: DeviceBatch) -> dict:
     msa.msa_build_metadata(d.cbatch)
     N = d.host.num_rows

@@ -73,6 +73,16 @@ def check_selection_valid(b, oracle_scores, sel, rows):
             assert np.all(s[others] - tol[others] <= thr), f"row {n}: a dropped block is clearly above the k-th"
 
 
+def check_metadata(b, got):
+    """Bit-exact batch metadata, including the per-request unit counts."""
+    ref = O.build_metadata(b.seq_lens, b.query_lens)
+    for key in ("cu_seqlens_q", "cu_seqlens_k", "cu_blocks", "row_req", "row_pos"):
+        assert got[key].tolist() == ref[key].tolist(), key
+    L, ql = b.seq_lens.astype(np.int64), b.query_lens.astype(np.int64)
+    units = [0] + np.cumsum(-(-L // 128) * -(-ql // 64)).tolist()
+    assert got["cu_units"].tolist() == units, "cu_units"
+
+
 def check_attention(b, out, table, ctx, rows):
     ref = O.attention_from_table(b, table, ctx, rows)
     err = np.abs(out[rows] - ref)
@@ -99,13 +109,7 @@ def test_metadata_bitexact(gpu_lib, case):
     else:
         b = syn.random_batch(40 + case, num_reqs=37 + 500 * (case - len(META_CASES)), max_len=3000, max_q=9)
     d = H.upload(b)
-    got = H.run_metadata(d)
-    ref = O.build_metadata(b.seq_lens, b.query_lens)
-    for key in ("cu_seqlens_q", "cu_seqlens_k", "cu_blocks", "row_req", "row_pos"):
-        assert got[key].tolist() == ref[key].tolist(), key
-    L, ql = b.seq_lens.astype(np.int64), b.query_lens.astype(np.int64)
-    units = [0] + np.cumsum(-(-L // 128) * -(-ql // 64)).tolist()
-    assert got["cu_units"].tolist() == units
+    check_metadata(b, H.run_metadata(d))
 
 
 # ---------------------------------------------------------------------------
@@ -220,11 +224,20 @@ def test_attention_zero_context_rows_give_zeros(gpu_lib):
 # ---------------------------------------------------------------------------
 # the fused decode step
 # ---------------------------------------------------------------------------
-def test_fused_decode_equals_steps_and_oracle(gpu_lib):
-    b = syn.make_batch("fused", 110, [9000, 700, 129, 1, 20000], [1, 2, 1, 1, 4], topk=16, num_q_heads=16)
+FUSED_CASES = [
+    ([9000, 700, 129, 1, 20000], [1, 2, 1, 1, 4]),
+    ([9000, 0, 700, 129, 300, 1], [1, 0, 2, 0, 3, 1]),   # empty request, requests with no rows
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+def test_fused_decode_equals_steps_and_oracle(gpu_lib, case):
+    L, ql = FUSED_CASES[case]
+    b = syn.make_batch("fused", 110 + case, L, ql, topk=16, num_q_heads=16)
     d = H.upload(b)
     o = H.alloc_decode(d)
     H.run_decode(d, o)
+    check_metadata(b, H.read_metadata(d))  # written by the fused step
     scores = o.scores.cpu().numpy()
     table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
     out = H.bf16_to_np(o.out)
@@ -376,10 +389,7 @@ def test_workload_parity(gpu_lib, name, scale_mode):
     o = H.alloc_decode(d)
     H.run_decode(d, o)
     torch.cuda.synchronize()
-    meta = H.run_metadata(d)
-    ref_meta = O.build_metadata(b.seq_lens, b.query_lens)
-    for key in ("cu_seqlens_q", "cu_seqlens_k", "cu_blocks", "row_req", "row_pos"):
-        assert meta[key].tolist() == ref_meta[key].tolist(), key
+    check_metadata(b, H.read_metadata(d))  # as written by the fused step itself
     scores = o.scores.cpu().numpy()
     table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
     out = H.bf16_to_np(o.out)
