@@ -149,6 +149,7 @@ msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, 
   a.num_pages = b->num_pages;
   a.len_cap = len_cap(b);
   a.write_meta = write_meta ? 1 : 0;
+  a.xcd_remap = b->num_rows > kRowsPerUnit ? 1 : 0;
   // first-group slots r*S + j, S = ceil(len_cap/128); extra row groups are at
   // most S * floor(N/64) (sum_r (ceil(ql_r/64) - 1) <= N/64)
   const int64_t S = ceil_div(a.len_cap, kPage) > 0 ? ceil_div(a.len_cap, kPage) : 1;

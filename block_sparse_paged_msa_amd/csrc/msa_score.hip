@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   const bool writer = a.write_meta && blockIdx.x == 0;
   const int slots_a = R * a.blocks_per_req;
   const int nwaves = gridDim.x * kWavesPerWg;
-  int u = blockIdx.x * kWavesPerWg + wave;
+  int u = (a.xcd_remap ? xcd_local_block() : static_cast<int>(blockIdx.x)) * kWavesPerWg + wave;
 
   // Decode-only launches (at most 64 rows in all, so no request has a row
   // group past the first) with no metadata to write need no prefix: a wave

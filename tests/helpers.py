@@ -154,7 +154,7 @@ def alloc_decode(d: DeviceBatch, with_scores: bool = True) -> DecodeOut:
     N, hq, topk = b.num_rows, b.num_q_heads, b.topk
     wsb = msa.msa_workspace_bytes(N, hq, 128 * topk, 0 if with_scores else b.ld_s)
     return DecodeOut(
-        out=torch.zeros((N, hq, 128), dtype=torch.int16, device="cuda"),
+        out=torch.full((N, hq, 128), 0x7FC0, dtype=torch.int16, device="cuda"),  # bf16 NaN: unwritten shows
         table=torch.full((N, 8 * topk), SENTINEL_I32, dtype=torch.int32, device="cuda"),
         ctx=torch.full((N,), SENTINEL_I32, dtype=torch.int32, device="cuda"),
         sel=torch.full((N, topk), SENTINEL_I32, dtype=torch.int32, device="cuda"),

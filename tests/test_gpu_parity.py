@@ -260,6 +260,32 @@ def test_fused_decode_equals_steps_and_oracle(gpu_lib, case):
     assert torch.equal(o3.out, o.out) and torch.equal(o3.table, o.table)
 
 
+FUSED_SHAPES = [
+    # (name, lengths, query rows, top-k, query heads): many splits per row
+    # (the merge takes several rounds), and head groups past the first
+    ("topk300", [140000, 70000], [1, 2], 300, 16),
+    ("hq24", [9000, 3000, 20000], [1, 3, 2], 24, 24),
+    ("hq8", [5000, 129, 70000], [2, 1, 1], 40, 8),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_SHAPES)))
+def test_fused_decode_shapes(gpu_lib, case):
+    name, L, ql, topk, hq = FUSED_SHAPES[case]
+    b = syn.make_batch(name, 140 + case, L, ql, topk=topk, num_q_heads=hq)
+    print(f"[fused] {name} rows={b.num_rows} topk={topk} hq={hq}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    check_metadata(b, H.read_metadata(d))
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    rows = list(range(b.num_rows))
+    check_scores(b, scores, rows)
+    check_selection(b, scores, table, ctx, sel, rows)
+    check_attention(b, H.bf16_to_np(o.out), table, ctx, rows)
+
+
 @pytest.mark.parametrize("topk", [1, 5, 16, 64])
 def test_fused_selection_with_tied_scores(gpu_lib, topk):
     """Index queries and keys in {-1, 0, 1}: every token score is an integer,
