@@ -308,12 +308,102 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   attend_split<KV_FP8, SCALE_MODE>(a, ml, n, hgi, split, ctx, qb, [&](int sp) { return s_sub[sp - sp0]; });
 }
 
-// Fused mode: select the row's blocks from its scores, then attend. Every
-// wave loads the row's keys and block-table entries into registers and runs
-// the selection itself (wave_select / wave_compact), keeping only the pages
-// of its own sub-pages, so nothing before the attention's own merge needs a
-// workgroup barrier. KEY_REGS keys per lane sit in registers (64*KEY_REGS
-// blocks); keys and pages past them are read from global memory.
+// Fused mode, after the selection: attend over this split and write the
+// selection's outputs. s_wpage / s_wsel hold the raw page and block id of the
+// ranks [wblk0, wblk0 + wnblk) this wave's sub-pages fall in.
+template <int KV_FP8, int SCALE_MODE>
+__device__ __forceinline__ void attend_selected(const MsaAttnArgs& a, MergeLds& ml, const int* s_wpage,
+                                                const int* s_wsel, int n, int hgi, int split, int sp_begin,
+                                                int wblk0, int wnblk, int kk, int ctx_row, const bf16x8 (&qb)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int pmax = a.num_subpages / kSubsPerPage - 1;
+  const int ctx = min(ctx_row, a.max_ctx);
+  if (ctx > 0 && split * a.split_tok < ctx)
+    attend_split<KV_FP8, SCALE_MODE>(a, ml, n, hgi, split, ctx, qb, [&](int sp) {
+      return 8 * clampi(s_wpage[(sp >> 3) - wblk0], 0, pmax) + (sp & 7);
+    });
+  else if (ctx == 0 && split == 0)
+    write_zero_row(a, n, hgi);
+
+  // The selection's outputs, written once the attention's loads are out so
+  // that no wait for these stores holds them back. Rank q is written by the
+  // wave whose sub-pages start its block, in head group 0 (every rank lies in
+  // a split that attends, since 128*q < ctx).
+  if (hgi == 0 && (sp_begin & 7) == 0) {
+    int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
+    const int nq = min(wblk0 + wnblk, kk) - wblk0;
+    for (int idx = lane; idx < 8 * nq; idx += 64) trow[8 * wblk0 + idx] = 8 * s_wpage[idx >> 3] + (idx & 7);
+    if (a.sel_out)
+      for (int m = lane; m < nq; m += 64) a.sel_out[static_cast<size_t>(n) * a.topk + wblk0 + m] = s_wsel[m];
+  }
+  if (split == 0 && hgi == 0 && (threadIdx.x >> 6) == 0) {  // context length and the zero tail past K'
+    int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
+    for (int m = 8 * kk + lane; m < 8 * a.topk; m += 64) trow[m] = 0;
+    if (a.sel_out)
+      for (int m = kk + lane; m < a.topk; m += 64) a.sel_out[static_cast<size_t>(n) * a.topk + m] = -1;
+    if (lane == 0) a.ctx_out[n] = ctx_row;
+  }
+}
+
+// Fused mode for rows of at most 256*KC blocks: the four waves select
+// together (coop_select / coop_locate: shared radix histogram, one barrier
+// per pass), then attend.
+template <int KV_FP8, int SCALE_MODE, int KC>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void msa_attn_coop_kernel(MsaAttnArgs a) {
+  __shared__ MergeLds ml;
+  __shared__ __attribute__((aligned(16))) CoopLds cl;
+  __shared__ int s_wpage[4][kMaxSplitBlocks];  // raw page of each of the wave's ranks
+  __shared__ int s_wsel[4][kMaxSplitBlocks];   // and its block id
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x % a.nsplit;
+  const int rest = blockIdx.x / a.nsplit;
+  const int hgi = rest % a.num_hgroups;
+  const int n = rest / a.num_hgroups;
+  const int nbmax = min(min(a.ld_s, a.ld_bt), 256 * KC);
+  // round 1: the row's keys, its request and position, and Q (indices
+  // clamped so that every load issues unconditionally); round 2: the
+  // block-table entries, which arrive during the radix passes
+  const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
+  float kraw[KC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) kraw[i] = srow[min(tid + 256 * i, max(nbmax, 1) - 1)];
+  const int r = clampi(a.row_req[n], 0, a.num_reqs - 1);
+  const int v = a.row_pos[n] + 1;
+  bf16x8 qb[4];
+  load_q(a, n, hgi, qb);
+  coop_clear(cl);
+  const int nb = clampi((v + kPage - 1) / kPage, 0, nbmax);
+  const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
+  int pg[KC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) pg[i] = bt[min(tid + 256 * i, max(nb, 1) - 1)];
+  uint32_t k[KC];
+#pragma unroll
+  for (int i = 0; i < KC; ++i) k[i] = order_key(kraw[i]);
+  const WaveSelection ws = coop_select<KC>(k, nb, a.topk, cl);
+  // this wave's sub-pages and the blocks (ranks) they fall in
+  const int sp_per_wave = a.split_tok / (4 * kSub);
+  const int sp_begin = split * (a.split_tok / kSub) + wave * sp_per_wave;
+  const int wblk0 = sp_begin >> 3;
+  const int wnblk = max(1, sp_per_wave >> 3);
+  const int ctx = coop_locate<KC>(k, pg, nb, v, ws, wblk0, wblk0 + wnblk, cl, [&](int q, int e, int page) {
+    if (lane == 0) {
+      s_wpage[wave][q - wblk0] = page;
+      s_wsel[wave][q - wblk0] = e;
+    }
+  });
+  wave_lds_order();  // this wave's pages
+  attend_selected<KV_FP8, SCALE_MODE>(a, ml, s_wpage[wave], s_wsel[wave], n, hgi, split, sp_begin, wblk0, wnblk,
+                                      ws.kk, ctx, qb);
+}
+
+// Fused mode for longer rows: every wave loads the row's keys and
+// block-table entries into registers and runs the selection itself
+// (wave_select / wave_locate), keeping only the pages of its own sub-pages,
+// so nothing before the attention's own merge needs a workgroup barrier.
+// KEY_REGS keys per lane sit in registers (64*KEY_REGS blocks); keys and
+// pages past them are read from global memory.
 template <int KV_FP8, int SCALE_MODE, int KEY_REGS>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void msa_attn_select_kernel(MsaAttnArgs a) {
   __shared__ MergeLds ml;
@@ -327,12 +417,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int hgi = rest % a.num_hgroups;
   const int n = rest / a.num_hgroups;
   const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
-  // round 1: the row's keys (nb <= nbmax is not known yet), its request and
-  // position, and Q; round 2: the block-table entries, which arrive while the
-  // radix passes run
   const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
-  // (indices clamped so that every load is issued unconditionally, in one
-  // round; slots at or past nb are ignored by the selection)
   WaveKeys<KEY_REGS> wk;
   float kraw[KEY_REGS];
 #pragma unroll
@@ -353,46 +438,19 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   auto tail_page = [&](int e) { return bt[e]; };
   wave_lds_order();  // histograms cleared
   const WaveSelection ws = wave_select(wk, nb, a.topk, s_hist[wave], tail_key);
-  // this wave's sub-pages and the blocks (ranks) they fall in
   const int sp_per_wave = a.split_tok / (4 * kSub);
   const int sp_begin = split * (a.split_tok / kSub) + wave * sp_per_wave;
   const int wblk0 = sp_begin >> 3;
   const int wnblk = max(1, sp_per_wave >> 3);
-  int ctx = wave_locate(wk, pg, nb, v, ws, wblk0, wblk0 + wnblk, tail_key, tail_page, [&](int q, int e, int page) {
+  const int ctx = wave_locate(wk, pg, nb, v, ws, wblk0, wblk0 + wnblk, tail_key, tail_page, [&](int q, int e, int page) {
     if (lane == 0) {
       s_wpage[wave][q - wblk0] = page;
       s_wsel[wave][q - wblk0] = e;
     }
   });
   wave_lds_order();  // this wave's pages
-  const int pmax = a.num_subpages / kSubsPerPage - 1;
-  const int ctx_row = ctx;
-  ctx = min(ctx, a.max_ctx);
-  if (ctx > 0 && split * a.split_tok < ctx)
-    attend_split<KV_FP8, SCALE_MODE>(a, ml, n, hgi, split, ctx, qb, [&](int sp) {
-      return 8 * clampi(s_wpage[wave][(sp >> 3) - wblk0], 0, pmax) + (sp & 7);
-    });
-  else if (ctx == 0 && split == 0)
-    write_zero_row(a, n, hgi);
-
-  // The selection's outputs, written once the attention's loads are out so
-  // that no wait for these stores holds them back. Rank q is written by the
-  // wave whose sub-pages start its block, in head group 0 (every rank lies in
-  // a split that attends, since 128*q < ctx).
-  if (hgi == 0 && (sp_begin & 7) == 0) {
-    int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
-    const int nq = min(wblk0 + wnblk, ws.kk) - wblk0;
-    for (int idx = lane; idx < 8 * nq; idx += 64) trow[8 * wblk0 + idx] = 8 * s_wpage[wave][idx >> 3] + (idx & 7);
-    if (a.sel_out)
-      for (int m = lane; m < nq; m += 64) a.sel_out[static_cast<size_t>(n) * a.topk + wblk0 + m] = s_wsel[wave][m];
-  }
-  if (split == 0 && hgi == 0 && wave == 0) {  // context length and the zero tail past K'
-    int32_t* trow = a.table_out + static_cast<size_t>(n) * (8 * a.topk);
-    for (int m = 8 * ws.kk + lane; m < 8 * a.topk; m += 64) trow[m] = 0;
-    if (a.sel_out)
-      for (int m = ws.kk + lane; m < a.topk; m += 64) a.sel_out[static_cast<size_t>(n) * a.topk + m] = -1;
-    if (lane == 0) a.ctx_out[n] = ctx_row;
-  }
+  attend_selected<KV_FP8, SCALE_MODE>(a, ml, s_wpage[wave], s_wsel[wave], n, hgi, split, sp_begin, wblk0, wnblk,
+                                      ws.kk, ctx, qb);
 }
 
 // Combines the split partials of rows that needed more than one split. One
@@ -497,8 +555,14 @@ hipError_t launch(const MsaAttnArgs& a, hipStream_t s) {
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups * a.nsplit;
   if (a.scores) {
     const int nbmax = min(min(a.ld_s, a.ld_bt), kMaxBlocksPerRow);
+    // short rows: each wave selects alone (4 keys per lane, no barrier);
+    // up to 1024 blocks the four waves share the work; longer rows again
+    // wave by wave with 16 keys per lane and the rest re-read from memory
     if (nbmax <= 256)
       hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE, 4>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kAttnThreads), 0, s, a);
+    else if (nbmax <= 1024)
+      hipLaunchKernelGGL((msa_attn_coop_kernel<KV_FP8, SCALE_MODE, 4>), dim3(static_cast<unsigned>(grid)),
                          dim3(kAttnThreads), 0, s, a);
     else
       hipLaunchKernelGGL((msa_attn_select_kernel<KV_FP8, SCALE_MODE, 16>), dim3(static_cast<unsigned>(grid)),

@@ -320,4 +320,175 @@ __device__ __forceinline__ int wave_locate(const WaveKeys<KR>& wk, const int (&p
   return kPage * w.kk - (last_kept ? kPage * nb - v : 0);
 }
 
+// ---------------------------------------------------------------------------
+// The same selection with the four waves of a workgroup sharing the work:
+// thread t holds the keys of blocks t + 256*i, i < KC (a row of at most
+// 256*KC blocks), the radix histogram is shared, and every wave reads the
+// same histogram after one barrier per pass, so all waves reach the same
+// threshold. The keep ballots of 64-block chunks (chunk c = 4*i + wave) go to
+// LDS, and each wave then looks up the ranks it needs.
+// ---------------------------------------------------------------------------
+constexpr int kCoopMaxChunks = 16;  // 1024 blocks
+
+struct CoopLds {
+  int hist[kWaveRadixPasses][256];  // cleared before the selection
+  uint32_t ext[4][2];               // per-wave max / min key
+  int eqc[kCoopMaxChunks];          // keys equal to the threshold, per chunk
+  int cnt[kCoopMaxChunks];          // kept blocks per chunk
+  unsigned long long mask[kCoopMaxChunks];
+  int page[kCoopMaxChunks * 64];    // block-table entry of every kept block
+};
+
+// Clears the histograms (all 256 threads; the first barrier of coop_select
+// orders it before any use).
+__device__ __forceinline__ void coop_clear(CoopLds& L) {
+  i32x4* h = reinterpret_cast<i32x4*>(&L.hist[0][0]);
+  h[threadIdx.x] = i32x4{0, 0, 0, 0};
+}
+
+// Every thread of the workgroup calls it; the result is uniform.
+template <int KC>
+__device__ __forceinline__ WaveSelection coop_select(const uint32_t (&k)[KC], int nb, int topk, CoopLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  WaveSelection w;
+  w.kk = min(topk, nb);
+  w.partial = w.kk < nb;
+  w.T = 0;
+  w.need = 0;
+  w.all_eq_kept = true;
+  if (!w.partial) return w;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < KC; ++i)
+    if (tid + 256 * i < nb) {
+      kmax = max(kmax, k[i]);
+      kmin = min(kmin, k[i]);
+    }
+  kmax = wave_extreme_u32<true>(kmax);
+  kmin = wave_extreme_u32<false>(kmin);
+  if (lane == 0) {
+    L.ext[wave][0] = kmax;
+    L.ext[wave][1] = kmin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    kmax = max(kmax, L.ext[x][0]);
+    kmin = min(kmin, L.ext[x][1]);
+  }
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0u) {  // every key is equal: the lowest K' ids
+    w.T = kmax;
+    w.need = w.kk;
+    w.all_eq_kept = false;
+    return w;
+  }
+  int top = 31 - __clz(diff);
+  uint32_t prefix = (top == 31) ? 0u : (kmax & (~0u << (top + 1)));
+  int need = w.kk;
+#pragma unroll 1
+  for (int pass = 0; pass < kWaveRadixPasses; ++pass) {
+    const int width = min(8, top + 1);
+    const int shift = top + 1 - width;
+    const uint32_t fixed = (top == 31) ? 0u : (~0u << (top + 1));
+    const uint32_t dmask = (1u << width) - 1u;
+    int* h = L.hist[pass];
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+      if (tid + 256 * i < nb && (k[i] & fixed) == prefix) atomicAdd(&h[(k[i] >> shift) & dmask], 1);
+    __syncthreads();
+    // lane owns digits 255-4*lane .. 252-4*lane (descending); every wave
+    // scans the same counts
+    const i32x4 h4 = *reinterpret_cast<const i32x4*>(&h[252 - 4 * lane]);
+    const int c[4] = {h4[3], h4[2], h4[1], h4[0]};
+    const int local = c[0] + c[1] + c[2] + c[3];
+    const int incl = wave_inclusive_scan(local);
+    int run = incl - local, my_digit = 0, my_need = 0, my_cnt = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (run < need && need <= run + c[i]) {
+        found = true;
+        my_digit = 255 - 4 * lane - i;
+        my_need = need - run;
+        my_cnt = c[i];
+      }
+      run += c[i];
+    }
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(__ballot(found))) - 1);
+    prefix |= static_cast<uint32_t>(__builtin_amdgcn_readlane(my_digit, src)) << shift;
+    need = __builtin_amdgcn_readlane(my_need, src);
+    const int cnt = __builtin_amdgcn_readlane(my_cnt, src);
+    if (need == cnt) {
+      w.T = prefix;
+      w.all_eq_kept = true;
+      return w;
+    }
+    if (shift == 0) break;
+    top = shift - 1;
+  }
+  w.T = prefix;
+  w.need = need;
+  w.all_eq_kept = false;
+  return w;
+}
+
+// Keep ballots to LDS, then found(rank, block, page) for the ranks
+// [q0, q1) this wave needs (uniform arguments). Every thread calls it.
+// Returns the context length 128*K' - (block nb-1 kept ? 128*nb - v : 0).
+template <int KC, typename Found>
+__device__ __forceinline__ int coop_locate(const uint32_t (&k)[KC], const int (&pg)[KC], int nb, int v,
+                                           const WaveSelection& w, int q0, int q1, CoopLds& L, Found found) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  bool keep[KC];
+  if (!w.partial || w.all_eq_kept) {
+#pragma unroll
+    for (int i = 0; i < KC; ++i) keep[i] = tid + 256 * i < nb && (!w.partial || k[i] >= w.T);
+  } else {
+    // ties straddle the cut: equal keys are kept in ascending block order
+    unsigned long long em[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      em[i] = __ballot(tid + 256 * i < nb && k[i] == w.T);
+      if (lane == 0) L.eqc[4 * i + wave] = __popcll(em[i]);
+    }
+    __syncthreads();
+    const int ev = lane < 4 * KC ? L.eqc[lane] : 0;
+    const int eincl = wave_inclusive_scan(ev);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int before = __builtin_amdgcn_readlane(eincl - ev, 4 * i + wave);
+      const bool eq = (em[i] >> lane) & 1ull;
+      keep[i] = tid + 256 * i < nb && (k[i] > w.T || (eq && before + __popcll(em[i] & lt) < w.need));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const unsigned long long km = __ballot(keep[i]);
+    if (lane == 0) {
+      L.mask[4 * i + wave] = km;
+      L.cnt[4 * i + wave] = __popcll(km);
+    }
+    if (keep[i]) L.page[tid + 256 * i] = pg[i];
+  }
+  __syncthreads();
+  const int nchunks = (nb + 63) >> 6;
+  const int cv = lane < nchunks ? L.cnt[lane] : 0;
+  const int cincl = wave_inclusive_scan(cv);
+  q1 = min(q1, w.kk);
+  for (int q = q0; q < q1; ++q) {
+    const int c = __popcll(__ballot(lane < nchunks && cincl <= q));
+    const int excl = __builtin_amdgcn_readlane(cincl - cv, c);
+    const unsigned long long m = L.mask[c];
+    const unsigned long long hit = __ballot(((m >> lane) & 1ull) && __popcll(m & lt) == q - excl);
+    const int e = 64 * c + __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(hit)) - 1);
+    found(q, e, L.page[e]);
+  }
+  const bool last_kept = nb > 0 && ((L.mask[(nb - 1) >> 6] >> ((nb - 1) & 63)) & 1ull);
+  return kPage * w.kk - (last_kept ? kPage * nb - v : 0);
+}
+
 }  // namespace msa
