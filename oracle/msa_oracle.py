@@ -14,7 +14,7 @@ Section names are the pages' own: 功能与动机 (motivation), 实现拆解 (im
 breakdown, numbered items), 关键源码片段 (key source excerpt), 评论区精华 (review
 highlights), 风险与影响 (risks).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * index score = raw dot product of the row's index query with each token's
     index key, one index head, no scale;
   * pooling over a 128-token block = max over the block's visible tokens;
@@ -399,3 +399,85 @@ def attention_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows) -> np.
             out[i, g * group:(g + 1) * group] = softmax_attention(
                 q[g * group:(g + 1) * group], kh, vh, batch.sm_scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# The step before the path: new tokens written into the paged caches
+# ([P1] 实现拆解 items 1, 2 and 5: the fused K/V insert writes the separate K
+# and V planes and, unless the layer reuses another layer's index, the index
+# cache; FP8 caches carry per-token-head or scalar K/V scales)
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0   # largest finite e4m3fn magnitude
+
+
+def tile_store(tile: np.ndarray, tok: int, row: np.ndarray) -> None:
+    """Inverse of tile_row: element d of the token goes to [d//32][(d//8)%4][tok][d%8]."""
+    tile[:, :, tok, :] = np.asarray(row).reshape(4, 4, 8)
+
+
+def _f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _f32_to_e4m3fn_codes(x32: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy().copy()
+
+
+def quantize_row(x_bits: np.ndarray, kv_dtype: int, scale_mode: int, scalar_scale: float | None):
+    """Stored values and scale of one token-head row of 128 bf16 inputs, in
+    fp32 (each code is decided in fp32, as the device decides it):
+      per-token-head scale: s = fp32(max |x|) / 448, or 1 for an all-zero row
+        (bf16 storage keeps s = 1);
+      scalar scale: s = the given fp32 scale; no scale: s = 1;
+      fp8: code = e4m3fn RNE of clamp(fp32(x) / s, -448, 448);
+      bf16: stored = bf16 RNE of fp32(x) / s.
+    So that s x stored reproduces x up to the storage format's rounding."""
+    x = bf16_to_f64(np.asarray(x_bits)).astype(np.float32)
+    if scale_mode == 2 and kv_dtype == 1:
+        amax = np.float32(np.max(np.abs(x)))
+        s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    elif scale_mode == 1:
+        s = np.float32(scalar_scale)
+    else:
+        s = np.float32(1.0)
+    y = (x / s).astype(np.float32)
+    if kv_dtype == 1:
+        y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+        return _f32_to_e4m3fn_codes(y), float(s)
+    return _f32_to_bf16_bits(y), float(s)
+
+
+def cache_insert(k_cache, v_cache, k_scale, v_scale, index_k, slot_mapping, k_new, v_new,
+                 index_k_new, kv_dtype: int, scale_mode: int):
+    """Writes token t of k_new / v_new ([T][Hkv][128] bf16) and index_k_new
+    ([T][128] bf16, or None to leave the index cache alone) at slot
+    slot_mapping[t] = 128 * page + offset (negative: skipped). Returns updated
+    copies (k_cache, v_cache, k_scale, v_scale, index_k). Per-token-head scales
+    are written for every inserted token-head; a scalar scale is only read."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    ks = None if k_scale is None else np.array(k_scale, dtype=np.float32, copy=True)
+    vs = None if v_scale is None else np.array(v_scale, dtype=np.float32, copy=True)
+    ik = None if index_k is None else np.array(index_k, copy=True)
+    hkv_n = kc.shape[1]
+    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        page, off = divmod(int(slot), PAGE)
+        sub, j = SUBS_PER_PAGE * page + off // SUB, off % SUB
+        for h in range(hkv_n):
+            for plane, cache, scales, new in (("k", kc, ks, k_new), ("v", vc, vs, v_new)):
+                scalar = None if scales is None or scale_mode != 1 else float(scales.reshape(-1)[0])
+                stored, s = quantize_row(np.asarray(new)[t, h], kv_dtype, scale_mode, scalar)
+                if plane == "k":
+                    tile_store(cache[sub, h], j, stored)
+                else:
+                    cache[sub, h, :, j] = stored
+                if scale_mode == 2:
+                    scales.reshape(-1, SUB, hkv_n)[sub, j, h] = np.float32(s)
+        if index_k_new is not None and ik is not None:
+            tile_store(ik[page, off // SUB], j, np.asarray(index_k_new)[t])
+    return kc, vc, ks, vs, ik

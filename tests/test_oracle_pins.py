@@ -508,3 +508,130 @@ def test_decode_step_chain_on_tiny_workload():
     others = [x for x in range(16) if x not in sel]
     assert s[sel].min() >= s[others].max()
     assert res["table"][0].tolist() == [8 * int(blk) + i for blk in sel for i in range(8)]
+
+
+# ---------------------------------------------------------------------------
+# cache insert (new tokens into the paged caches, FP8 quantisation)
+# ---------------------------------------------------------------------------
+def _insert_case(seed, T, num_pages, kv_fp8, scale_mode, with_index=True):
+    rng = np.random.default_rng(seed)
+    k_new = bf16_bits(rng.standard_normal((T, 1, 128)) * rng.uniform(0.1, 4.0, (T, 1, 1)))
+    v_new = bf16_bits(rng.standard_normal((T, 1, 128)) * rng.uniform(0.1, 4.0, (T, 1, 1)))
+    ik_new = bf16_bits(rng.standard_normal((T, 128)))
+    slots = rng.choice(num_pages * 128, size=T, replace=False).astype(np.int32)
+    slots[rng.uniform(size=T) < 0.15] = -1
+    dt = np.uint8 if kv_fp8 else np.uint16
+    kc = rng.integers(0, 256 if kv_fp8 else 65536, (num_pages * 8, 1, 4, 4, 16, 8)).astype(dt)
+    vc = rng.integers(0, 256 if kv_fp8 else 65536, (num_pages * 8, 1, 128, 16)).astype(dt)
+    ik = rng.integers(0, 65536, (num_pages, 8, 4, 4, 16, 8)).astype(np.uint16)
+    if scale_mode == 2:
+        ks = rng.uniform(0.5, 2.0, (num_pages * 8, 16, 1)).astype(np.float32)
+        vs = rng.uniform(0.5, 2.0, (num_pages * 8, 16, 1)).astype(np.float32)
+    elif scale_mode == 1:
+        ks, vs = np.array([0.75], np.float32), np.array([1.25], np.float32)
+    else:
+        ks = vs = None
+    return dict(k_new=k_new, v_new=v_new, ik_new=ik_new if with_index else None, slots=slots,
+                kc=kc, vc=vc, ik=ik, ks=ks, vs=vs, kv_dtype=1 if kv_fp8 else 0, scale_mode=scale_mode)
+
+
+def _run_insert(c):
+    return O.cache_insert(c["kc"], c["vc"], c["ks"], c["vs"], c["ik"], c["slots"], c["k_new"], c["v_new"],
+                          c["ik_new"], c["kv_dtype"], c["scale_mode"])
+
+
+def test_insert_bf16_is_an_exact_scatter_into_the_documented_layouts():
+    """bf16 caches with no scale: the insert is a copy; checked against this
+    file's own scatter (shuffle_into / dim-major V / index tiles)."""
+    c = _insert_case(31, 40, 6, kv_fp8=False, scale_mode=0)
+    kc, vc, _, _, ik = _run_insert(c)
+    ek, ev, eik = c["kc"].copy(), c["vc"].copy(), c["ik"].copy()
+    for t, slot in enumerate(c["slots"]):
+        if slot < 0:
+            continue
+        page, off = divmod(int(slot), 128)
+        sub, j = page * 8 + off // 16, off % 16
+        shuffle_into(ek[sub, 0], j, c["k_new"][t, 0])
+        ev[sub, 0, :, j] = c["v_new"][t, 0]
+        shuffle_into(eik[page, off // 16], j, c["ik_new"][t])
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev) and np.array_equal(ik, eik)
+
+
+def test_insert_leaves_skipped_slots_and_the_index_cache_alone():
+    c = _insert_case(32, 30, 4, kv_fp8=True, scale_mode=2, with_index=False)
+    c["slots"][:] = -1
+    kc, vc, ks, vs, ik = _run_insert(c)
+    assert np.array_equal(kc, c["kc"]) and np.array_equal(vc, c["vc"])
+    assert np.array_equal(ks, c["ks"]) and np.array_equal(ik, c["ik"])
+    c = _insert_case(33, 30, 4, kv_fp8=True, scale_mode=2, with_index=False)
+    _, _, _, _, ik = _run_insert(c)
+    assert np.array_equal(ik, c["ik"]), "no index rows given: the index cache is untouched"
+
+
+def test_insert_fp8_per_token_head_scale_is_amax_over_448_and_roundtrips():
+    """The largest |x| of each token-head lands exactly on code +-448 (0x7E /
+    0xFE); every value comes back within half an e4m3 step (relative 2^-4,
+    absolute s*2^-10 in the subnormal range)."""
+    c = _insert_case(34, 48, 6, kv_fp8=True, scale_mode=2)
+    kc, vc, ks, vs, _ = _run_insert(c)
+    bt = np.arange(6)
+    for t, slot in enumerate(c["slots"]):
+        if slot < 0:
+            continue
+        for plane, cache, sc, new in (("k", kc, ks, c["k_new"]), ("v", vc, vs, c["v_new"])):
+            x = O.bf16_to_f64(new[t, 0])
+            s = O.token_scale(sc, 2, bt, int(slot), 0)
+            assert s == float(np.float32(np.float32(np.abs(x).max()) / np.float32(448.0)))
+            stored = O.kv_token(cache, bt, int(slot), 0, 1, plane)
+            assert np.abs(stored).max() == 448.0
+            assert stored[np.argmax(np.abs(x))] == np.sign(x[np.argmax(np.abs(x))]) * 448.0
+            err = np.abs(s * stored - x)
+            assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6))
+
+
+def test_insert_fp8_exact_on_representable_values_and_zero_rows():
+    """x = s * (e4m3 value) with the row's max at 448: codes are exact, the
+    dequantised row equals x; an all-zero row stores zeros with scale 1."""
+    rng = np.random.default_rng(35)
+    codes = rng.integers(0, 0x7F, 128).astype(np.uint8)          # finite, positive
+    codes[5] = 0x7E                                                 # 448
+    codes[rng.uniform(size=128) < 0.5] |= 0x80                      # signs
+    vals = O.e4m3fn_to_f64(codes)
+    s = 0.25                                                        # power of two: x exact in bf16
+    x_bits = bf16_bits(vals * s)
+    stored, scale = O.quantize_row(x_bits, 1, 2, None)
+    assert scale == s and np.array_equal(O.e4m3fn_to_f64(stored), vals)
+    stored, scale = O.quantize_row(np.zeros(128, np.uint16), 1, 2, None)
+    assert scale == 1.0 and not stored.any()
+
+
+def test_insert_scalar_scale_divides_and_clamps():
+    x = np.array([1.0, -3.0, 0.5, 1000.0, -1000.0] + [0.0] * 123)
+    stored, s = O.quantize_row(bf16_bits(x), 1, 1, 0.5)
+    back = O.e4m3fn_to_f64(stored)
+    assert s == 0.5 and back[:5].tolist() == [2.0, -6.0, 1.0, 448.0, -448.0]
+    stored, s = O.quantize_row(bf16_bits(x), 0, 1, 0.5)            # bf16 storage: x / s
+    assert O.bf16_to_f64(stored)[:5].tolist() == [2.0, -6.0, 1.0, 2000.0, -2000.0]
+
+
+def test_insert_then_decode_equals_decode_on_the_written_cache():
+    """Writing a request's last token through the insert and then running the
+    decode step gives the same output as a cache built with that token in
+    place by this file's own scatter (bf16, no scale)."""
+    b = syn.make_batch("ins", 36, [700, 300], [1, 1], topk=4, num_q_heads=8)
+    last = [int(L) - 1 for L in b.seq_lens]
+    slots = np.array([int(b.block_table[r, t // 128]) * 128 + t % 128 for r, t in enumerate(last)], np.int32)
+    k_new = np.stack([O.tile_row(b.k_cache[int(s) // 128 * 8 + (int(s) % 128) // 16, 0], int(s) % 16)
+                      for s in slots])[:, None, :]
+    v_new = np.stack([b.v_cache[int(s) // 128 * 8 + (int(s) % 128) // 16, 0, :, int(s) % 16]
+                      for s in slots])[:, None, :]
+    ref = O.decode_step(b)["out"]
+    # wipe the two tokens, then insert them back
+    kc, vc = b.k_cache.copy(), b.v_cache.copy()
+    for s in slots:
+        sub, j = int(s) // 128 * 8 + (int(s) % 128) // 16, int(s) % 16
+        kc[sub, 0, :, :, j, :] = 0
+        vc[sub, 0, :, j] = 0
+    kc, vc, _, _, _ = O.cache_insert(kc, vc, None, None, None, slots, k_new, v_new, None, 0, 0)
+    b2 = syn.Batch(**{**b.__dict__, "k_cache": kc, "v_cache": vc})
+    assert np.array_equal(O.decode_step(b2)["out"], ref)
