@@ -95,6 +95,62 @@ def cpu_baseline(b, rows, budget_s=10.0):
                       f"full step (metadata, scores, pooling, selection, table, attention), {dt:.1f} s"}
 
 
+def time_insert(msa, torch, tokens=8192, copies=32, reps=32):
+    """msa_cache_insert of a prefill chunk (two sequences of 4096 new tokens, the
+    mixed workload's prefill shape) into fp8 e4m3fn caches with per-token-head
+    scales, index-K included: per-launch time over back-to-back launches in one
+    graph, cycling `copies` sets of inputs and caches (>= 256 MB in all, so no
+    launch finds its data in the Infinity Cache). Algorithmic bytes per token:
+    K, V and index-K rows read (3 x 256 B) + the slot (4 B); fp8 K and V (2 x 128
+    B), their scales (2 x 4 B) and the index-K row (256 B) written."""
+    dev = "cuda"
+    pages = tokens // 128
+    g = torch.Generator(device="cpu").manual_seed(11)
+    sets = []
+    for c in range(copies):
+        k_new = (torch.randn((tokens, 1, 128), generator=g) * 2).to(torch.bfloat16).to(dev)
+        v_new = (torch.randn((tokens, 1, 128), generator=g) * 2).to(torch.bfloat16).to(dev)
+        i_new = torch.randn((tokens, 128), generator=g).to(torch.bfloat16).to(dev)
+        perm = torch.randperm(pages, generator=g)
+        t = torch.arange(tokens)
+        slots = (perm[t // 128] * 128 + t % 128).to(torch.int32).to(dev)
+        kc = torch.zeros((pages * 8, 1, 2048), dtype=torch.uint8, device=dev)
+        vc = torch.zeros((pages * 8, 1, 2048), dtype=torch.uint8, device=dev)
+        ks = torch.ones((pages * 8, 16, 1), dtype=torch.float32, device=dev)
+        vs = torch.ones((pages * 8, 16, 1), dtype=torch.float32, device=dev)
+        ik = torch.zeros((pages, 128 * 128), dtype=torch.int16, device=dev)
+        kv = msa.make_kv(kc, vc, 1, 2, pages, ks, vs)
+        sets.append((slots, k_new, v_new, i_new, ik, kv, kc, vc, ks, vs))
+    stream = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        for st in sets:
+            msa.msa_cache_insert(tokens, st[0], st[1], st[2], st[5], st[3], st[4])
+        with torch.cuda.graph(graph, stream=gs):
+            for i in range(reps):
+                st = sets[i % copies]
+                msa.msa_cache_insert(tokens, st[0], st[1], st[2], st[5], st[3], st[4])
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    runs = []
+    for _ in range(5):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) * 1e3 / reps)
+    us = sorted(runs)[len(runs) // 2]
+    nbytes = tokens * (3 * 256 + 4 + 2 * 128 + 2 * 4 + 256)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "msa_insert_kernel (msa_cache_insert)", "tokens": tokens,
+            "kv": "fp8 e4m3fn, per-token-head scales, index-K written", "us_per_launch": us,
+            "tokens_per_s": tokens / (us * 1e-6), "algorithmic_bytes": nbytes, "achieved": gbps,
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,6 +343,7 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},
     }
+    res["cache_insert"] = time_insert(msa, torch)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, list(range(min(N, 8))))

@@ -28,7 +28,7 @@ MSA_SCALE_PER_TOKEN_HEAD = 2
 
 EXPORTS = (
     "msa_build_metadata", "msa_index_score", "msa_topk_block_table", "msa_sparse_paged_attn",
-    "msa_sparse_decode", "msa_workspace_bytes", "msa_status_string", "msa_version",
+    "msa_sparse_decode", "msa_cache_insert", "msa_workspace_bytes", "msa_status_string", "msa_version",
 )
 
 
@@ -77,6 +77,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "msa_topk_block_table": ([vp, bp, vp, i32, i32, vp, vp, vp], i32),
         "msa_sparse_paged_attn": ([vp, vp, i32, i32, kp, vp, i32, vp, i32, f32, vp, vp, sz], i32),
         "msa_sparse_decode": ([vp, bp, vp, vp, vp, i32, kp, i32, f32, vp, vp, vp, vp, vp, i32, vp, sz], i32),
+        "msa_cache_insert": ([vp, i32, vp, vp, vp, kp, vp, vp], i32),
         "msa_workspace_bytes": ([i32, i32, i32, i32], sz),
         "msa_status_string": ([i32], ctypes.c_char_p),
         "msa_version": ([], i32),
@@ -160,6 +161,13 @@ def msa_sparse_decode(batch: MsaBatch, index_q, index_k, q, num_q_heads: int, kv
         _stream(stream), ctypes.byref(batch), _ptr(index_q), _ptr(index_k), _ptr(q), num_q_heads,
         ctypes.byref(kv), topk, sm_scale, _ptr(out), _ptr(sparse_table), _ptr(ctx_lens), _ptr(sel_blocks),
         _ptr(block_scores), ld_s, _ptr(workspace), workspace_bytes))
+
+
+def msa_cache_insert(num_tokens: int, slot_mapping, k_new, v_new, kv: MsaKV, index_k_new, index_k,
+                     stream=None) -> None:
+    _check("msa_cache_insert", load().msa_cache_insert(
+        _stream(stream), num_tokens, _ptr(slot_mapping), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
+        _ptr(index_k_new), _ptr(index_k)))
 
 
 def msa_workspace_bytes(num_rows: int, num_q_heads: int, max_ctx: int, ld_s: int) -> int:

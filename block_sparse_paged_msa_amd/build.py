@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.hip", "msa_meta.hip", "msa_score.hip", "msa_topk.hip", "msa_attn.hip"]
+SOURCES = ["msa_api.hip", "msa_meta.hip", "msa_score.hip", "msa_topk.hip", "msa_attn.hip", "msa_insert.hip"]
 ARCH = "gfx950"
 
 

@@ -302,6 +302,35 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
   return launch_attn_and_merge(s, a, kv);
 }
 
+msa_status msa_cache_insert(msa_stream_t stream, int32_t num_tokens, const int32_t* slot_mapping, const void* k_new,
+                            const void* v_new, const msa_kv* kv, const void* index_k_new, void* index_k) {
+  msa_status st = check_kv(kv);
+  if (st != MSA_OK) return st;
+  if (num_tokens < 0) return MSA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MSA_OK;
+  if (!slot_mapping || !k_new || !v_new) return MSA_ERR_INVALID_ARG;
+  if (index_k_new && !index_k) return MSA_ERR_INVALID_ARG;
+  MsaInsertArgs a;
+  a.slot_mapping = slot_mapping;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.index_k_new = static_cast<const uint16_t*>(index_k_new);
+  // the caches (and per-token-head scales) are the call's outputs
+  a.k_cache = const_cast<void*>(kv->k_cache);
+  a.v_cache = const_cast<void*>(kv->v_cache);
+  a.index_k = static_cast<uint16_t*>(index_k);
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
+  a.k_scale_out = const_cast<float*>(kv->k_scale);
+  a.v_scale_out = const_cast<float*>(kv->v_scale);
+  a.num_tokens = num_tokens;
+  a.num_pages = kv->num_pages;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.kv_fp8 = kv->kv_dtype == MSA_KV_FP8_E4M3FN ? 1 : 0;
+  a.scale_mode = kv->scale_mode;
+  return hip_status(msa_launch_insert(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ctx, int32_t ld_s) {
   if (num_rows < 0 || num_q_heads < 1 || max_ctx < 0 || ld_s < 0) return 0;
   return ws_layout(num_rows, num_q_heads, max_ctx, ld_s).total;

@@ -1,0 +1,201 @@
+// The step before the path: new tokens written into the paged caches (vLLM PR
+// #47287 page, 实现拆解 items 1, 2 and 5: the fused K/V insert writes the
+// separate K and V planes and, unless the layer reuses another layer's index,
+// the index cache; FP8 caches carry per-token-head or scalar K/V scales).
+//
+// One wave per new token. Lanes 0..15 take the K row and lanes 16..31 the
+// index-K row, eight dims each (one 16-byte load per lane), and write them
+// into their shuffled tiles as one contiguous 8-element run per lane. V is
+// dim-major ([128 dims][16 token slots] per sub-page), so all 64 lanes take
+// it, two dims each, and every store instruction fills one token slot of 64
+// dim rows.
+//
+// Quantisation (each code decided in fp32): per-token-head scale
+// s = max|x| / 448 over the token-head's 128 values (1 for an all-zero row),
+// code = e4m3fn RNE of clamp(x / s, -448, 448); a scalar scale is read, not
+// written; bf16 caches store bf16 RNE of x / s with s = 1 unless scalar.
+#include "msa_internal.h"
+
+using namespace msa;
+
+namespace {
+
+constexpr int kInsertThreads = 256;
+constexpr float kE4m3Max = 448.f;
+
+struct alignas(16) f32x8 {
+  float v[8];
+};
+
+__device__ __forceinline__ f32x8 widen(u32x4 w) {
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.v[2 * i] = __uint_as_float(w[i] << 16);
+    r.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  return r;
+}
+
+// Scale of one token-head row given its largest magnitude.
+__device__ __forceinline__ float row_scale(const MsaInsertArgs& a, int plane, float amax) {
+  if (a.scale_mode == 1) return plane == 0 ? a.k_scale[0] : a.v_scale[0];
+  if (a.scale_mode == 2 && a.kv_fp8) return amax > 0.f ? amax / kE4m3Max : 1.f;
+  return 1.f;
+}
+
+__device__ __forceinline__ uint32_t fp8_code(float x, float s) {
+  const float y = fminf(fmaxf(x / s, -kE4m3Max), kE4m3Max);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false)) & 0xffu;
+}
+
+// One token with one wave (decode: scattered slots).
+__device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int t, int lane) {
+  const int c = lane & 15;
+  // every load of the token is issued before its slot is known (one round
+  // trip): lanes 0..15 the K row, lanes 16..31 the index-K row (8 dims
+  // each), all lanes two dims of the V row; one KV head (the caller checks)
+  const size_t row = static_cast<size_t>(t) * a.num_kv_heads;
+  u32x4 kw = {0u, 0u, 0u, 0u}, iw = {0u, 0u, 0u, 0u};
+  if (lane < 16) kw = *reinterpret_cast<const u32x4*>(a.k_new + row * kDim + 8 * c);
+  if ((lane >> 4) == 1 && a.index_k_new) iw = *reinterpret_cast<const u32x4*>(a.index_k_new + static_cast<size_t>(t) * kDim + 8 * c);
+  const uint16_t* vsrc = a.v_new + row * kDim;
+  const uint32_t vb0 = vsrc[lane], vb1 = vsrc[lane + 64];
+  const int slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= kPage * a.num_pages) return;  // skipped (or outside the caches)
+  const int page = slot >> 7, off = slot & (kPage - 1);
+  const int sub = kSubsPerPage * page + (off >> 4), j = off & (kSub - 1);
+  const size_t sp = static_cast<size_t>(sub) * a.num_kv_heads;  // the head's sub-page
+
+  // index-K: a bf16 copy into the page's shuffled tile
+  if ((lane >> 4) == 1 && a.index_k_new) {
+    uint16_t* dst = a.index_k + static_cast<size_t>(page) * (kPage * kDim) + (off >> 4) * (kSub * kDim) + (c * 16 + j) * 8;
+    *reinterpret_cast<u32x4*>(dst) = iw;
+  }
+  // K (lanes 0..15, dims 8c..8c+7): one contiguous run of the shuffled tile
+  {
+    const f32x8 x = widen(kw);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x.v[i]));
+    const float s = row_scale(a, 0, max16(amax));  // lanes 0..15 hold the whole row
+    if (lane < 16) {
+      if (a.kv_fp8) {
+        uint32_t code[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e >> 2] |= fp8_code(x.v[e], s) << (8 * (e & 3));
+        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.k_cache) + sp * (kSub * kDim) + (c * 16 + j) * 8) =
+            u32x2{code[0], code[1]};
+      } else {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = f32_to_bf16(x.v[2 * i] / s) | (static_cast<uint32_t>(f32_to_bf16(x.v[2 * i + 1] / s)) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k_cache) + sp * (kSub * kDim) + (c * 16 + j) * 8) = w;
+      }
+    }
+    if (a.scale_mode == 2 && lane == 0) a.k_scale_out[(static_cast<size_t>(sub) * kSub + j) * a.num_kv_heads] = s;
+  }
+  // V (all lanes, dims lane and lane+64): the cache is dim-major, so each
+  // store instruction writes one token slot of 64 dim rows
+  {
+    const float x0 = __uint_as_float(vb0 << 16), x1 = __uint_as_float(vb1 << 16);
+    const float s = row_scale(a, 1, max_across_rows(max16(fmaxf(fabsf(x0), fabsf(x1)))));
+    const size_t base = sp * (kSub * kDim) + j;
+    if (a.kv_fp8) {
+      uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
+      vc[base + lane * kSub] = static_cast<uint8_t>(fp8_code(x0, s));
+      vc[base + (lane + 64) * kSub] = static_cast<uint8_t>(fp8_code(x1, s));
+    } else {
+      uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
+      vc[base + lane * kSub] = f32_to_bf16(x0 / s);
+      vc[base + (lane + 64) * kSub] = f32_to_bf16(x1 / s);
+    }
+    if (a.scale_mode == 2 && lane == 0) a.v_scale_out[(static_cast<size_t>(sub) * kSub + j) * a.num_kv_heads] = s;
+  }
+}
+
+// Sixteen tokens that fill one sub-page in order (a prefill chunk): the
+// workgroup quantises them, lays the K / index-K tiles and the dim-major V
+// sub-page out in LDS, and writes each as one contiguous run. Thread i takes
+// token i/16 and dims 8*(i%16).. of it, so the 16 lanes of a DPP row hold one
+// token's whole row for the scale.
+__device__ __forceinline__ void insert_subpage(const MsaInsertArgs& a, int t0, int slot0, uint8_t* lds) {
+  const int tid = threadIdx.x, j = tid >> 4, c = tid & 15;
+  const int t = t0 + j;
+  const int page = slot0 >> 7, sub = kSubsPerPage * page + ((slot0 & (kPage - 1)) >> 4);
+  const int nbytes = a.kv_fp8 ? 1 : 2;
+  const int kv_bytes = kSub * kDim * nbytes;  // one plane of one sub-page
+  uint8_t* ks = lds;                 // K tile
+  uint8_t* vs = lds + kv_bytes;      // V sub-page
+  uint16_t* is = reinterpret_cast<uint16_t*>(lds + 2 * kv_bytes);  // index-K tile
+  const u32x4 kw = *reinterpret_cast<const u32x4*>(a.k_new + static_cast<size_t>(t) * kDim + 8 * c);
+  const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v_new + static_cast<size_t>(t) * kDim + 8 * c);
+  u32x4 iw = {0u, 0u, 0u, 0u};
+  if (a.index_k_new) iw = *reinterpret_cast<const u32x4*>(a.index_k_new + static_cast<size_t>(t) * kDim + 8 * c);
+#pragma unroll
+  for (int plane = 0; plane < 2; ++plane) {
+    const f32x8 x = widen(plane == 0 ? kw : vw);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x.v[e]));
+    const float s = row_scale(a, plane, max16(amax));
+    if (a.scale_mode == 2 && c == 0) (plane == 0 ? a.k_scale_out : a.v_scale_out)[static_cast<size_t>(sub) * kSub + j] = s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element (dim 8c+e, token j): tile slot (c*16 + j)*8 + e for K, dim row (8c+e)*16 + j for V
+      const int at = plane == 0 ? (c * 16 + j) * 8 + e : (8 * c + e) * kSub + j;
+      uint8_t* dst = plane == 0 ? ks : vs;
+      if (a.kv_fp8)
+        dst[at] = static_cast<uint8_t>(fp8_code(x.v[e], s));
+      else
+        reinterpret_cast<uint16_t*>(dst)[at] = f32_to_bf16(x.v[e] / s);
+    }
+  }
+  if (a.index_k_new) *reinterpret_cast<u32x4*>(is + (c * 16 + j) * 8) = iw;
+  __syncthreads();
+  // each plane of the sub-page as one contiguous run: 16 bytes per thread
+  const int per = kv_bytes / 16;  // 16-byte pieces per plane (128 or 256)
+  for (int i = tid; i < per; i += kInsertThreads) {
+    reinterpret_cast<u32x4*>(static_cast<uint8_t*>(a.k_cache) + static_cast<size_t>(sub) * kv_bytes)[i] =
+        reinterpret_cast<const u32x4*>(ks)[i];
+    reinterpret_cast<u32x4*>(static_cast<uint8_t*>(a.v_cache) + static_cast<size_t>(sub) * kv_bytes)[i] =
+        reinterpret_cast<const u32x4*>(vs)[i];
+  }
+  if (a.index_k_new)
+    reinterpret_cast<u32x4*>(a.index_k + static_cast<size_t>(page) * (kPage * kDim) +
+                             ((slot0 & (kPage - 1)) >> 4) * (kSub * kDim))[tid] = reinterpret_cast<const u32x4*>(is)[tid];
+}
+
+// Workgroup = 16 consecutive tokens. When their slots are one whole sub-page
+// in order (a prefill chunk), the sub-page path writes it in contiguous runs;
+// otherwise each wave inserts four of the tokens one by one.
+__global__ __launch_bounds__(kInsertThreads) void msa_insert_kernel(MsaInsertArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kSub * kDim * 2];
+  const int lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kSub;
+  const int lt = threadIdx.x & 15;
+  const int sl = t0 + lt < a.num_tokens ? a.slot_mapping[t0 + lt] : -1;
+  const int slot0 = __shfl(sl, 0, 16);
+  const bool whole = t0 + kSub <= a.num_tokens && slot0 >= 0 && (slot0 & (kSub - 1)) == 0 &&
+                     slot0 + kSub <= kPage * a.num_pages && a.num_kv_heads == 1;
+  // every lane compares its token's slot (all four waves see the same 16)
+  const bool in_order = __all(sl == slot0 + lt);
+  if (__builtin_amdgcn_readfirstlane(whole && in_order)) {
+    insert_subpage(a, t0, slot0, lds);
+    return;
+  }
+  const int wave = threadIdx.x >> 6;
+  for (int k = 0; k < 4; ++k) {
+    const int t = t0 + 4 * wave + k;
+    if (t < a.num_tokens) insert_token(a, t, lane);
+  }
+}
+
+}  // namespace
+
+hipError_t msa_launch_insert(const MsaInsertArgs& a, hipStream_t s) {
+  const int grid = (a.num_tokens + kSub - 1) / kSub;
+  hipLaunchKernelGGL(msa_insert_kernel, dim3(static_cast<unsigned>(grid)), dim3(kInsertThreads), 0, s, a);
+  return hipGetLastError();
+}

@@ -233,6 +233,27 @@ struct MsaAttnArgs {
   int32_t num_subpages;
   float scale_log2;    // sm_scale * log2(e)
 };
+// New tokens into the paged caches (K / V planes, scales, index-K).
+struct MsaInsertArgs {
+  const int32_t* slot_mapping;   // [T] 128*page + offset; < 0: skipped
+  const uint16_t* k_new;         // [T][Hkv][128] bf16
+  const uint16_t* v_new;
+  const uint16_t* index_k_new;   // [T][128] bf16, or null: the index cache is left alone
+  void* k_cache;
+  void* v_cache;
+  uint16_t* index_k;
+  const float* k_scale;          // scalar mode: [1], read
+  const float* v_scale;
+  float* k_scale_out;            // per-token-head mode: [8P][16][Hkv], written
+  float* v_scale_out;
+  int32_t num_tokens;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t kv_fp8;
+  int32_t scale_mode;
+};
+hipError_t msa_launch_insert(const MsaInsertArgs& a, hipStream_t s);
+
 constexpr int kMaxSplitTokens = 8192;
 hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, hipStream_t s);
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s);

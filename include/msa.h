@@ -218,6 +218,35 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
                              size_t workspace_bytes);
 
 /*
+ * msa_cache_insert — the step before the path: writes new tokens' K, V and
+ * index keys into the paged caches (#47287 page, 实现拆解 items 1, 2 and 5: the
+ * fused K/V insert fills the separate K and V planes and, unless the layer
+ * reuses another layer's index, the index cache; FP8 caches carry
+ * per-token-head or scalar K/V scales).
+ *   slot_mapping [num_tokens] int32: 128*page + offset of token t in its
+ *     page-128 physical page; negative (or >= 128*kv->num_pages): skipped.
+ *   k_new, v_new [num_tokens][Hkv][128] bf16.
+ *   kv: the caches written, in the layouts above; with
+ *     MSA_SCALE_PER_TOKEN_HEAD the scale arrays [8P][16][Hkv] are written too
+ *     (the struct's pointers are written through).
+ *   index_k_new [num_tokens][128] bf16, or NULL to leave the index cache alone
+ *     (a layer that reuses another layer's index); index_k [P][8][4][4][16][8]
+ *     bf16 is then written.
+ * Quantisation, each code decided in fp32: e4m3fn with per-token-head scales
+ * stores code = RNE(clamp(x / s, -448, 448)) with s = max|x| / 448 over the
+ * token-head (1 for an all-zero row); with a scalar scale s is read from
+ * k_scale[0] / v_scale[0] and not written; bf16 caches store RNE(x / s) with
+ * s = 1 unless scalar (per-token-head bf16 caches get scale 1).
+ * Two tokens mapped to one slot race. One launch, no workspace.
+ * Errors: as check of kv in msa_sparse_paged_attn; INVALID_ARG for
+ * num_tokens < 0, null slot_mapping / k_new / v_new, or index_k_new without
+ * index_k.
+ */
+msa_status msa_cache_insert(msa_stream_t stream, int32_t num_tokens, const int32_t* slot_mapping,
+                            const void* k_new, const void* v_new, const msa_kv* kv,
+                            const void* index_k_new, void* index_k);
+
+/*
  * msa_workspace_bytes — workspace needed by msa_sparse_paged_attn (ld_s = 0)
  * or msa_sparse_decode (max_ctx = 128*topk; ld_s > 0 when the scores live in
  * the workspace) on the current device. Returns 0 for invalid arguments.

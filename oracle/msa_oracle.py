@@ -455,7 +455,8 @@ def cache_insert(k_cache, v_cache, k_scale, v_scale, index_k, slot_mapping, k_ne
                  index_k_new, kv_dtype: int, scale_mode: int):
     """Writes token t of k_new / v_new ([T][Hkv][128] bf16) and index_k_new
     ([T][128] bf16, or None to leave the index cache alone) at slot
-    slot_mapping[t] = 128 * page + offset (negative: skipped). Returns updated
+    slot_mapping[t] = 128 * page + offset (negative, or past the caches' last
+    page: skipped). Returns updated
     copies (k_cache, v_cache, k_scale, v_scale, index_k). Per-token-head scales
     are written for every inserted token-head; a scalar scale is only read."""
     kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
@@ -463,8 +464,9 @@ def cache_insert(k_cache, v_cache, k_scale, v_scale, index_k, slot_mapping, k_ne
     vs = None if v_scale is None else np.array(v_scale, dtype=np.float32, copy=True)
     ik = None if index_k is None else np.array(index_k, copy=True)
     hkv_n = kc.shape[1]
+    num_slots = PAGE * (kc.shape[0] // SUBS_PER_PAGE)
     for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
-        if slot < 0:
+        if slot < 0 or slot >= num_slots:
             continue
         page, off = divmod(int(slot), PAGE)
         sub, j = SUBS_PER_PAGE * page + off // SUB, off % SUB

@@ -67,7 +67,8 @@ def _no_gpu_for_fake_pointers(request):
     # a machine with a GPU a validation bug would launch on them, so they only
     # run where no GPU is visible
     if request.node.name.startswith(("test_metadata_rejects", "test_index_score", "test_topk_rejects",
-                                     "test_attention_rejects", "test_empty_calls", "test_decode_rejects")):
+                                     "test_attention_rejects", "test_empty_calls", "test_decode_rejects",
+                                     "test_insert_rejects")):
         import torch
         if torch.cuda.is_available():
             pytest.skip("fake device pointers are only passed where no GPU is visible")
@@ -174,3 +175,21 @@ def test_decode_rejects_before_launch():
     bad = list(args)
     bad[5] = _fake_kv(num_pages=9)          # caches and batch disagree on P
     assert _code(msa.msa_sparse_decode, *bad) == msa.MSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,kv,expect", [
+    (dict(num_tokens=-1), {}, msa.MSA_ERR_INVALID_ARG),
+    (dict(slot_mapping=0), {}, msa.MSA_ERR_INVALID_ARG),
+    (dict(k_new=0), {}, msa.MSA_ERR_INVALID_ARG),
+    (dict(v_new=0), {}, msa.MSA_ERR_INVALID_ARG),
+    (dict(index_k=0), {}, msa.MSA_ERR_INVALID_ARG),     # index rows given, no index cache
+    ({}, dict(num_kv_heads=2), msa.MSA_ERR_UNSUPPORTED),
+    ({}, dict(kv_dtype=1, scale_mode=0), msa.MSA_ERR_UNSUPPORTED),
+    ({}, dict(kv_dtype=1, scale_mode=1, k_scale=0x10, v_scale=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_tokens=0), {}, 0),                          # nothing to do: no launch
+])
+def test_insert_rejects(args, kv, expect):
+    a = dict(num_tokens=4, slot_mapping=0x1, k_new=0x2, v_new=0x3, index_k_new=0x4, index_k=0x5)
+    a.update(args)
+    assert _code(msa.msa_cache_insert, a["num_tokens"], a["slot_mapping"], a["k_new"], a["v_new"],
+                 _fake_kv(**kv), a["index_k_new"], a["index_k"], 0) == expect
