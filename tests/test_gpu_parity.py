@@ -328,6 +328,35 @@ def test_fused_selection_with_tied_scores(gpu_lib, topk, shape):
     check_attention(b, H.bf16_to_np(o.out), table, ctx, rows)
 
 
+PREFILL_CASES = [
+    # prefill-shaped batches (>= 1024 rows): long requests around a one-row
+    # request, fp8 with both scale modes, a row bound past 1024 blocks
+    dict(L=[20000, 5000, 3000], ql=[600, 1, 500], kv=syn.KV_BF16, sm=syn.SCALE_NONE, topk=24),
+    dict(L=[9000, 140000, 700], ql=[300, 720, 17], kv=syn.KV_FP8, sm=syn.SCALE_PER_TOKEN_HEAD, topk=40),
+    dict(L=[4100, 2000], ql=[1000, 37], kv=syn.KV_FP8, sm=syn.SCALE_SCALAR, topk=8),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_fused_prefill_batches(gpu_lib, case):
+    c = PREFILL_CASES[case]
+    b = syn.make_batch("prefill", 150 + case, c["L"], c["ql"], topk=c["topk"], num_q_heads=16,
+                       kv_dtype=c["kv"], scale_mode=c["sm"])
+    print(f"[prefill] case {case} rows={b.num_rows} ld_s={b.ld_s}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    check_metadata(b, H.read_metadata(d))
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    check_selection(b, scores, table, ctx, sel, range(b.num_rows))
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all(), "every row's output is written"
+    rows = _sample_rows(b, 16, 160 + case)
+    check_scores(b, scores, rows)
+    check_attention(b, out, table, ctx, rows)
+
+
 def test_fused_decode_repeat_and_graph_replay_bitwise(gpu_lib):
     b = syn.make_batch("graph", 120, [20000, 3000, 7000], [4, 1, 2], topk=16, num_q_heads=16)
     d = H.upload(b)
