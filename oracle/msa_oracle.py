@@ -9,6 +9,8 @@ the C header documents and computes every step from its definition, in float64.
 Sources (prhub.com.cn summaries of vLLM pull requests):
   [P1] PR #47287, "add ROCm AITER sparse paged attention for MiniMax-M3"
   [P2] PR #54682, "optimise gfx950 MiniMax-M3 decode index and top-k"
+  [P3] PR #54404, "attention sinks for ROCm AITER sparse MLA, with a decode
+       operator that returns natural-log LSE"
   [P4] PR #56170, "MiniMax M3 cu_seqlens_k first element zeroed on the device"
 Section names are the pages' own: 功能与动机 (motivation), 实现拆解 (implementation
 breakdown, numbered items), 关键源码片段 (key source excerpt), 评论区精华 (review
@@ -24,7 +26,10 @@ Readings taken where the pages are silent:
   * every selected block expands to all 8 of its 16-token sub-pages, sub-page i
     of physical page P being 8P + i; the row is zero-filled up to 8*topk;
   * attention over the selected blocks' visible tokens with an exact softmax;
-    FP8 values are dequantised as scale x e4m3fn(code).
+    FP8 values are dequantised as scale x e4m3fn(code);
+  * the log-sum-exp is that of the scaled logits over the attended tokens
+    alone; a head's sink adds exp(sink) to its softmax denominator (a logit
+    with no value vector) and leaves the log-sum-exp unchanged.
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py to
 closed forms, brute force, library routines or invariants, except the modelling
@@ -284,6 +289,28 @@ def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: flo
     return (e @ v) / e.sum(axis=1, keepdims=True)
 
 
+def softmax_attention_lse(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float,
+                          sinks: np.ndarray | None = None):
+    """Attention of query heads q [H][D] over keys k [T][D], values v [T][D],
+    with each head's natural-log log-sum-exp of its scaled logits
+    z = sm_scale q k^T ([P3] 实现拆解 item 1: a decode operator that also
+    returns natural-log LSE):  lse[h] = ln sum_t exp(z[h][t]).
+    sinks [H] ([P3] 实现拆解 item 2: one float32 sink per head) add exp(sinks[h])
+    to head h's softmax denominator; lse stays that of the keys alone.
+    Returns (out [H][D], lse [H]); no keys give zeros and lse = -inf."""
+    H = q.shape[0]
+    if k.shape[0] == 0:
+        return np.zeros((H, v.shape[1]), dtype=np.float64), np.full(H, -np.inf)
+    z = sm_scale * (q @ k.T)                       # [H][T]
+    m = z.max(axis=1)
+    e = np.exp(z - m[:, None])
+    den = e.sum(axis=1)
+    lse = m + np.log(den)
+    if sinks is not None:
+        den = den + np.exp(np.asarray(sinks, dtype=np.float64) - m)
+    return (e @ v) / den[:, None], lse
+
+
 def sparse_attention_row(q_row_bits: np.ndarray, k_cache, v_cache, kv_dtype: int,
                          scale_mode: int, k_scale, v_scale, bt_row: np.ndarray,
                          sel: np.ndarray, v: int, sm_scale: float) -> np.ndarray:
@@ -369,6 +396,28 @@ def decode_step(batch, rows=None, scores_fp32: np.ndarray | None = None) -> dict
             "table": table, "ctx": ctx, "out": out, "rows": rows}
 
 
+def _table_keys_values(batch, table: np.ndarray, n: int, c: int, g: int):
+    """Dequantised K and V [c][128] of row n's tokens u < c for KV head g,
+    walked through the page-16 table (entry u // 16 names the sub-page of
+    token u, slot u % 16)."""
+    kh = np.empty((c, 128))
+    vh = np.empty((c, 128))
+    dec = bf16_to_f64 if batch.kv_dtype == 0 else e4m3fn_to_f64
+    for u in range(c):
+        sub = int(table[n][u // SUB])
+        slot = u % SUB
+        ks = vs = 1.0
+        if batch.scale_mode == 1:
+            ks = float(batch.k_scale.reshape(-1)[0])
+            vs = float(batch.v_scale.reshape(-1)[0])
+        elif batch.scale_mode == 2:
+            ks = float(batch.k_scale[sub, slot, g])
+            vs = float(batch.v_scale[sub, slot, g])
+        kh[u] = ks * dec(tile_row(batch.k_cache[sub, g], slot))
+        vh[u] = vs * dec(batch.v_cache[sub, g, :, slot])
+    return kh, vh
+
+
 def attention_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows) -> np.ndarray:
     """Attention for given rows driven by a page-16 table and context lengths
     (the path's own contract: entry u // 16 of the row names the sub-page of
@@ -381,24 +430,31 @@ def attention_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows) -> np.
         c = int(ctx[n])
         q = bf16_to_f64(batch.q[n])
         for g in range(hkv_n):
-            kh = np.empty((c, 128))
-            vh = np.empty((c, 128))
-            for u in range(c):
-                sub = int(table[n][u // SUB])
-                slot = u % SUB
-                ks = vs = 1.0
-                if batch.scale_mode == 1:
-                    ks = float(batch.k_scale.reshape(-1)[0])
-                    vs = float(batch.v_scale.reshape(-1)[0])
-                elif batch.scale_mode == 2:
-                    ks = float(batch.k_scale[sub, slot, g])
-                    vs = float(batch.v_scale[sub, slot, g])
-                dec = bf16_to_f64 if batch.kv_dtype == 0 else e4m3fn_to_f64
-                kh[u] = ks * dec(tile_row(batch.k_cache[sub, g], slot))
-                vh[u] = vs * dec(batch.v_cache[sub, g, :, slot])
+            kh, vh = _table_keys_values(batch, table, n, c, g)
             out[i, g * group:(g + 1) * group] = softmax_attention(
                 q[g * group:(g + 1) * group], kh, vh, batch.sm_scale)
     return out
+
+
+def attention_lse_from_table(batch, table: np.ndarray, ctx: np.ndarray, rows,
+                             sinks: np.ndarray | None = None):
+    """As attention_from_table, also returning the natural-log LSE per (row,
+    head) and applying optional per-query-head sinks [Hq] ([P3] 实现拆解
+    items 1-2; see softmax_attention_lse). Returns (out [R][Hq][128],
+    lse [R][Hq])."""
+    out = np.zeros((len(rows), batch.num_q_heads, batch.q.shape[-1]), dtype=np.float64)
+    lse = np.full((len(rows), batch.num_q_heads), -np.inf)
+    hkv_n = batch.k_cache.shape[1]
+    group = batch.num_q_heads // hkv_n
+    for i, n in enumerate(rows):
+        c = int(ctx[n])
+        q = bf16_to_f64(batch.q[n])
+        for g in range(hkv_n):
+            kh, vh = _table_keys_values(batch, table, n, c, g)
+            hs = slice(g * group, (g + 1) * group)
+            out[i, hs], lse[i, hs] = softmax_attention_lse(
+                q[hs], kh, vh, batch.sm_scale, None if sinks is None else np.asarray(sinks)[hs])
+    return out, lse
 
 
 # ---------------------------------------------------------------------------

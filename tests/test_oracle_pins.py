@@ -511,6 +511,115 @@ def test_decode_step_chain_on_tiny_workload():
 
 
 # ---------------------------------------------------------------------------
+# natural-log LSE and per-head sinks
+# ---------------------------------------------------------------------------
+def _lse_case(seed, T, H=8, scale=0.09):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, 128))
+    k = rng.standard_normal((T, 128)) * 1.5
+    v = rng.standard_normal((T, 128))
+    return q, k, v, scale
+
+
+def test_lse_matches_torch_logsumexp_and_output_matches_sdpa():
+    q, k, v, sc = _lse_case(40, 77)
+    out, lse = O.softmax_attention_lse(q, k, v, sc)
+    z = sc * torch.from_numpy(q) @ torch.from_numpy(k).T
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=1).numpy(), rtol=0, atol=1e-12)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k).expand(q.shape[0], -1, -1)[None],
+        torch.from_numpy(v).expand(q.shape[0], -1, -1)[None], scale=sc)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_lse_closed_forms():
+    # all-zero keys: every logit 0, lse = ln T, output = mean of the values
+    q, _, v, sc = _lse_case(41, 37)
+    out, lse = O.softmax_attention_lse(q, np.zeros((37, 128)), v, sc)
+    np.testing.assert_allclose(lse, np.full(8, math.log(37)), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=0), out.shape), rtol=0, atol=1e-13)
+    # one key: lse is its logit; two keys: ln(e^a + e^b) = max + log1p(e^-|a-b|)
+    q, k, v, sc = _lse_case(42, 2)
+    _, l1 = O.softmax_attention_lse(q, k[:1], v[:1], sc)
+    a = np.array([sc * math.fsum(q[h] * k[0]) for h in range(8)])
+    np.testing.assert_allclose(l1, a, rtol=0, atol=1e-12)
+    _, l2 = O.softmax_attention_lse(q, k, v, sc)
+    b = np.array([sc * math.fsum(q[h] * k[1]) for h in range(8)])
+    np.testing.assert_allclose(l2, np.maximum(a, b) + np.log1p(np.exp(-np.abs(a - b))), rtol=0, atol=1e-12)
+
+
+def test_lse_merges_splits():
+    """Attention over a union of key sets from its parts: lse = logaddexp of
+    the parts' lse, output = sum of part outputs weighted by exp(lse_i - lse)."""
+    q, k, v, sc = _lse_case(43, 300)
+    cuts = [0, 16, 128, 129, 300]
+    parts = [O.softmax_attention_lse(q, k[a:b], v[a:b], sc) for a, b in zip(cuts, cuts[1:])]
+    out, lse = O.softmax_attention_lse(q, k, v, sc)
+    lse_m = parts[0][1]
+    for _, l in parts[1:]:
+        lse_m = np.logaddexp(lse_m, l)
+    np.testing.assert_allclose(lse, lse_m, rtol=0, atol=1e-12)
+    out_m = sum(o * np.exp(l - lse)[:, None] for o, l in parts)
+    np.testing.assert_allclose(out, out_m, rtol=0, atol=1e-12)
+
+
+def test_sink_is_an_extra_logit_with_a_zero_value():
+    """torch softmax over the logits with the sink appended as one more column,
+    applied to the values with a zero row appended."""
+    q, k, v, sc = _lse_case(44, 50)
+    sinks = np.random.default_rng(45).uniform(-3.0, 6.0, 8).astype(np.float32)
+    out, lse = O.softmax_attention_lse(q, k, v, sc, sinks)
+    z = sc * torch.from_numpy(q) @ torch.from_numpy(k).T
+    z = torch.cat([z, torch.from_numpy(sinks.astype(np.float64))[:, None]], dim=1)
+    vv = torch.cat([torch.from_numpy(v), torch.zeros(1, 128, dtype=torch.float64)], dim=0)
+    np.testing.assert_allclose(out, (torch.softmax(z, dim=1) @ vv).numpy(), rtol=0, atol=1e-12)
+    # the lse is that of the keys alone
+    np.testing.assert_array_equal(lse, O.softmax_attention_lse(q, k, v, sc)[1])
+
+
+def test_sink_special_values():
+    q, k, v, sc = _lse_case(46, 90)
+    out0, lse0 = O.softmax_attention_lse(q, k, v, sc)
+    # -inf: no sink at all
+    out, _ = O.softmax_attention_lse(q, k, v, sc, np.full(8, -np.inf))
+    np.testing.assert_array_equal(out, out0)
+    # a sink equal to the lse takes half of the mass
+    out, _ = O.softmax_attention_lse(q, k, v, sc, lse0)
+    np.testing.assert_allclose(out, out0 / 2, rtol=0, atol=1e-13)
+    # no keys: zeros and -inf, with or without sinks, never NaN
+    for sinks in (None, np.zeros(8), np.full(8, -np.inf)):
+        out, lse = O.softmax_attention_lse(q, k[:0], v[:0], sc, sinks)
+        assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def test_table_lse_equals_logical_walk():
+    b = syn.make_batch("t", 31, seq_lens=[1000, 260, 40], query_lens=[2, 1, 1], topk=3, num_q_heads=16,
+                       kv_dtype=syn.KV_FP8, scale_mode=syn.SCALE_PER_TOKEN_HEAD)
+    res = O.decode_step(b)
+    ctx = res["ctx"].copy()
+    ctx[1] = 0                                   # a row with nothing to attend
+    sinks = np.linspace(-2.0, 3.0, 16).astype(np.float32)
+    out, lse = O.attention_lse_from_table(b, res["table"], ctx, res["rows"], sinks)
+    plain = O.attention_from_table(b, res["table"], ctx, res["rows"])
+    for i, n in enumerate(res["rows"]):
+        c = int(ctx[n])
+        if c == 0:
+            assert np.all(out[i] == 0) and np.all(lse[i] == -np.inf)
+            continue
+        # logits of the logical tokens the selection covers (walked through the page-128 table)
+        r = int(res["meta"]["row_req"][n])
+        v_n = O.visible_keys(res["meta"]["row_pos"][n])
+        toks = [t for blk in res["sel"][n] if blk >= 0 for t in range(128 * blk, min(128 * blk + 128, v_n))]
+        assert len(toks) == c
+        kh = O.dequant_tokens(b.k_cache, b.k_scale, b.scale_mode, b.kv_dtype, b.block_table[r], toks, 0, "k")
+        qf = O.bf16_to_f64(b.q[n])
+        z = b.sm_scale * torch.from_numpy(qf) @ torch.from_numpy(kh).T
+        np.testing.assert_allclose(lse[i], torch.logsumexp(z, dim=1).numpy(), rtol=0, atol=1e-12)
+        factor = 1.0 / (1.0 + np.exp(sinks.astype(np.float64) - lse[i]))
+        np.testing.assert_allclose(out[i], plain[i] * factor[:, None], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # cache insert (new tokens into the paged caches, FP8 quantisation)
 # ---------------------------------------------------------------------------
 def _insert_case(seed, T, num_pages, kv_fp8, scale_mode, with_index=True):
