@@ -200,7 +200,7 @@ MsaAttnArgs attn_args(const void* q, int32_t num_rows, int32_t num_q_heads, cons
   a.split_tok = p.split_tok;
   a.nsplit = p.nsplit;
   a.num_subpages = kv->num_pages * msa::kSubsPerPage;
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.scale_log2 = sm_scale * msa::kLog2e;
   return a;
 }
 
@@ -249,6 +249,14 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
                                  const msa_kv* kv, const int32_t* sparse_table, int32_t ld_table,
                                  const int32_t* ctx_lens, int32_t max_ctx, float sm_scale, void* out,
                                  void* workspace, size_t workspace_bytes) {
+  return msa_sparse_paged_attn_lse(stream, q, num_rows, num_q_heads, kv, sparse_table, ld_table, ctx_lens, max_ctx,
+                                   sm_scale, nullptr, out, nullptr, workspace, workspace_bytes);
+}
+
+msa_status msa_sparse_paged_attn_lse(msa_stream_t stream, const void* q, int32_t num_rows, int32_t num_q_heads,
+                                     const msa_kv* kv, const int32_t* sparse_table, int32_t ld_table,
+                                     const int32_t* ctx_lens, int32_t max_ctx, float sm_scale, const float* sinks,
+                                     void* out, float* lse, void* workspace, size_t workspace_bytes) {
   if (num_rows < 0 || max_ctx < 0 || ld_table < 0) return MSA_ERR_INVALID_ARG;
   if (num_q_heads < 1) return MSA_ERR_INVALID_ARG;
   if (num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
@@ -262,6 +270,8 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
   MsaAttnArgs a = attn_args(q, num_rows, num_q_heads, kv, ld_table, max_ctx, sm_scale, out, workspace);
   a.table_in = sparse_table;
   a.ctx_in = ctx_lens;
+  a.sinks = sinks;
+  a.lse_out = lse;
   return launch_attn_and_merge(static_cast<hipStream_t>(stream), a, kv);
 }
 
@@ -269,6 +279,16 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
                              const void* q, int32_t num_q_heads, const msa_kv* kv, int32_t topk, float sm_scale,
                              void* out, int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
                              float* block_scores, int32_t ld_s, void* workspace, size_t workspace_bytes) {
+  return msa_sparse_decode_lse(stream, batch, index_q, index_k, q, num_q_heads, kv, topk, sm_scale, nullptr, out,
+                               nullptr, sparse_table, ctx_lens, sel_blocks, block_scores, ld_s, workspace,
+                               workspace_bytes);
+}
+
+msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                                 const void* index_k, const void* q, int32_t num_q_heads, const msa_kv* kv,
+                                 int32_t topk, float sm_scale, const float* sinks, void* out, float* lse,
+                                 int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks, float* block_scores,
+                                 int32_t ld_s, void* workspace, size_t workspace_bytes) {
   msa_status st = check_batch(batch, true);
   if (st != MSA_OK) return st;
   st = check_kv(kv);
@@ -299,6 +319,8 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
   a.table_out = sparse_table;
   a.ctx_out = ctx_lens;
   a.sel_out = sel_blocks;
+  a.sinks = sinks;
+  a.lse_out = lse;
   return launch_attn_and_merge(s, a, kv);
 }
 

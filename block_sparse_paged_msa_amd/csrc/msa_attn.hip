@@ -19,6 +19,11 @@
 // workgroups leaves one partial (max, sum, unnormalised output) per split;
 // msa_merge_kernel combines them after the kernel boundary, in split order.
 //
+// Optional extras (vLLM PR #54404 page, 实现拆解 items 1-2): the natural-log
+// log-sum-exp of each (row, head)'s scaled logits, ln 2 * (m + log2 l) in the
+// log2-domain state, and one sink logit per query head that adds
+// 2^(sink*log2(e) - m) to the final denominator (the LSE excludes it).
+//
 // In the fused decode step (vLLM PR #54682 page, 实现拆解 items 1-3: the
 // indexer's selection feeds attention in the same step) every workgroup
 // selects its row's blocks from the block scores itself (msa_select.h): the
@@ -201,6 +206,8 @@ __device__ __forceinline__ void attend_split(const MsaAttnArgs& a, MergeLds& ml,
     vscal = a.v_scale[0];
   }
   const float zscale = a.scale_log2 * kscal;
+  // the sink is fetched now so that its load is long done at the end
+  const float sink2 = (a.sinks && th < nheads) ? a.sinks[hgi * kHeadTile + th] * kLog2e : -INFINITY;
 
   const int sp_per_wave = a.split_tok / (4 * kSub);
   const int sp_begin = split * (a.split_tok / kSub) + wave * sp_per_wave;
@@ -261,8 +268,11 @@ __device__ __forceinline__ void attend_split(const MsaAttnArgs& a, MergeLds& ml,
   }
 
   if (nsplit_n == 1) {
-    const float inv = (Lsum > 0.f) ? vscal / Lsum : 0.f;
+    const float den = Lsum + fast_exp2(sink2 - M);  // M is finite: the split holds a token
+    const float inv = (Lsum > 0.f) ? vscal / den : 0.f;
     if (th < nheads) *reinterpret_cast<u32x4*>(orow + th * kDim + td) = pack_bf16x8(acc0, acc1, inv);
+    if (a.lse_out && (tid & 15) == 0 && th < nheads)
+      a.lse_out[static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + th] = (M + log2f(Lsum)) * kLn2;
     return;
   }
   // partial: a scalar V scale is folded in here (the merge is linear in acc)
@@ -280,6 +290,8 @@ __device__ __forceinline__ void write_zero_row(const MsaAttnArgs& a, int n, int 
   const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
   uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile) * kDim;
   if (th < nheads) *reinterpret_cast<u32x4*>(orow + th * kDim + td) = u32x4{0u, 0u, 0u, 0u};
+  if (a.lse_out && (threadIdx.x & 15) == 0 && th < nheads)
+    a.lse_out[static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + th] = -INFINITY;
 }
 
 // Table mode: the row's sub-pages and context length come from the caller.
@@ -514,6 +526,7 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
     }
   };
   fetch(0);
+  const float sink2 = a.sinks ? a.sinks[head] * kLog2e : -INFINITY;
   const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
   const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
   if (nsplit_n <= 1) return;
@@ -545,8 +558,11 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   st = merge_partner<true>(st);
   if (sg == 0) {
     uint16_t* orow = a.out + (static_cast<size_t>(n) * a.num_q_heads + head) * kDim;
-    const float inv = (st.l > 0.f) ? 1.f / st.l : 0.f;
+    const float den = st.l + fast_exp2(sink2 - st.m);
+    const float inv = (st.l > 0.f) ? 1.f / den : 0.f;
     *reinterpret_cast<u32x4*>(orow + td) = pack_bf16x8(st.o0, st.o1, inv);
+    if (a.lse_out && lane == 0)
+      a.lse_out[static_cast<size_t>(n) * a.num_q_heads + head] = (st.m + log2f(st.l)) * kLn2;
   }
 }
 

@@ -90,6 +90,9 @@ __device__ __forceinline__ float sum_across_rows(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e): natural-log logits to log2 domain
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2): back to natural log
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
 // 1, 2, 4, 8 inside each 16-lane row, then the row totals are carried forward
 // (lane 15 into row 1 and row 3, then lane 31 into rows 2 and 3). Lanes whose
@@ -218,6 +221,8 @@ struct MsaAttnArgs {
   int32_t* ctx_out;
   int32_t* sel_out;    // may be null
   uint16_t* out;
+  float* lse_out;      // [rows][Hq] natural-log LSE, or null
+  const float* sinks;  // [Hq] per-head sink logits, or null
   float* partials;     // [rows][hgroups][nsplit][16*2 + 16*128]
   int32_t ld_table;    // row stride of the table (8*topk in fused mode)
   int32_t ld_s;

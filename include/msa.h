@@ -218,6 +218,37 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
                              size_t workspace_bytes);
 
 /*
+ * msa_sparse_paged_attn_lse / msa_sparse_decode_lse — the same two operations
+ * with two optional extras (#54404 page, 实现拆解 item 1: a decode operator
+ * that also returns the natural-log LSE, for merging partial attention;
+ * item 2: one learnable float32 sink per query head). Arguments as in
+ * msa_sparse_paged_attn / msa_sparse_decode, plus:
+ *   sinks [num_q_heads] fp32 (device), or NULL: head h's softmax denominator
+ *     gains exp(sinks[h]) — a logit with no value vector —
+ *       out[n][h] = sum_u e^{z_u} V-hat_u / (e^{sinks[h]} + sum_u e^{z_u}),
+ *     z_u = sm_scale * q[n][h] . K-hat_u. -inf means no sink; +inf gives zeros.
+ *   lse [num_rows][num_q_heads] fp32 (device), or NULL: written with
+ *     ln sum_u e^{z_u} over the attended tokens; the sink is not included, so
+ *     partial results over disjoint token sets can be merged with it and a
+ *     sink applied once afterwards. Rows with ctx 0 get -inf (and zero output).
+ * The plain entry points are these with sinks = lse = NULL. No extra
+ * workspace; errors as for the plain entry points.
+ */
+msa_status msa_sparse_paged_attn_lse(msa_stream_t stream, const void* q, int32_t num_rows,
+                                     int32_t num_q_heads, const msa_kv* kv,
+                                     const int32_t* sparse_table, int32_t ld_table,
+                                     const int32_t* ctx_lens, int32_t max_ctx, float sm_scale,
+                                     const float* sinks, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes);
+msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                                 const void* index_k, const void* q, int32_t num_q_heads,
+                                 const msa_kv* kv, int32_t topk, float sm_scale,
+                                 const float* sinks, void* out, float* lse,
+                                 int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
+                                 float* block_scores, int32_t ld_s, void* workspace,
+                                 size_t workspace_bytes);
+
+/*
  * msa_cache_insert — the step before the path: writes new tokens' K, V and
  * index keys into the paged caches (#47287 page, 实现拆解 items 1, 2 and 5: the
  * fused K/V insert fills the separate K and V planes and, unless the layer

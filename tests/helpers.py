@@ -167,3 +167,34 @@ def run_decode(d: DeviceBatch, o: DecodeOut, with_scores: bool = True) -> None:
     b = d.host
     msa.msa_sparse_decode(d.cbatch, d.index_q, d.index_k, d.q, b.num_q_heads, d.ckv, b.topk, b.sm_scale,
                           o.out, o.table, o.ctx, o.sel, o.scores if with_scores else None, b.ld_s, o.ws, o.wsb)
+
+
+def run_attn_lse(d: DeviceBatch, table: np.ndarray, ctx: np.ndarray, sinks: np.ndarray | None,
+                 max_ctx: int | None = None):
+    """msa_sparse_paged_attn_lse on a given table; returns (out, lse)."""
+    b = d.host
+    N, hq = b.num_rows, b.num_q_heads
+    ld_table = table.shape[1]
+    max_ctx = 16 * ld_table if max_ctx is None else max_ctx
+    t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
+    c = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32)).cuda()
+    s = None if sinks is None else torch.from_numpy(np.ascontiguousarray(sinks, dtype=np.float32)).cuda()
+    ofull, out = guarded(N * hq * 128, torch.int16, SENTINEL_U16)
+    lfull, lse = guarded(N * hq, torch.float32, SENTINEL_F32)
+    wsb = msa.msa_workspace_bytes(N, hq, max_ctx, 0)
+    ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+    msa.msa_sparse_paged_attn_lse(d.q, N, hq, d.ckv, t, ld_table, c, max_ctx, b.sm_scale, s, out, lse, ws, wsb)
+    assert guards_intact(ofull, SENTINEL_U16), "attention wrote outside its output"
+    assert guards_intact(lfull, SENTINEL_F32), "attention wrote outside its lse"
+    return bf16_to_np(out.view(N, hq, 128)), lse.view(N, hq).cpu().numpy().astype(np.float64)
+
+
+def run_decode_lse(d: DeviceBatch, o: DecodeOut, sinks: np.ndarray | None) -> np.ndarray:
+    """msa_sparse_decode_lse into o; returns the lse [N][Hq]."""
+    b = d.host
+    s = None if sinks is None else torch.from_numpy(np.ascontiguousarray(sinks, dtype=np.float32)).cuda()
+    lfull, lse = guarded(b.num_rows * b.num_q_heads, torch.float32, SENTINEL_F32)
+    msa.msa_sparse_decode_lse(d.cbatch, d.index_q, d.index_k, d.q, b.num_q_heads, d.ckv, b.topk, b.sm_scale, s,
+                              o.out, lse, o.table, o.ctx, o.sel, o.scores, b.ld_s, o.ws, o.wsb)
+    assert guards_intact(lfull, SENTINEL_F32), "decode wrote outside its lse"
+    return lse.view(b.num_rows, b.num_q_heads).cpu().numpy().astype(np.float64)
