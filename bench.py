@@ -344,6 +344,40 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},
     }
     res["cache_insert"] = time_insert(msa, torch)
+
+    # the same step through msa_sparse_decode_lse: LSE written, per-head sinks
+    # applied; both variants timed here the same way (one graph of `copies`
+    # steps, replayed)
+    sinks = torch.linspace(-1.0, 2.0, hq, device=dev, dtype=torch.float32)
+    lse = torch.empty((N, hq), dtype=torch.float32, device=dev)
+
+    def step_lse(c):
+        msa.msa_sparse_decode_lse(batches[c], index_q, index_k, q, hq, kv, topk, b.sm_scale, sinks, out, lse,
+                                  table, ctx, None, scores, ld_s, ws, wsb)
+
+    def graph_us_per_step(fn):
+        gs2 = torch.cuda.Stream()
+        gs2.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs2):
+            with torch.cuda.graph(g, stream=gs2):
+                for c in range(copies):
+                    fn(c)
+        stream.wait_stream(gs2)
+        torch.cuda.synchronize()
+        reps_g = max(1, 192 // copies)
+        runs = []
+        for _ in range(5):
+            e0.record(stream)
+            for _ in range(reps_g):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) * 1e3 / (reps_g * copies))
+        return sorted(runs)[len(runs) // 2]
+
+    res["lse_sinks"] = {"entry": "msa_sparse_decode_lse", "us_per_step": graph_us_per_step(step_lse),
+                        "plain_us_per_step": graph_us_per_step(step), "rows": N, "q_heads": hq}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, list(range(min(N, 8))))
