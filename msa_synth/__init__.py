@@ -19,14 +19,18 @@ Generator
   fp32 value; N(0,1) draws never approach the 448 limit.
 
 Draw order per batch: lengths, page permutation, index_q, index_k, q, k, v,
-scales. Everything is a pure function of ``(config, seed)``.
+scales, index-K scales (fp8 index caches only). Everything is a pure function
+of ``(config, seed)``; an fp8 index cache draws the same normals as a bf16 one,
+so every other array is the same in both.
 
 Buffer layouts (see ``include/msa.h``)
 --------------------------------------
 A 16-token tile of 128-dim rows is stored "MFMA-shuffled" as [4][4][16][8]:
 (32-dim chunk, 8-dim group, token, element); dim d of a token is at chunk d//32,
 group (d%32)//8, element d%8.
-* ``index_k``  [P][8][4][4][16][8] bf16 bits (uint16): page, 16-token tile, shuffled tile.
+* ``index_k``  [P][8][4][4][16][8] bf16 bits (uint16): page, 16-token tile, shuffled tile;
+  or e4m3fn codes (uint8) in the same order, with ``index_scale`` [P][128] fp32
+  (one scale per token slot of each page).
 * ``k_cache``  [P*8][Hkv][4][4][16][8]: sub-page, KV head, shuffled tile.
 * ``v_cache``  [P*8][Hkv][128][16]: dim-major inside each 16-token sub-page.
 * per-token-head scales [P*8][16][Hkv] fp32; scalar scales are a [1] array.
@@ -56,6 +60,8 @@ KV_FP8 = 1
 SCALE_NONE = 0
 SCALE_SCALAR = 1
 SCALE_PER_TOKEN_HEAD = 2
+INDEX_BF16 = 0
+INDEX_FP8 = 1
 
 
 class SplitMix64:
@@ -170,6 +176,8 @@ class Batch:
     v_cache: np.ndarray         # [8P][Hkv][128][16] uint16 or uint8
     k_scale: np.ndarray | None  # [1] or [8P][16][Hkv] float32
     v_scale: np.ndarray | None
+    index_dtype: int = INDEX_BF16
+    index_scale: np.ndarray | None = None   # [P][128] float32 (fp8 index only)
 
     @property
     def num_reqs(self) -> int:
@@ -192,7 +200,8 @@ def make_batch(name: str, seed: int, seq_lens, query_lens, topk: int, num_q_head
                *, kv_dtype: int = KV_BF16, scale_mode: int = SCALE_NONE,
                permute_pages: bool = True, max_seq_len: int | None = None,
                scale_lo: float = 0.5, scale_hi: float = 2.0, num_kv_heads: int = 1,
-               extra_pages: int = 0, ld_bt: int | None = None, data: bool = True) -> Batch:
+               extra_pages: int = 0, ld_bt: int | None = None, data: bool = True,
+               index_dtype: int = INDEX_BF16) -> Batch:
     """Build a batch from explicit lengths (lengths are not drawn here).
     With ``data=False`` only lengths and the block table are drawn; the tensor
     fields are empty (for tests of metadata and selection alone)."""
@@ -201,11 +210,12 @@ def make_batch(name: str, seed: int, seq_lens, query_lens, topk: int, num_q_head
     query_lens = np.asarray(query_lens, dtype=np.int32)
     return _fill(rng, name, seed, seq_lens, query_lens, topk, num_q_heads, kv_dtype,
                  scale_mode, permute_pages, max_seq_len, scale_lo, scale_hi,
-                 num_kv_heads, extra_pages, ld_bt, data)
+                 num_kv_heads, extra_pages, ld_bt, data, index_dtype)
 
 
 def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
-          permute_pages, max_seq_len, scale_lo, scale_hi, hkv, extra_pages, ld_bt, data=True):
+          permute_pages, max_seq_len, scale_lo, scale_hi, hkv, extra_pages, ld_bt, data=True,
+          index_dtype=INDEX_BF16):
     R = int(seq_lens.shape[0])
     nblk = [-(-int(L) // PAGE) for L in seq_lens]
     P = int(sum(nblk)) + int(extra_pages)
@@ -230,7 +240,10 @@ def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
                      k_cache=e16 if kv_dtype == KV_BF16 else e8,
                      v_cache=e16 if kv_dtype == KV_BF16 else e8, k_scale=None, v_scale=None)
     index_q = bf16_normal(rng, (N, INDEX_DIM))
-    index_k = bf16_normal(rng, (P,) + INDEX_PAGE_SHAPE)
+    if index_dtype == INDEX_FP8:
+        index_k = fp8_normal(rng, (P,) + INDEX_PAGE_SHAPE)
+    else:
+        index_k = bf16_normal(rng, (P,) + INDEX_PAGE_SHAPE)
     q = bf16_normal(rng, (N, hq, HEAD_DIM))
     if kv_dtype == KV_BF16:
         k_cache = bf16_normal(rng, (P * 8, hkv) + TILE_SHAPE)
@@ -246,12 +259,16 @@ def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
         n = P * 8 * SUB * hkv
         k_scale = (scale_lo + (scale_hi - scale_lo) * rng.uniform(n)).astype(np.float32).reshape(P * 8, SUB, hkv)
         v_scale = (scale_lo + (scale_hi - scale_lo) * rng.uniform(n)).astype(np.float32).reshape(P * 8, SUB, hkv)
+    index_scale = None
+    if index_dtype == INDEX_FP8:
+        index_scale = (scale_lo + (scale_hi - scale_lo) * rng.uniform(P * PAGE)).astype(np.float32) \
+            .reshape(P, PAGE)
     return Batch(name=name, seed=seed, seq_lens=seq_lens, query_lens=query_lens,
                  block_table=bt, num_pages=P, max_seq_len=int(max_seq_len), topk=int(topk),
                  num_q_heads=int(hq), num_kv_heads=int(hkv), kv_dtype=int(kv_dtype),
                  scale_mode=int(scale_mode), sm_scale=1.0 / math.sqrt(HEAD_DIM),
                  index_q=index_q, index_k=index_k, q=q, k_cache=k_cache, v_cache=v_cache,
-                 k_scale=k_scale, v_scale=v_scale)
+                 k_scale=k_scale, v_scale=v_scale, index_dtype=int(index_dtype), index_scale=index_scale)
 
 
 # ---------------------------------------------------------------------------

@@ -12,6 +12,9 @@ Sources (prhub.com.cn summaries of vLLM pull requests):
   [P3] PR #54404, "attention sinks for ROCm AITER sparse MLA, with a decode
        operator that returns natural-log LSE"
   [P4] PR #56170, "MiniMax M3 cu_seqlens_k first element zeroed on the device"
+The FP8 index cache is named on the [P2] page (相关 PRs: #52664 routes FP8
+decode scoring and top-k elsewhere, #53448 adds optional FP8 index storage);
+its format is a reading (below).
 Section names are the pages' own: 功能与动机 (motivation), 实现拆解 (implementation
 breakdown, numbered items), 关键源码片段 (key source excerpt), 评论区精华 (review
 highlights), 风险与影响 (risks).
@@ -27,6 +30,8 @@ Readings taken where the pages are silent:
     of physical page P being 8P + i; the row is zero-filled up to 8*topk;
   * attention over the selected blocks' visible tokens with an exact softmax;
     FP8 values are dequantised as scale x e4m3fn(code);
+  * an FP8 index cache holds e4m3fn codes with one fp32 scale per token
+    (index key = scale x e4m3fn(code)); the index query stays bf16;
   * the log-sum-exp is that of the scaled logits over the attended tokens
     alone; a head's sink adds exp(sink) to its softmax denominator (a logit
     with no value vector) and leaves the log-sum-exp unchanged.
@@ -130,17 +135,26 @@ def tile_row(tile: np.ndarray, tok: int) -> np.ndarray:
     return tile[:, :, tok, :].reshape(-1)
 
 
-def index_keys_of_request(index_k_bits: np.ndarray, bt_row: np.ndarray, ntok: int) -> np.ndarray:
+def index_keys_of_request(index_k_bits: np.ndarray, bt_row: np.ndarray, ntok: int,
+                          index_scale: np.ndarray | None = None) -> np.ndarray:
     """Logical index keys [ntok][128] of one request: token t lives in physical
     page bt_row[t // 128], slot s = t % 128 (the page-128 cache, [P1] 实现拆解
-    item 3), i.e. in 16-token tile s // 16 of the page, as token s % 16."""
+    item 3), i.e. in 16-token tile s // 16 of the page, as token s % 16.
+    With ``index_scale`` ([P][128] fp32) the pages hold e4m3fn codes and the
+    key is index_scale[page][s] x e4m3fn(code) (the optional FP8 index cache
+    of PR #53448, named on the [P2] page; per-token scale is a reading)."""
     out = np.empty((ntok, 128), dtype=np.float64)
     for j in range(num_blocks(ntok)):
         lo, hi = j * PAGE, min((j + 1) * PAGE, ntok)
-        page = index_k_bits[int(bt_row[j])]               # [8][4][4][16][8]
+        pid = int(bt_row[j])
+        page = index_k_bits[pid]                          # [8][4][4][16][8]
         # (tile, chunk, group, token, element) -> (tile, token, chunk, group, element)
-        rows = page.transpose(0, 3, 1, 2, 4).reshape(PAGE, 128)
-        out[lo:hi] = bf16_to_f64(rows[: hi - lo])
+        rows = page.transpose(0, 3, 1, 2, 4).reshape(PAGE, 128)[: hi - lo]
+        if index_scale is None:
+            out[lo:hi] = bf16_to_f64(rows)
+        else:
+            sc = np.asarray(index_scale, dtype=np.float64)[pid, : hi - lo]
+            out[lo:hi] = e4m3fn_to_f64(rows) * sc[:, None]
     return out
 
 
@@ -163,10 +177,11 @@ def pool_blocks(tok_scores: np.ndarray, nb: int) -> np.ndarray:
 
 def block_scores(index_q: np.ndarray, index_k: np.ndarray, block_table: np.ndarray,
                  seq_lens: np.ndarray, query_lens: np.ndarray, ld_s: int,
-                 rows=None) -> np.ndarray:
+                 rows=None, index_scale: np.ndarray | None = None) -> np.ndarray:
     """[N][ld_s] pooled scores; -inf at and beyond each row's block count.
 
-    ``rows`` restricts the computation to a subset of rows (others stay -inf)."""
+    ``rows`` restricts the computation to a subset of rows (others stay -inf);
+    ``index_scale`` marks an FP8 index cache (see index_keys_of_request)."""
     meta = build_metadata(seq_lens, query_lens)
     N = len(meta["row_req"])
     out = np.full((N, ld_s), -np.inf, dtype=np.float64)
@@ -175,7 +190,7 @@ def block_scores(index_q: np.ndarray, index_k: np.ndarray, block_table: np.ndarr
     for n in want:
         by_req.setdefault(int(meta["row_req"][n]), []).append(n)
     for r, ns in by_req.items():
-        keys = index_keys_of_request(index_k, block_table[r], int(seq_lens[r]))
+        keys = index_keys_of_request(index_k, block_table[r], int(seq_lens[r]), index_scale)
         for n in ns:
             v = visible_keys(meta["row_pos"][n])
             nb = num_blocks(v)
@@ -371,7 +386,8 @@ def decode_step(batch, rows=None, scores_fp32: np.ndarray | None = None) -> dict
     rows = list(range(N)) if rows is None else [int(r) for r in rows]
     if scores_fp32 is None:
         s64 = block_scores(batch.index_q, batch.index_k, batch.block_table, batch.seq_lens,
-                           batch.query_lens, batch.ld_s, rows=rows)
+                           batch.query_lens, batch.ld_s, rows=rows,
+                           index_scale=getattr(batch, "index_scale", None))
         s32 = s64.astype(np.float32)
     else:
         s64 = None
@@ -539,3 +555,23 @@ def cache_insert(k_cache, v_cache, k_scale, v_scale, index_k, slot_mapping, k_ne
         if index_k_new is not None and ik is not None:
             tile_store(ik[page, off // SUB], j, np.asarray(index_k_new)[t])
     return kc, vc, ks, vs, ik
+
+
+def index_insert_fp8(index_k_codes, index_scale, slot_mapping, index_k_new):
+    """The index half of the insert for an FP8 index cache: token t's index
+    key ([T][128] bf16) is quantised with its own scale by the per-token rule
+    of quantize_row (s = fp32(max |x|) / 448, 1 for an all-zero row; code =
+    e4m3fn RNE of clamp(x / s, +-448)), stored at slot_mapping[t] = 128 * page
+    + offset (negative, or past the last page: skipped) with index_scale[page]
+    [offset] = s. Returns updated copies (index_k_codes, index_scale)."""
+    ik = np.array(index_k_codes, copy=True)
+    isc = np.array(index_scale, dtype=np.float32, copy=True)
+    num_slots = PAGE * ik.shape[0]
+    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0 or slot >= num_slots:
+            continue
+        page, off = slot // PAGE, slot % PAGE
+        codes, sc = quantize_row(np.asarray(index_k_new)[t], 1, 2, None)
+        tile_store(ik[page, off // SUB], off % SUB, codes)
+        isc[page, off] = np.float32(sc)
+    return ik, isc

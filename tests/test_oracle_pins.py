@@ -744,3 +744,117 @@ def test_insert_then_decode_equals_decode_on_the_written_cache():
     kc, vc, _, _, _ = O.cache_insert(kc, vc, None, None, None, slots, k_new, v_new, None, 0, 0)
     b2 = syn.Batch(**{**b.__dict__, "k_cache": kc, "v_cache": vc})
     assert np.array_equal(O.decode_step(b2)["out"], ref)
+
+
+# ---------------------------------------------------------------------------
+# FP8 index cache (e4m3fn codes, one fp32 scale per token)
+# ---------------------------------------------------------------------------
+def test_fp8_index_with_power_of_two_scales_equals_the_bf16_path():
+    """e4m3 values times 2^k are exact in bf16: an fp8 index cache whose
+    per-token scales are random powers of two must score exactly like a bf16
+    index cache holding bf16(scale * e4m3(code)), written by this file's own
+    writer at the same logical positions."""
+    rng = np.random.default_rng(50)
+    L = [700, 300, 1]
+    nb = [-(-x // 128) for x in L]
+    P = sum(nb) + 2
+    perm = rng.permutation(P)
+    bt = np.zeros((3, max(nb)), np.int32)
+    pos = 0
+    for r in range(3):
+        bt[r, :nb[r]] = perm[pos:pos + nb[r]]
+        pos += nb[r]
+    codes = fp8_codes(rng.standard_normal((P, 8, 4, 4, 16, 8)))
+    scale = np.exp2(rng.integers(-3, 4, (P, 128))).astype(np.float32)
+    # logical keys of every physical slot, then the bf16 cache through the test's writer
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    bf = np.zeros((P, 8, 4, 4, 16, 8), np.uint16)
+    for p in range(P):
+        for s_ in range(128):
+            row = np.array([vals[p, s_ // 16, d // 32, (d % 32) // 8, s_ % 16, d % 8] for d in range(128)])
+            shuffle_into(bf[p, s_ // 16], s_ % 16, bf16_bits(row * float(scale[p, s_])))
+    iq = bf16_bits(rng.standard_normal((5, 128)))
+    ql = np.array([2, 2, 1])
+    a = O.block_scores(iq, codes, bt, np.array(L), ql, 8, index_scale=scale)
+    b = O.block_scores(iq, bf, bt, np.array(L), ql, 8)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_fp8_index_scale_of_one_token_moves_only_its_score():
+    """One-hot query on dim d: each token's score is scale x e4m3(code[d]);
+    doubling one token's scale doubles that token's score and leaves the
+    block max of every other block alone."""
+    rng = np.random.default_rng(51)
+    P = 3
+    codes = fp8_codes(rng.standard_normal((P, 8, 4, 4, 16, 8)))
+    scale = rng.uniform(0.5, 2.0, (P, 128)).astype(np.float32)
+    bt = np.array([[2, 0, 1]], np.int32)
+    d = 77
+    keys = O.index_keys_of_request(codes, bt[0], 300, scale)
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    for t in (0, 130, 299):
+        p, s_ = int(bt[0, t // 128]), t % 128
+        want = float(scale[p, s_]) * vals[p, s_ // 16, d // 32, (d % 32) // 8, s_ % 16, d % 8]
+        assert keys[t, d] == want
+    scale2 = scale.copy()
+    scale2[0, 5] *= 2                              # token 128 + 5 lives in page 0
+    keys2 = O.index_keys_of_request(codes, bt[0], 300, scale2)
+    changed = np.flatnonzero(np.any(keys2 != keys, axis=1))
+    assert changed.tolist() == [133]
+    np.testing.assert_array_equal(keys2[133], 2 * keys[133])
+
+
+def test_index_insert_fp8_scale_rule_placement_and_skips():
+    rng = np.random.default_rng(52)
+    P, T = 4, 40
+    x = rng.standard_normal((T, 128)) * rng.uniform(0.01, 30.0, (T, 1))
+    x[7] = 0.0                                     # all-zero row: scale 1, zero codes
+    new = bf16_bits(x)
+    slots = rng.choice(P * 128, size=T, replace=False).astype(np.int32)
+    slots[3], slots[9] = -1, P * 128 + 2           # skipped
+    ik0 = rng.integers(0, 256, (P, 8, 4, 4, 16, 8)).astype(np.uint8)
+    sc0 = rng.uniform(1, 2, (P, 128)).astype(np.float32)
+    ik, sc = O.index_insert_fp8(ik0, sc0, slots, new)
+    touched = np.zeros((P, 128), bool)
+    for t, slot in enumerate(slots.tolist()):
+        if slot < 0 or slot >= P * 128:
+            continue
+        p, off = slot // 128, slot % 128
+        touched[p, off] = True
+        xf = O.bf16_to_f64(new[t])
+        amax = np.float32(np.abs(xf).max())
+        s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+        assert sc[p, off] == s
+        # the stored row, read back through this file's own tile addressing
+        stored = np.array([ik[p, off // 16, d // 32, (d % 32) // 8, off % 16, d % 8] for d in range(128)],
+                          np.uint8)
+        vals = torch.from_numpy(stored.copy()).view(torch.float8_e4m3fn).double().numpy()
+        if amax == 0:
+            assert np.all(vals == 0)
+            continue
+        assert np.abs(vals).max() == 448.0
+        err = np.abs(float(s) * vals - xf)
+        assert np.all(err <= np.maximum(np.abs(xf) * 2.0 ** -4, float(s) * 2.0 ** -10) * (1 + 1e-6))
+    # untouched slots keep their codes and scales
+    np.testing.assert_array_equal(sc[~touched], sc0[~touched])
+    for p in range(P):
+        for off in range(128):
+            if not touched[p, off]:
+                assert np.array_equal(ik[p, off // 16, :, :, off % 16, :], ik0[p, off // 16, :, :, off % 16, :])
+
+
+def test_decode_step_on_an_fp8_index_cache_scores_with_the_scales():
+    """The whole oracle step on an fp8 index batch: its scores equal the
+    scores of the same batch with the index cache dequantised into fp64 keys
+    by hand (scale x code value) and scored by matrix product."""
+    b = syn.make_batch("f8i", 53, [1000, 260], [2, 1], topk=3, num_q_heads=16, index_dtype=syn.INDEX_FP8)
+    res = O.decode_step(b)
+    vals = torch.from_numpy(b.index_k.copy()).view(torch.float8_e4m3fn).double().numpy()
+    for n, (r, pos) in enumerate([(0, 998), (0, 999), (1, 259)]):
+        keys = []
+        for t in range(pos + 1):
+            p, s_ = int(b.block_table[r, t // 128]), t % 128
+            keys.append(vals[p, s_ // 16].transpose(2, 0, 1, 3)[s_ % 16].reshape(-1) * float(b.index_scale[p, s_]))
+        z = np.array(keys) @ O.bf16_to_f64(b.index_q[n])
+        want = [z[128 * j:128 * (j + 1)].max() for j in range(-(-(pos + 1) // 128))]
+        np.testing.assert_allclose(res["scores"][n, :len(want)], want, rtol=1e-13, atol=0)
