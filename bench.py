@@ -345,15 +345,15 @@ def main():
     }
     res["cache_insert"] = time_insert(msa, torch)
 
-    # the same step through msa_sparse_decode_lse: LSE written, per-head sinks
+    # the same step through msa_sparse_decode_ex: LSE written, per-head sinks
     # applied; both variants timed here the same way (one graph of `copies`
     # steps, replayed)
     sinks = torch.linspace(-1.0, 2.0, hq, device=dev, dtype=torch.float32)
     lse = torch.empty((N, hq), dtype=torch.float32, device=dev)
 
     def step_lse(c):
-        msa.msa_sparse_decode_lse(batches[c], index_q, index_k, q, hq, kv, topk, b.sm_scale, sinks, out, lse,
-                                  table, ctx, None, scores, ld_s, ws, wsb)
+        msa.msa_sparse_decode_ex(batches[c], index_q, index_k, None, q, hq, kv, topk, b.sm_scale, sinks, out, lse,
+                                 table, ctx, None, scores, ld_s, ws, wsb)
 
     def graph_us_per_step(fn):
         gs2 = torch.cuda.Stream()
@@ -376,7 +376,7 @@ def main():
             runs.append(e0.elapsed_time(e1) * 1e3 / (reps_g * copies))
         return sorted(runs)[len(runs) // 2]
 
-    res["lse_sinks"] = {"entry": "msa_sparse_decode_lse", "us_per_step": graph_us_per_step(step_lse),
+    res["lse_sinks"] = {"entry": "msa_sparse_decode_ex", "us_per_step": graph_us_per_step(step_lse),
                         "plain_us_per_step": graph_us_per_step(step), "rows": N, "q_heads": hq}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)

@@ -28,7 +28,8 @@ MSA_SCALE_PER_TOKEN_HEAD = 2
 
 EXPORTS = (
     "msa_build_metadata", "msa_index_score", "msa_topk_block_table", "msa_sparse_paged_attn",
-    "msa_sparse_decode", "msa_sparse_paged_attn_lse", "msa_sparse_decode_lse", "msa_cache_insert",
+    "msa_sparse_decode", "msa_index_score_ex", "msa_sparse_paged_attn_ex", "msa_sparse_decode_ex",
+    "msa_cache_insert", "msa_cache_insert_ex",
     "msa_workspace_bytes", "msa_status_string", "msa_version",
 )
 
@@ -78,10 +79,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "msa_topk_block_table": ([vp, bp, vp, i32, i32, vp, vp, vp], i32),
         "msa_sparse_paged_attn": ([vp, vp, i32, i32, kp, vp, i32, vp, i32, f32, vp, vp, sz], i32),
         "msa_sparse_decode": ([vp, bp, vp, vp, vp, i32, kp, i32, f32, vp, vp, vp, vp, vp, i32, vp, sz], i32),
-        "msa_sparse_paged_attn_lse": ([vp, vp, i32, i32, kp, vp, i32, vp, i32, f32, vp, vp, vp, vp, sz], i32),
-        "msa_sparse_decode_lse": ([vp, bp, vp, vp, vp, i32, kp, i32, f32, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz],
-                                  i32),
+        "msa_index_score_ex": ([vp, bp, vp, vp, vp, vp, i32], i32),
+        "msa_sparse_paged_attn_ex": ([vp, vp, i32, i32, kp, vp, i32, vp, i32, f32, vp, vp, vp, vp, sz], i32),
+        "msa_sparse_decode_ex": ([vp, bp, vp, vp, vp, vp, i32, kp, i32, f32, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                  sz], i32),
         "msa_cache_insert": ([vp, i32, vp, vp, vp, kp, vp, vp], i32),
+        "msa_cache_insert_ex": ([vp, i32, vp, vp, vp, kp, vp, vp, vp], i32),
         "msa_workspace_bytes": ([i32, i32, i32, i32], sz),
         "msa_status_string": ([i32], ctypes.c_char_p),
         "msa_version": ([], i32),
@@ -167,21 +170,28 @@ def msa_sparse_decode(batch: MsaBatch, index_q, index_k, q, num_q_heads: int, kv
         _ptr(block_scores), ld_s, _ptr(workspace), workspace_bytes))
 
 
-def msa_sparse_paged_attn_lse(q, num_rows: int, num_q_heads: int, kv: MsaKV, sparse_table, ld_table: int,
-                              ctx_lens, max_ctx: int, sm_scale: float, sinks, out, lse, workspace,
-                              workspace_bytes: int, stream=None) -> None:
-    _check("msa_sparse_paged_attn_lse", load().msa_sparse_paged_attn_lse(
+def msa_index_score_ex(batch: MsaBatch, index_q, index_k, index_k_scale, block_scores, ld_s: int,
+                       stream=None) -> None:
+    _check("msa_index_score_ex", load().msa_index_score_ex(
+        _stream(stream), ctypes.byref(batch), _ptr(index_q), _ptr(index_k), _ptr(index_k_scale),
+        _ptr(block_scores), ld_s))
+
+
+def msa_sparse_paged_attn_ex(q, num_rows: int, num_q_heads: int, kv: MsaKV, sparse_table, ld_table: int,
+                             ctx_lens, max_ctx: int, sm_scale: float, sinks, out, lse, workspace,
+                             workspace_bytes: int, stream=None) -> None:
+    _check("msa_sparse_paged_attn_ex", load().msa_sparse_paged_attn_ex(
         _stream(stream), _ptr(q), num_rows, num_q_heads, ctypes.byref(kv), _ptr(sparse_table), ld_table,
         _ptr(ctx_lens), max_ctx, sm_scale, _ptr(sinks), _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes))
 
 
-def msa_sparse_decode_lse(batch: MsaBatch, index_q, index_k, q, num_q_heads: int, kv: MsaKV, topk: int,
-                          sm_scale: float, sinks, out, lse, sparse_table, ctx_lens, sel_blocks, block_scores,
-                          ld_s: int, workspace, workspace_bytes: int, stream=None) -> None:
-    _check("msa_sparse_decode_lse", load().msa_sparse_decode_lse(
-        _stream(stream), ctypes.byref(batch), _ptr(index_q), _ptr(index_k), _ptr(q), num_q_heads,
-        ctypes.byref(kv), topk, sm_scale, _ptr(sinks), _ptr(out), _ptr(lse), _ptr(sparse_table), _ptr(ctx_lens),
-        _ptr(sel_blocks), _ptr(block_scores), ld_s, _ptr(workspace), workspace_bytes))
+def msa_sparse_decode_ex(batch: MsaBatch, index_q, index_k, index_k_scale, q, num_q_heads: int, kv: MsaKV,
+                         topk: int, sm_scale: float, sinks, out, lse, sparse_table, ctx_lens, sel_blocks,
+                         block_scores, ld_s: int, workspace, workspace_bytes: int, stream=None) -> None:
+    _check("msa_sparse_decode_ex", load().msa_sparse_decode_ex(
+        _stream(stream), ctypes.byref(batch), _ptr(index_q), _ptr(index_k), _ptr(index_k_scale), _ptr(q),
+        num_q_heads, ctypes.byref(kv), topk, sm_scale, _ptr(sinks), _ptr(out), _ptr(lse), _ptr(sparse_table),
+        _ptr(ctx_lens), _ptr(sel_blocks), _ptr(block_scores), ld_s, _ptr(workspace), workspace_bytes))
 
 
 def msa_cache_insert(num_tokens: int, slot_mapping, k_new, v_new, kv: MsaKV, index_k_new, index_k,
@@ -189,6 +199,13 @@ def msa_cache_insert(num_tokens: int, slot_mapping, k_new, v_new, kv: MsaKV, ind
     _check("msa_cache_insert", load().msa_cache_insert(
         _stream(stream), num_tokens, _ptr(slot_mapping), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
         _ptr(index_k_new), _ptr(index_k)))
+
+
+def msa_cache_insert_ex(num_tokens: int, slot_mapping, k_new, v_new, kv: MsaKV, index_k_new, index_k,
+                        index_k_scale, stream=None) -> None:
+    _check("msa_cache_insert_ex", load().msa_cache_insert_ex(
+        _stream(stream), num_tokens, _ptr(slot_mapping), _ptr(k_new), _ptr(v_new), ctypes.byref(kv),
+        _ptr(index_k_new), _ptr(index_k), _ptr(index_k_scale)))
 
 
 def msa_workspace_bytes(num_rows: int, num_q_heads: int, max_ctx: int, ld_s: int) -> int:

@@ -128,10 +128,11 @@ MsaMetaArgs meta_args(const msa_batch* b) {
 }
 
 msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, const void* index_k,
-                        float* scores, int32_t ld_s, bool write_meta) {
+                        const float* index_scale, float* scores, int32_t ld_s, bool write_meta) {
   MsaScoreArgs a;
   a.index_q = static_cast<const uint16_t*>(index_q);
-  a.index_k = static_cast<const uint16_t*>(index_k);
+  a.index_k = index_k;
+  a.index_scale = index_scale;
   a.block_table = b->block_table;
   a.seq_lens = b->seq_lens;
   a.query_lens = b->query_lens;
@@ -223,12 +224,18 @@ msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch) {
 
 msa_status msa_index_score(msa_stream_t stream, const msa_batch* batch, const void* index_q, const void* index_k,
                            float* block_scores, int32_t ld_s) {
+  return msa_index_score_ex(stream, batch, index_q, index_k, nullptr, block_scores, ld_s);
+}
+
+msa_status msa_index_score_ex(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                              const void* index_k, const float* index_k_scale, float* block_scores, int32_t ld_s) {
   msa_status st = check_batch(batch, false);
   if (st != MSA_OK) return st;
   if (batch->num_rows == 0) return MSA_OK;
   if (!index_q || !index_k || !block_scores) return MSA_ERR_INVALID_ARG;
   if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
-  return launch_score(static_cast<hipStream_t>(stream), batch, index_q, index_k, block_scores, ld_s, false);
+  return launch_score(static_cast<hipStream_t>(stream), batch, index_q, index_k, index_k_scale, block_scores, ld_s,
+                      false);
 }
 
 msa_status msa_topk_block_table(msa_stream_t stream, const msa_batch* batch, const float* block_scores,
@@ -249,14 +256,14 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
                                  const msa_kv* kv, const int32_t* sparse_table, int32_t ld_table,
                                  const int32_t* ctx_lens, int32_t max_ctx, float sm_scale, void* out,
                                  void* workspace, size_t workspace_bytes) {
-  return msa_sparse_paged_attn_lse(stream, q, num_rows, num_q_heads, kv, sparse_table, ld_table, ctx_lens, max_ctx,
-                                   sm_scale, nullptr, out, nullptr, workspace, workspace_bytes);
+  return msa_sparse_paged_attn_ex(stream, q, num_rows, num_q_heads, kv, sparse_table, ld_table, ctx_lens, max_ctx,
+                                  sm_scale, nullptr, out, nullptr, workspace, workspace_bytes);
 }
 
-msa_status msa_sparse_paged_attn_lse(msa_stream_t stream, const void* q, int32_t num_rows, int32_t num_q_heads,
-                                     const msa_kv* kv, const int32_t* sparse_table, int32_t ld_table,
-                                     const int32_t* ctx_lens, int32_t max_ctx, float sm_scale, const float* sinks,
-                                     void* out, float* lse, void* workspace, size_t workspace_bytes) {
+msa_status msa_sparse_paged_attn_ex(msa_stream_t stream, const void* q, int32_t num_rows, int32_t num_q_heads,
+                                    const msa_kv* kv, const int32_t* sparse_table, int32_t ld_table,
+                                    const int32_t* ctx_lens, int32_t max_ctx, float sm_scale, const float* sinks,
+                                    void* out, float* lse, void* workspace, size_t workspace_bytes) {
   if (num_rows < 0 || max_ctx < 0 || ld_table < 0) return MSA_ERR_INVALID_ARG;
   if (num_q_heads < 1) return MSA_ERR_INVALID_ARG;
   if (num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
@@ -279,16 +286,16 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
                              const void* q, int32_t num_q_heads, const msa_kv* kv, int32_t topk, float sm_scale,
                              void* out, int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
                              float* block_scores, int32_t ld_s, void* workspace, size_t workspace_bytes) {
-  return msa_sparse_decode_lse(stream, batch, index_q, index_k, q, num_q_heads, kv, topk, sm_scale, nullptr, out,
-                               nullptr, sparse_table, ctx_lens, sel_blocks, block_scores, ld_s, workspace,
-                               workspace_bytes);
+  return msa_sparse_decode_ex(stream, batch, index_q, index_k, nullptr, q, num_q_heads, kv, topk, sm_scale, nullptr,
+                              out, nullptr, sparse_table, ctx_lens, sel_blocks, block_scores, ld_s, workspace,
+                              workspace_bytes);
 }
 
-msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, const void* index_q,
-                                 const void* index_k, const void* q, int32_t num_q_heads, const msa_kv* kv,
-                                 int32_t topk, float sm_scale, const float* sinks, void* out, float* lse,
-                                 int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks, float* block_scores,
-                                 int32_t ld_s, void* workspace, size_t workspace_bytes) {
+msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, const void* index_q, const void* index_k,
+                                const float* index_k_scale, const void* q, int32_t num_q_heads, const msa_kv* kv,
+                                int32_t topk, float sm_scale, const float* sinks, void* out, float* lse,
+                                int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks, float* block_scores,
+                                int32_t ld_s, void* workspace, size_t workspace_bytes) {
   msa_status st = check_batch(batch, true);
   if (st != MSA_OK) return st;
   st = check_kv(kv);
@@ -305,7 +312,7 @@ msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores);
   // 1) metadata + index scores, 2) per-row selection + attention, 3) split merge
-  st = launch_score(s, batch, index_q, index_k, scores, ld_s, true);
+  st = launch_score(s, batch, index_q, index_k, index_k_scale, scores, ld_s, true);
   if (st != MSA_OK) return st;
   MsaAttnArgs a = attn_args(q, batch->num_rows, num_q_heads, kv, 8 * topk, max_ctx, sm_scale, out, workspace);
   a.scores = scores;
@@ -326,6 +333,12 @@ msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, co
 
 msa_status msa_cache_insert(msa_stream_t stream, int32_t num_tokens, const int32_t* slot_mapping, const void* k_new,
                             const void* v_new, const msa_kv* kv, const void* index_k_new, void* index_k) {
+  return msa_cache_insert_ex(stream, num_tokens, slot_mapping, k_new, v_new, kv, index_k_new, index_k, nullptr);
+}
+
+msa_status msa_cache_insert_ex(msa_stream_t stream, int32_t num_tokens, const int32_t* slot_mapping,
+                               const void* k_new, const void* v_new, const msa_kv* kv, const void* index_k_new,
+                               void* index_k, float* index_k_scale) {
   msa_status st = check_kv(kv);
   if (st != MSA_OK) return st;
   if (num_tokens < 0) return MSA_ERR_INVALID_ARG;
@@ -345,6 +358,7 @@ msa_status msa_cache_insert(msa_stream_t stream, int32_t num_tokens, const int32
   a.v_scale = kv->v_scale;
   a.k_scale_out = const_cast<float*>(kv->k_scale);
   a.v_scale_out = const_cast<float*>(kv->v_scale);
+  a.index_scale_out = index_k_new ? index_k_scale : nullptr;
   a.num_tokens = num_tokens;
   a.num_pages = kv->num_pages;
   a.num_kv_heads = kv->num_kv_heads;

@@ -14,6 +14,9 @@
 // s = max|x| / 448 over the token-head's 128 values (1 for an all-zero row),
 // code = e4m3fn RNE of clamp(x / s, -448, 448); a scalar scale is read, not
 // written; bf16 caches store bf16 RNE of x / s with s = 1 unless scalar.
+// An FP8 index cache (the optional FP8 index storage named on the vLLM PR
+// #54682 page, 相关 PRs) takes each token's index key by the per-token rule:
+// s = max|x| / 448 over its 128 values, codes e4m3fn RNE of clamp(x / s).
 #include "msa_internal.h"
 
 using namespace msa;
@@ -49,6 +52,20 @@ __device__ __forceinline__ uint32_t fp8_code(float x, float s) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false)) & 0xffu;
 }
 
+// Eight values of one row held by a lane whose 16-lane DPP row holds the
+// whole 128-value row: the row's per-token scale and the lane's eight codes.
+__device__ __forceinline__ u32x2 fp8_row_codes(const f32x8& x, float& s) {
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x.v[e]));
+  amax = max16(amax);
+  s = amax > 0.f ? amax / kE4m3Max : 1.f;
+  uint32_t code[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) code[e >> 2] |= fp8_code(x.v[e], s) << (8 * (e & 3));
+  return u32x2{code[0], code[1]};
+}
+
 // One token with one wave (decode: scattered slots).
 __device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int t, int lane) {
   const int c = lane & 15;
@@ -67,10 +84,20 @@ __device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int t, int 
   const int sub = kSubsPerPage * page + (off >> 4), j = off & (kSub - 1);
   const size_t sp = static_cast<size_t>(sub) * a.num_kv_heads;  // the head's sub-page
 
-  // index-K: a bf16 copy into the page's shuffled tile
-  if ((lane >> 4) == 1 && a.index_k_new) {
-    uint16_t* dst = a.index_k + static_cast<size_t>(page) * (kPage * kDim) + (off >> 4) * (kSub * kDim) + (c * 16 + j) * 8;
-    *reinterpret_cast<u32x4*>(dst) = iw;
+  // index-K: a bf16 copy into the page's shuffled tile, or fp8 codes and
+  // the token's scale (lanes 16..31 form one DPP row: the whole index row)
+  if (a.index_k_new) {
+    const size_t at = static_cast<size_t>(page) * (kPage * kDim) + (off >> 4) * (kSub * kDim) + (c * 16 + j) * 8;
+    if (a.index_scale_out) {
+      float s;
+      const u32x2 codes = fp8_row_codes(widen(iw), s);
+      if ((lane >> 4) == 1) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.index_k) + at) = codes;
+        if (c == 0) a.index_scale_out[static_cast<size_t>(page) * kPage + off] = s;
+      }
+    } else if ((lane >> 4) == 1) {
+      *reinterpret_cast<u32x4*>(a.index_k + at) = iw;
+    }
   }
   // K (lanes 0..15, dims 8c..8c+7): one contiguous run of the shuffled tile
   {
@@ -152,7 +179,16 @@ __device__ __forceinline__ void insert_subpage(const MsaInsertArgs& a, int t0, i
         reinterpret_cast<uint16_t*>(dst)[at] = f32_to_bf16(x.v[e] / s);
     }
   }
-  if (a.index_k_new) *reinterpret_cast<u32x4*>(is + (c * 16 + j) * 8) = iw;
+  if (a.index_k_new) {
+    if (a.index_scale_out) {  // fp8 index: per-token scale over the DPP row holding token j
+      float s;
+      const u32x2 codes = fp8_row_codes(widen(iw), s);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(is) + (c * 16 + j) * 8) = codes;
+      if (c == 0) a.index_scale_out[static_cast<size_t>(page) * kPage + (slot0 & (kPage - 1)) + j] = s;
+    } else {
+      *reinterpret_cast<u32x4*>(is + (c * 16 + j) * 8) = iw;
+    }
+  }
   __syncthreads();
   // each plane of the sub-page as one contiguous run: 16 bytes per thread
   const int per = kv_bytes / 16;  // 16-byte pieces per plane (128 or 256)
@@ -162,9 +198,14 @@ __device__ __forceinline__ void insert_subpage(const MsaInsertArgs& a, int t0, i
     reinterpret_cast<u32x4*>(static_cast<uint8_t*>(a.v_cache) + static_cast<size_t>(sub) * kv_bytes)[i] =
         reinterpret_cast<const u32x4*>(vs)[i];
   }
-  if (a.index_k_new)
-    reinterpret_cast<u32x4*>(a.index_k + static_cast<size_t>(page) * (kPage * kDim) +
-                             ((slot0 & (kPage - 1)) >> 4) * (kSub * kDim))[tid] = reinterpret_cast<const u32x4*>(is)[tid];
+  if (a.index_k_new) {
+    // the index tile: 4 KiB of bf16 (256 pieces) or 2 KiB of codes (128)
+    const int ibytes = a.index_scale_out ? 1 : 2;
+    uint8_t* idst = reinterpret_cast<uint8_t*>(a.index_k) +
+                    (static_cast<size_t>(page) * (kPage * kDim) + ((slot0 & (kPage - 1)) >> 4) * (kSub * kDim)) * ibytes;
+    if (tid < kSub * kDim * ibytes / 16)
+      reinterpret_cast<u32x4*>(idst)[tid] = reinterpret_cast<const u32x4*>(is)[tid];
+  }
 }
 
 // Workgroup = 16 consecutive tokens. When their slots are one whole sub-page

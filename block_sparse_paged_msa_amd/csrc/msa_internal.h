@@ -161,7 +161,8 @@ hipError_t msa_launch_meta(const MsaMetaArgs& a, hipStream_t s);
 
 struct MsaScoreArgs {
   const uint16_t* index_q;
-  const uint16_t* index_k;
+  const void* index_k;        // bf16 keys, or e4m3fn codes when index_scale is set
+  const float* index_scale;   // [P][128] per-token scales of an fp8 index cache, or null
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* query_lens;
@@ -251,6 +252,7 @@ struct MsaInsertArgs {
   const float* v_scale;
   float* k_scale_out;            // per-token-head mode: [8P][16][Hkv], written
   float* v_scale_out;
+  float* index_scale_out;        // [P][128]: the index cache is fp8 and these scales are written; null: bf16
   int32_t num_tokens;
   int32_t num_pages;
   int32_t num_kv_heads;

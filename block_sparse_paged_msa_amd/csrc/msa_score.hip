@@ -23,6 +23,14 @@
 // with every 16-row tile of the group's index queries (the A operand), so the
 // page is shared by all of the request's rows in the group. The max over the
 // block's visible tokens is taken on the MFMA output, per row.
+//
+// An FP8 index cache (the optional FP8 index storage named on the vLLM PR
+// #54682 page, 相关 PRs) holds e4m3fn codes in the same shuffled order, 16 KiB
+// a page, and one fp32 scale per token: the wave streams the codes (512 B
+// runs), widens them to bf16 in registers (exact), runs the same bf16 MFMA
+// and multiplies each token's dot product by its scale before the max.
+#include <type_traits>
+
 #include "msa_internal.h"
 
 using namespace msa;
@@ -38,24 +46,54 @@ struct Unit {
   bool valid;
 };
 
-// B operand of the page: column = token tt*16 + lane%16, K entries = dims
-// kc*32 + 8*(lane/16) .. +7. A page is 8 shuffled 16-token tiles
-// [4][4][16][8], so each (tt, kc) operand is one contiguous 1 KiB run.
-__device__ __forceinline__ void load_page(const MsaScoreArgs& a, int page, int lane, bf16x8 (&kb)[8][4]) {
-  const uint16_t* kp = a.index_k + static_cast<size_t>(page) * (kPage * kDim);
+// One index-K page in registers as the B operand: column = token
+// tt*16 + lane%16, K entries = dims kc*32 + 8*(lane/16) .. +7. A page is 8
+// shuffled 16-token tiles [4][4][16][8], so each (tt, kc) operand is one
+// contiguous run (1 KiB of bf16, or 512 B of fp8 codes).
+template <int IDX_FP8>
+struct IndexPage {
+  using Raw = typename std::conditional<IDX_FP8 != 0, u32x2, bf16x8>::type;
+  Raw k[8][4];
+  float sc[8];  // fp8: scale of token tt*16 + lane%16
+
+  __device__ __forceinline__ void load(const MsaScoreArgs& a, int page, int lane) {
+    const size_t elem0 = static_cast<size_t>(page) * (kPage * kDim);
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt)
+    for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      kb[tt][kc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kp + tt * (kSub * kDim) + (kc * 64 + lane) * 8));
-}
+      for (int kc = 0; kc < 4; ++kc) {
+        const size_t at = elem0 + tt * (kSub * kDim) + (kc * 64 + lane) * 8;
+        if constexpr (IDX_FP8 != 0)
+          k[tt][kc] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(a.index_k) + at));
+        else
+          k[tt][kc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.index_k) + at));
+      }
+    if constexpr (IDX_FP8 != 0) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) sc[tt] = a.index_scale[static_cast<size_t>(page) * kPage + tt * kSub + (lane & 15)];
+    }
+  }
+  __device__ __forceinline__ bf16x8 op(int tt, int kc) const {
+    if constexpr (IDX_FP8 != 0) {
+      const u32x2 lo = fp8x4_to_bf16x4(k[tt][kc].x), hi = fp8x4_to_bf16x4(k[tt][kc].y);
+      return __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
+    } else {
+      return k[tt][kc];
+    }
+  }
+  __device__ __forceinline__ float scale(int tt) const {
+    if constexpr (IDX_FP8 != 0) return sc[tt];
+    else return 1.f;
+  }
+};
 
 __device__ __forceinline__ int page_of(const MsaScoreArgs& a, const Unit& w) {
   return clampi(a.block_table[static_cast<size_t>(w.r) * a.ld_bt + w.j], 0, a.num_pages - 1);
 }
 
 // Scores of one unit once its page is in registers; q0 is the request's first row.
-__device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const Unit& w, int q0, const bf16x8 (&kb)[8][4],
+template <int IDX_FP8>
+__device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const Unit& w, int q0, const IndexPage<IDX_FP8>& kb,
                                            int lane) {
   const int g0 = w.g * kRowsPerUnit;
   const int nrows = min(kRowsPerUnit, w.ql - g0);
@@ -79,13 +117,14 @@ __device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const Unit& w,
     for (int tt = 0; tt < 8; ++tt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) acc = mfma_16x16x32(qa[kc], kb[tt][kc], acc);
+      for (int kc = 0; kc < 4; ++kc) acc = mfma_16x16x32(qa[kc], kb.op(tt, kc), acc);
       const int t = t_base + tt * 16;
+      const float sc = kb.scale(tt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + 4 * (lane >> 4) + i;
         const bool visible = (m < nrows) && (t <= pos0 + m);
-        mx[i] = fmaxf(mx[i], visible ? acc[i] : -INFINITY);
+        mx[i] = fmaxf(mx[i], visible ? acc[i] * sc : -INFINITY);
       }
     }
 #pragma unroll
@@ -141,6 +180,7 @@ __device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_e
   return w;
 }
 
+template <int IDX_FP8>
 __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a) {
   extern __shared__ int s_dyn[];  // [R+1] row prefix, [R+1] extra-group prefix
   __shared__ int s_tot[kWavesPerWg][5];
@@ -157,14 +197,14 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   // Decode-only launches (at most 64 rows in all, so no request has a row
   // group past the first) with no metadata to write need no prefix: a wave
   // sums query_lens below its request itself and never waits on a barrier.
-  bf16x8 kb[8][4];
+  IndexPage<IDX_FP8> kb;
   if (!writer && a.num_rows <= kRowsPerUnit) {
     for (; u < slots_a; u += nwaves) {
       const Unit w = slot_unit(a, u);
       if (!w.valid) continue;
       int q0 = 0;
       for (int r = lane; r < w.r; r += 64) q0 += clampi(a.query_lens[r], 0, clampi(a.seq_lens[r], 0, a.len_cap));
-      load_page(a, page_of(a, w), lane, kb);
+      kb.load(a, page_of(a, w), lane);
       q0 = __builtin_amdgcn_readlane(wave_inclusive_scan(q0), 63);
       score_unit(a, w, q0, kb, lane);
     }
@@ -176,7 +216,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   const bool first_is_a = u < slots_a;
   if (first_is_a) {
     w0 = slot_unit(a, u);
-    if (w0.valid) load_page(a, page_of(a, w0), lane, kb);
+    if (w0.valid) kb.load(a, page_of(a, w0), lane);
   }
 
   // running sums over the requests of (query rows, KV tokens, blocks, score
@@ -260,7 +300,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   for (; u < total; u += nwaves) {
     const Unit w = u < slots_a ? slot_unit(a, u) : extra_unit(a, s_extra, s_cuq, u - slots_a);
     if (!w.valid) continue;
-    load_page(a, page_of(a, w), lane, kb);
+    kb.load(a, page_of(a, w), lane);
     score_unit(a, w, s_cuq[w.r], kb, lane);
   }
 }
@@ -269,6 +309,9 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
 
 hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s) {
   const size_t lds = sizeof(int) * 2 * static_cast<size_t>(a.num_reqs + 1);
-  hipLaunchKernelGGL(msa_score_kernel, dim3(num_wgs), dim3(kScoreThreads), lds, s, a);
+  if (a.index_scale)
+    hipLaunchKernelGGL(msa_score_kernel<1>, dim3(num_wgs), dim3(kScoreThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(msa_score_kernel<0>, dim3(num_wgs), dim3(kScoreThreads), lds, s, a);
   return hipGetLastError();
 }

@@ -218,11 +218,20 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
                              size_t workspace_bytes);
 
 /*
- * msa_sparse_paged_attn_lse / msa_sparse_decode_lse — the same two operations
- * with two optional extras (#54404 page, 实现拆解 item 1: a decode operator
- * that also returns the natural-log LSE, for merging partial attention;
- * item 2: one learnable float32 sink per query head). Arguments as in
- * msa_sparse_paged_attn / msa_sparse_decode, plus:
+ * The _ex entry points — the same operations with optional extras; each plain
+ * entry point is its _ex form with every extra NULL.
+ *
+ * FP8 index cache (index_k_scale != NULL; the optional FP8 index storage and
+ * FP8 decode scoring named on the #54682 page, 相关 PRs): index_k then holds
+ * e4m3fn codes [P][8][4][4][16][8] u8 (the bf16 layout, one byte per value:
+ * 16 KiB a page) and index_k_scale [P][128] fp32 one scale per token slot;
+ * token t's key is index_k_scale[page][t%128] * e4m3fn(code). The index query
+ * stays bf16; each token's score is its scale times the dot product of the
+ * query with the codes' values (exact bf16 products, fp32 sum).
+ *
+ * Sinks and LSE (#54404 page, 实现拆解 item 1: a decode operator that also
+ * returns the natural-log LSE, for merging partial attention; item 2: one
+ * learnable float32 sink per query head):
  *   sinks [num_q_heads] fp32 (device), or NULL: head h's softmax denominator
  *     gains exp(sinks[h]) — a logit with no value vector —
  *       out[n][h] = sum_u e^{z_u} V-hat_u / (e^{sinks[h]} + sum_u e^{z_u}),
@@ -231,22 +240,24 @@ msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const 
  *     ln sum_u e^{z_u} over the attended tokens; the sink is not included, so
  *     partial results over disjoint token sets can be merged with it and a
  *     sink applied once afterwards. Rows with ctx 0 get -inf (and zero output).
- * The plain entry points are these with sinks = lse = NULL. No extra
- * workspace; errors as for the plain entry points.
+ * No extra workspace; errors as for the plain entry points.
  */
-msa_status msa_sparse_paged_attn_lse(msa_stream_t stream, const void* q, int32_t num_rows,
-                                     int32_t num_q_heads, const msa_kv* kv,
-                                     const int32_t* sparse_table, int32_t ld_table,
-                                     const int32_t* ctx_lens, int32_t max_ctx, float sm_scale,
-                                     const float* sinks, void* out, float* lse, void* workspace,
-                                     size_t workspace_bytes);
-msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, const void* index_q,
-                                 const void* index_k, const void* q, int32_t num_q_heads,
-                                 const msa_kv* kv, int32_t topk, float sm_scale,
-                                 const float* sinks, void* out, float* lse,
-                                 int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
-                                 float* block_scores, int32_t ld_s, void* workspace,
-                                 size_t workspace_bytes);
+msa_status msa_index_score_ex(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                              const void* index_k, const float* index_k_scale,
+                              float* block_scores, int32_t ld_s);
+msa_status msa_sparse_paged_attn_ex(msa_stream_t stream, const void* q, int32_t num_rows,
+                                    int32_t num_q_heads, const msa_kv* kv,
+                                    const int32_t* sparse_table, int32_t ld_table,
+                                    const int32_t* ctx_lens, int32_t max_ctx, float sm_scale,
+                                    const float* sinks, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes);
+msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                                const void* index_k, const float* index_k_scale, const void* q,
+                                int32_t num_q_heads, const msa_kv* kv, int32_t topk,
+                                float sm_scale, const float* sinks, void* out, float* lse,
+                                int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
+                                float* block_scores, int32_t ld_s, void* workspace,
+                                size_t workspace_bytes);
 
 /*
  * msa_cache_insert — the step before the path: writes new tokens' K, V and
@@ -276,6 +287,18 @@ msa_status msa_sparse_decode_lse(msa_stream_t stream, const msa_batch* batch, co
 msa_status msa_cache_insert(msa_stream_t stream, int32_t num_tokens, const int32_t* slot_mapping,
                             const void* k_new, const void* v_new, const msa_kv* kv,
                             const void* index_k_new, void* index_k);
+/*
+ * msa_cache_insert_ex — msa_cache_insert with index_k_scale [P][128] fp32:
+ * when it is non-NULL (and index_k_new is given) the index cache is the FP8
+ * one described above, and each token's index key is stored by the
+ * per-token rule s = max|x| / 448 over its 128 values (1 for an all-zero
+ * row), codes e4m3fn RNE of clamp(x / s, -448, 448), s written to
+ * index_k_scale[page][offset]. NULL: the bf16 copy of msa_cache_insert.
+ */
+msa_status msa_cache_insert_ex(msa_stream_t stream, int32_t num_tokens,
+                               const int32_t* slot_mapping, const void* k_new, const void* v_new,
+                               const msa_kv* kv, const void* index_k_new, void* index_k,
+                               float* index_k_scale);
 
 /*
  * msa_workspace_bytes — workspace needed by msa_sparse_paged_attn (ld_s = 0)

@@ -277,7 +277,7 @@ def _fill(rng, name, seed, seq_lens, query_lens, topk, hq, kv_dtype, scale_mode,
 CONFIG_NAMES = ("tiny", "bf16_batch", "spec_decode", "fp8_kv", "mixed_prefill")
 
 
-def config(name: str, *, scale_mode: int | None = None) -> Batch:
+def config(name: str, *, scale_mode: int | None = None, index_dtype: int = INDEX_BF16) -> Batch:
     """The named workload with its fixed seed.
 
     tiny          1 request, 1 row, L=2048, identity pages, top-k 4, 8 q heads (seed 0)
@@ -287,33 +287,35 @@ def config(name: str, *, scale_mode: int | None = None) -> Batch:
                   per-token-head scales U[0.5,2] (or one scalar pair), top-k 64 (seed 3)
     mixed_prefill 6 decode rows at L=16384 then 2 prefill requests of 4096 rows on
                   28672 prior tokens (L=32768), top-k 32 (seed 4)
+    ``index_dtype=INDEX_FP8`` gives any of them an fp8 index cache (codes from
+    the same normals, per-token scales drawn last).
     """
     if name == "tiny":
         rng = SplitMix64(0)
         return _fill(rng, name, 0, np.array([2048], np.int32), np.array([1], np.int32), 4, 8,
-                     KV_BF16, SCALE_NONE, False, 2048, 0.5, 2.0, 1, 0, None)
+                     KV_BF16, SCALE_NONE, False, 2048, 0.5, 2.0, 1, 0, None, index_dtype=index_dtype)
     if name == "bf16_batch":
         rng = SplitMix64(1)
         L = rng.integers(8192, 32768, 8).astype(np.int32)
         return _fill(rng, name, 1, L, np.ones(8, np.int32), 16, 16, KV_BF16, SCALE_NONE,
-                     True, 32768, 0.5, 2.0, 1, 0, None)
+                     True, 32768, 0.5, 2.0, 1, 0, None, index_dtype=index_dtype)
     if name == "spec_decode":
         rng = SplitMix64(2)
         L = np.full(4, 65536, np.int32)
         return _fill(rng, name, 2, L, np.full(4, 4, np.int32), 32, 16, KV_BF16, SCALE_NONE,
-                     True, 65536, 0.5, 2.0, 1, 0, None)
+                     True, 65536, 0.5, 2.0, 1, 0, None, index_dtype=index_dtype)
     if name == "fp8_kv":
         rng = SplitMix64(3)
         L = rng.integers(32768, 131072, 11).astype(np.int32)
         sm = SCALE_PER_TOKEN_HEAD if scale_mode is None else scale_mode
         return _fill(rng, name, 3, L, np.ones(11, np.int32), 64, 16, KV_FP8, sm,
-                     True, 131072, 0.5, 2.0, 1, 0, None)
+                     True, 131072, 0.5, 2.0, 1, 0, None, index_dtype=index_dtype)
     if name == "mixed_prefill":
         rng = SplitMix64(4)
         L = np.array([16384] * 6 + [32768] * 2, np.int32)
         ql = np.array([1] * 6 + [4096] * 2, np.int32)
         return _fill(rng, name, 4, L, ql, 32, 16, KV_BF16, SCALE_NONE,
-                     True, 32768, 0.5, 2.0, 1, 0, None)
+                     True, 32768, 0.5, 2.0, 1, 0, None, index_dtype=index_dtype)
     raise KeyError(name)
 
 

@@ -56,6 +56,7 @@ class DeviceBatch:
     v_scale: torch.Tensor | None
     cbatch: msa.MsaBatch = None
     ckv: msa.MsaKV = None
+    index_scale: torch.Tensor | None = None   # set for an fp8 index cache
 
 
 def upload(b: syn.Batch, device="cuda") -> DeviceBatch:
@@ -76,6 +77,8 @@ def upload(b: syn.Batch, device="cuda") -> DeviceBatch:
     d.cbatch = msa.make_batch(d.seq_lens, d.query_lens, d.block_table, d.cu_q, d.cu_k, d.cu_blocks,
                               d.cu_units, d.row_req, d.row_pos, R, N, b.max_seq_len, b.num_pages)
     d.ckv = msa.make_kv(d.k_cache, d.v_cache, b.kv_dtype, b.scale_mode, b.num_pages, d.k_scale, d.v_scale)
+    if b.index_scale is not None:
+        d.index_scale = dev(b.index_scale, device)
     return d
 
 
@@ -98,7 +101,10 @@ def run_metadata(d: DeviceBatch) -> dict:
 def run_scores(d: DeviceBatch) -> np.ndarray:
     b = d.host
     full, scores = guarded(b.num_rows * b.ld_s, torch.float32, SENTINEL_F32)
-    msa.msa_index_score(d.cbatch, d.index_q, d.index_k, scores, b.ld_s)
+    if d.index_scale is None:
+        msa.msa_index_score(d.cbatch, d.index_q, d.index_k, scores, b.ld_s)
+    else:
+        msa.msa_index_score_ex(d.cbatch, d.index_q, d.index_k, d.index_scale, scores, b.ld_s)
     assert guards_intact(full, SENTINEL_F32), "index score wrote outside its buffer"
     return scores.view(b.num_rows, b.ld_s).cpu().numpy()
 
@@ -165,13 +171,18 @@ def alloc_decode(d: DeviceBatch, with_scores: bool = True) -> DecodeOut:
 
 def run_decode(d: DeviceBatch, o: DecodeOut, with_scores: bool = True) -> None:
     b = d.host
-    msa.msa_sparse_decode(d.cbatch, d.index_q, d.index_k, d.q, b.num_q_heads, d.ckv, b.topk, b.sm_scale,
-                          o.out, o.table, o.ctx, o.sel, o.scores if with_scores else None, b.ld_s, o.ws, o.wsb)
+    if d.index_scale is None:
+        msa.msa_sparse_decode(d.cbatch, d.index_q, d.index_k, d.q, b.num_q_heads, d.ckv, b.topk, b.sm_scale,
+                              o.out, o.table, o.ctx, o.sel, o.scores if with_scores else None, b.ld_s, o.ws, o.wsb)
+    else:
+        msa.msa_sparse_decode_ex(d.cbatch, d.index_q, d.index_k, d.index_scale, d.q, b.num_q_heads, d.ckv, b.topk,
+                                 b.sm_scale, None, o.out, None, o.table, o.ctx, o.sel,
+                                 o.scores if with_scores else None, b.ld_s, o.ws, o.wsb)
 
 
 def run_attn_lse(d: DeviceBatch, table: np.ndarray, ctx: np.ndarray, sinks: np.ndarray | None,
                  max_ctx: int | None = None):
-    """msa_sparse_paged_attn_lse on a given table; returns (out, lse)."""
+    """msa_sparse_paged_attn_ex on a given table; returns (out, lse)."""
     b = d.host
     N, hq = b.num_rows, b.num_q_heads
     ld_table = table.shape[1]
@@ -183,18 +194,18 @@ def run_attn_lse(d: DeviceBatch, table: np.ndarray, ctx: np.ndarray, sinks: np.n
     lfull, lse = guarded(N * hq, torch.float32, SENTINEL_F32)
     wsb = msa.msa_workspace_bytes(N, hq, max_ctx, 0)
     ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
-    msa.msa_sparse_paged_attn_lse(d.q, N, hq, d.ckv, t, ld_table, c, max_ctx, b.sm_scale, s, out, lse, ws, wsb)
+    msa.msa_sparse_paged_attn_ex(d.q, N, hq, d.ckv, t, ld_table, c, max_ctx, b.sm_scale, s, out, lse, ws, wsb)
     assert guards_intact(ofull, SENTINEL_U16), "attention wrote outside its output"
     assert guards_intact(lfull, SENTINEL_F32), "attention wrote outside its lse"
     return bf16_to_np(out.view(N, hq, 128)), lse.view(N, hq).cpu().numpy().astype(np.float64)
 
 
 def run_decode_lse(d: DeviceBatch, o: DecodeOut, sinks: np.ndarray | None) -> np.ndarray:
-    """msa_sparse_decode_lse into o; returns the lse [N][Hq]."""
+    """msa_sparse_decode_ex into o (with the batch's index cache); returns the lse [N][Hq]."""
     b = d.host
     s = None if sinks is None else torch.from_numpy(np.ascontiguousarray(sinks, dtype=np.float32)).cuda()
     lfull, lse = guarded(b.num_rows * b.num_q_heads, torch.float32, SENTINEL_F32)
-    msa.msa_sparse_decode_lse(d.cbatch, d.index_q, d.index_k, d.q, b.num_q_heads, d.ckv, b.topk, b.sm_scale, s,
-                              o.out, lse, o.table, o.ctx, o.sel, o.scores, b.ld_s, o.ws, o.wsb)
+    msa.msa_sparse_decode_ex(d.cbatch, d.index_q, d.index_k, d.index_scale, d.q, b.num_q_heads, d.ckv, b.topk,
+                             b.sm_scale, s, o.out, lse, o.table, o.ctx, o.sel, o.scores, b.ld_s, o.ws, o.wsb)
     assert guards_intact(lfull, SENTINEL_F32), "decode wrote outside its lse"
     return lse.view(b.num_rows, b.num_q_heads).cpu().numpy().astype(np.float64)

@@ -26,8 +26,9 @@ def lib():
 def test_header_declares_the_path_entry_points():
     names = header_functions()
     for want in ("msa_build_metadata", "msa_index_score", "msa_topk_block_table",
-                 "msa_sparse_paged_attn", "msa_sparse_decode", "msa_sparse_paged_attn_lse",
-                 "msa_sparse_decode_lse", "msa_cache_insert", "msa_workspace_bytes"):
+                 "msa_sparse_paged_attn", "msa_sparse_decode", "msa_index_score_ex",
+                 "msa_sparse_paged_attn_ex", "msa_sparse_decode_ex", "msa_cache_insert",
+                 "msa_cache_insert_ex", "msa_workspace_bytes"):
         assert want in names
 
 
@@ -69,7 +70,7 @@ def _no_gpu_for_fake_pointers(request):
     # run where no GPU is visible
     if request.node.name.startswith(("test_metadata_rejects", "test_index_score", "test_topk_rejects",
                                      "test_attention_rejects", "test_empty_calls", "test_decode_rejects",
-                                     "test_insert_rejects", "test_lse_entry_points")):
+                                     "test_insert_rejects", "test_ex_entry_points")):
         import torch
         if torch.cuda.is_available():
             pytest.skip("fake device pointers are only passed where no GPU is visible")
@@ -178,26 +179,29 @@ def test_decode_rejects_before_launch():
     assert _code(msa.msa_sparse_decode, *bad) == msa.MSA_ERR_INVALID_ARG
 
 
-def test_lse_entry_points_check_like_the_plain_ones():
+def test_ex_entry_points_check_like_the_plain_ones():
     kv = _fake_kv()
     # attention: heads, table stride, workspace, empty call
-    assert _code(msa.msa_sparse_paged_attn_lse, 0x1, 4, 200, kv, 0x2, 8, 0x3, 128, 0.1, 0x9, 0x4, 0xA, 0x5,
+    assert _code(msa.msa_sparse_paged_attn_ex, 0x1, 4, 200, kv, 0x2, 8, 0x3, 128, 0.1, 0x9, 0x4, 0xA, 0x5,
                  1 << 20, 0) == msa.MSA_ERR_UNSUPPORTED
-    assert _code(msa.msa_sparse_paged_attn_lse, 0x1, 4, 16, kv, 0x2, 7, 0x3, 128, 0.1, 0x9, 0x4, 0xA, 0x5,
+    assert _code(msa.msa_sparse_paged_attn_ex, 0x1, 4, 16, kv, 0x2, 7, 0x3, 128, 0.1, 0x9, 0x4, 0xA, 0x5,
                  1 << 20, 0) == msa.MSA_ERR_INVALID_ARG
     need = msa.msa_workspace_bytes(4, 16, 4096, 0)
-    assert _code(msa.msa_sparse_paged_attn_lse, 0x1, 4, 16, kv, 0x2, 256, 0x3, 4096, 0.1, 0x9, 0x4, 0xA, 0x5,
+    assert _code(msa.msa_sparse_paged_attn_ex, 0x1, 4, 16, kv, 0x2, 256, 0x3, 4096, 0.1, 0x9, 0x4, 0xA, 0x5,
                  need - 1, 0) == msa.MSA_ERR_WORKSPACE
-    assert _code(msa.msa_sparse_paged_attn_lse, 0x1, 0, 16, kv, 0x2, 8, 0x3, 128, 0.1, 0x9, 0x4, 0xA, 0, 0,
+    assert _code(msa.msa_sparse_paged_attn_ex, 0x1, 0, 16, kv, 0x2, 8, 0x3, 128, 0.1, 0x9, 0x4, 0xA, 0, 0,
                  0) == 0
     # decode: top-k, ld_s, workspace
     b = _fake_batch()
-    args = [b, 0x1, 0x2, 0x3, 16, kv, 4, 0.1, 0x9, 0x4, 0xA, 0x5, 0x6, None, None, 4, 0x7, 1 << 30, 0]
-    for idx, val, expect in ((6, 0, msa.MSA_ERR_INVALID_ARG), (15, 2, msa.MSA_ERR_UNSUPPORTED),
-                             (17, 16, msa.MSA_ERR_WORKSPACE)):
+    args = [b, 0x1, 0x2, 0xB, 0x3, 16, kv, 4, 0.1, 0x9, 0x4, 0xA, 0x5, 0x6, None, None, 4, 0x7, 1 << 30, 0]
+    for idx, val, expect in ((7, 0, msa.MSA_ERR_INVALID_ARG), (16, 2, msa.MSA_ERR_UNSUPPORTED),
+                             (18, 16, msa.MSA_ERR_WORKSPACE)):
         bad = list(args)
         bad[idx] = val
-        assert _code(msa.msa_sparse_decode_lse, *bad) == expect
+        assert _code(msa.msa_sparse_decode_ex, *bad) == expect
+    # index scores: ld_s too small; insert: index rows with no index cache
+    assert _code(msa.msa_index_score_ex, b, 0x1, 0x2, 0xB, 0x3, 2, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert _code(msa.msa_cache_insert_ex, 4, 0x1, 0x2, 0x3, kv, 0x4, 0, 0xB, 0) == msa.MSA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("args,kv,expect", [

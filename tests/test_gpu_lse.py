@@ -1,5 +1,5 @@
 """GPU parity of the natural-log LSE output and the per-head sinks
-(msa_sparse_paged_attn_lse / msa_sparse_decode_lse through the C ABI) with the
+(msa_sparse_paged_attn_ex / msa_sparse_decode_ex through the C ABI) with the
 oracle run on the device's own table and context lengths.
 
 Bars: outputs as for plain attention (2e-2 absolute for bf16 K/V, 6e-2 for

@@ -31,7 +31,8 @@ def atol_for(b):
 
 
 def check_scores(b, gpu, rows):
-    ref = O.block_scores(b.index_q, b.index_k, b.block_table, b.seq_lens, b.query_lens, b.ld_s, rows=rows)
+    ref = O.block_scores(b.index_q, b.index_k, b.block_table, b.seq_lens, b.query_lens, b.ld_s, rows=rows,
+                         index_scale=b.index_scale)
     meta = O.build_metadata(b.seq_lens, b.query_lens)
     for n in rows:
         nb = O.num_blocks(O.visible_keys(meta["row_pos"][n]))
@@ -423,8 +424,8 @@ def test_physical_page_permutation_changes_no_output_bit(gpu_lib):
 # the five workloads at full size
 # ---------------------------------------------------------------------------
 @functools.lru_cache(maxsize=1)
-def _config(name, scale_mode):
-    return syn.config(name, scale_mode=scale_mode)
+def _config(name, scale_mode, index_dtype=syn.INDEX_BF16):
+    return syn.config(name, scale_mode=scale_mode, index_dtype=index_dtype)
 
 
 def _sample_rows(b, k, seed):
@@ -442,13 +443,17 @@ def _sample_rows(b, k, seed):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name,scale_mode", [
-    ("tiny", None), ("bf16_batch", None), ("spec_decode", None),
-    ("fp8_kv", syn.SCALE_PER_TOKEN_HEAD), ("fp8_kv", syn.SCALE_SCALAR), ("mixed_prefill", None),
+@pytest.mark.parametrize("name,scale_mode,index_dtype", [
+    ("tiny", None, 0), ("bf16_batch", None, 0), ("spec_decode", None, 0),
+    ("fp8_kv", syn.SCALE_PER_TOKEN_HEAD, 0), ("fp8_kv", syn.SCALE_SCALAR, 0), ("mixed_prefill", None, 0),
+    # the same workloads on an fp8 index cache
+    ("bf16_batch", None, syn.INDEX_FP8), ("fp8_kv", syn.SCALE_PER_TOKEN_HEAD, syn.INDEX_FP8),
+    ("mixed_prefill", None, syn.INDEX_FP8),
 ])
-def test_workload_parity(gpu_lib, name, scale_mode):
-    b = _config(name, scale_mode)
-    print(f"[workload] {name} scale_mode={scale_mode} rows={b.num_rows} pages={b.num_pages}", flush=True)
+def test_workload_parity(gpu_lib, name, scale_mode, index_dtype):
+    b = _config(name, scale_mode, index_dtype)
+    print(f"[workload] {name} scale_mode={scale_mode} index_dtype={index_dtype} rows={b.num_rows} "
+          f"pages={b.num_pages}", flush=True)
     d = H.upload(b)
     o = H.alloc_decode(d)
     H.run_decode(d, o)
