@@ -1,11 +1,12 @@
 """Throughput of the fused block-sparse paged decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--index bf16|fp8]
 
 One step = metadata -> index score + pooling -> top-k + page-16 table + ctx ->
 sparse paged attention + split merge (msa_sparse_decode) over one batch of the
 named synthetic workload (default: 8 requests x 1 row, L ~ U{8192..32768},
-top-k 16, 16 query heads, bf16). The step's inputs live in HBM; several copies
+top-k 16, 16 query heads, bf16; --index fp8 stores the index keys as e4m3fn
+codes with per-token scales). The step's inputs live in HBM; several copies
 of the caches at different addresses are cycled so that no step finds the
 previous step's data in the 256 MB Infinity Cache. Steps are replayed from a
 HIP graph holding one step per copy. Prints one JSON line.
@@ -41,6 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="bf16_batch", choices=sorted(WORKLOAD_DESC))
+    p.add_argument("--index", default="bf16", choices=("bf16", "fp8"),
+                   help="index cache: bf16 keys, or e4m3fn codes with one fp32 scale per token")
     p.add_argument("--copies", type=int, default=0, help="cache copies cycled (0: enough for 768 MB)")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,13 +63,14 @@ TRAFFIC_FILE = "index_score_traffic_{}.json"
 
 def algorithmic_bytes(b, ctx):
     """Minimum HBM bytes of one step and of its index-score launch.
-    index-K: every visible token of every request once (128 bf16 = 256 B);
+    index-K: every visible token of every request once (128 bf16 = 256 B, or
+    128 e4m3fn codes + a 4-byte scale = 132 B);
     K/V: each row's ctx tokens (K and V rows of 128 elements, plus per-token
     scales); q/out/index_q once; scores, tables, ctx and metadata."""
     import numpy as np
     N, hq, ld_s, topk = b.num_rows, b.num_q_heads, b.ld_s, b.topk
     elt = 2 if b.kv_dtype == 0 else 1
-    idx_k = int(b.seq_lens.astype(np.int64).sum()) * 256
+    idx_k = int(b.seq_lens.astype(np.int64).sum()) * (256 if b.index_scale is None else 132)
     score_launch = idx_k + N * 256 + N * ld_s * 4
     kv_tok = 2 * 128 * elt + (8 if b.scale_mode == 2 else 0)
     kv = int(np.asarray(ctx, dtype=np.int64).sum()) * kv_tok
@@ -159,10 +163,10 @@ def main():
         sys.exit(2)
 
     if args.summarize_counters:
-        summarize_counters(args.workload, *args.summarize_counters)
+        summarize_counters(args.workload, args.index, *args.summarize_counters)
         return
     if args.summarize_trace:
-        summarize_trace(args.workload, args.summarize_trace)
+        summarize_trace(args.workload, args.index, args.summarize_trace)
         return
 
     import numpy as np
@@ -173,9 +177,10 @@ def main():
 
     torch.cuda.set_device(0)
     msa.load()
-    b = syn.config(args.workload)
+    idx_fp8 = args.index == "fp8"
+    b = syn.config(args.workload, index_dtype=syn.INDEX_FP8 if idx_fp8 else syn.INDEX_BF16)
     N, R, P, hq, topk, ld_s = b.num_rows, b.num_reqs, b.num_pages, b.num_q_heads, b.topk, b.ld_s
-    per_copy = b.index_k.nbytes + b.k_cache.nbytes + b.v_cache.nbytes
+    per_copy = b.index_k.nbytes + b.k_cache.nbytes + b.v_cache.nbytes + (b.index_scale.nbytes if idx_fp8 else 0)
     copies = args.copies or max(2, math.ceil(768e6 / per_copy))
     dev = "cuda"
 
@@ -191,6 +196,7 @@ def main():
         return out.view((copies * one.shape[0],) + tuple(one.shape[1:]))
 
     index_k = pool(b.index_k)
+    index_scale = pool(b.index_scale) if idx_fp8 else None
     k_cache = pool(b.k_cache)
     v_cache = pool(b.v_cache)
     k_scale = v_scale = None
@@ -220,8 +226,15 @@ def main():
     ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
 
     def step(c):
-        msa.msa_sparse_decode(batches[c], index_q, index_k, q, hq, kv, topk, b.sm_scale, out, table, ctx,
-                              None, scores, ld_s, ws, wsb)
+        if idx_fp8:
+            msa.msa_sparse_decode_ex(batches[c], index_q, index_k, index_scale, q, hq, kv, topk, b.sm_scale, None,
+                                     out, None, table, ctx, None, scores, ld_s, ws, wsb)
+        else:
+            msa.msa_sparse_decode(batches[c], index_q, index_k, q, hq, kv, topk, b.sm_scale, out, table, ctx,
+                                  None, scores, ld_s, ws, wsb)
+
+    def score(c):
+        msa.msa_index_score_ex(batches[c], index_q, index_k, index_scale, scores, ld_s)
 
     for c in range(copies):
         step(c)
@@ -235,7 +248,7 @@ def main():
             torch.mul(src, 1, out=dst)   # an elementwise kernel: reads and writes COPY_BYTES
         torch.cuda.synchronize()
         for i in range(8):
-            msa.msa_index_score(batches[i % copies], index_q, index_k, scores, ld_s)
+            score(i % copies)
         torch.cuda.synchronize()
         print(json.dumps({"counters_pass": args.workload, "copy_bytes": COPY_BYTES,
                           "score_algorithmic_bytes": algorithmic_bytes(b, ctx.cpu().numpy())["score"]}))
@@ -293,10 +306,10 @@ def main():
     gs.wait_stream(stream)
     g_score = torch.cuda.CUDAGraph()
     with torch.cuda.stream(gs):
-        msa.msa_index_score(batches[0], index_q, index_k, scores, ld_s)
+        score(0)
         with torch.cuda.graph(g_score, stream=gs):
             for i in range(reps):
-                msa.msa_index_score(batches[i % copies], index_q, index_k, scores, ld_s)
+                score(i % copies)
     stream.wait_stream(gs)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -311,7 +324,7 @@ def main():
 
     score_gbps = nbytes["score"] / (t_score * 1e-6) / 1e9
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(args.workload))
+    tpath = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(tag(args.workload, args.index)))
     if os.path.exists(tpath):
         try:
             tj = json.load(open(tpath))
@@ -333,7 +346,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if b.kv_dtype == 0 else "fp8-kv/bf16",
         "data": "synthetic (seeded splitmix64 N(0,1) values, random page permutation)",
-        "config": {"workload": WORKLOAD_DESC[args.workload], "requests": R, "rows": N, "top_k": topk,
+        "config": {"workload": WORKLOAD_DESC[args.workload] + (
+                       ", fp8 e4m3fn index keys + per-token scales" if idx_fp8 else ""),
+                   "requests": R, "rows": N, "top_k": topk,
                    "q_heads": hq, "kv_heads": 1, "head_dim": 128, "seq_lens_sum": int(b.seq_lens.sum()),
                    "cache_copies_cycled": copies, "graphs": not args.eager},
         "step_hbm_gbps": nbytes["step"] / sec / 1e9,
@@ -352,8 +367,8 @@ def main():
     lse = torch.empty((N, hq), dtype=torch.float32, device=dev)
 
     def step_lse(c):
-        msa.msa_sparse_decode_ex(batches[c], index_q, index_k, None, q, hq, kv, topk, b.sm_scale, sinks, out, lse,
-                                 table, ctx, None, scores, ld_s, ws, wsb)
+        msa.msa_sparse_decode_ex(batches[c], index_q, index_k, index_scale, q, hq, kv, topk, b.sm_scale, sinks,
+                                 out, lse, table, ctx, None, scores, ld_s, ws, wsb)
 
     def graph_us_per_step(fn):
         gs2 = torch.cuda.Stream()
@@ -398,9 +413,18 @@ def _counter_rows(d):
 
 
 PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <out> -o run -- "
-           "python3 -u bench.py --workload {workload} --counters")
+           "python3 -u bench.py --workload {workload}{index} --counters")
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- "
-             "python3 -u bench.py --workload {workload} --steps 50 --warmup 10 --no-cpu-baseline")
+             "python3 -u bench.py --workload {workload}{index} --steps 50 --warmup 10 --no-cpu-baseline")
+
+
+def tag(workload, index):
+    """File-name tag of a workload (and of its fp8-index variant)."""
+    return workload if index == "bf16" else f"{workload}_fp8index"
+
+
+def _index_flag(index):
+    return "" if index == "bf16" else f" --index {index}"
 
 
 def _short(name):
@@ -408,13 +432,14 @@ def _short(name):
     return name.split("(")[0]
 
 
-def summarize_counters(workload, fetch_dir, write_dir):
+def summarize_counters(workload, index, fetch_dir, write_dir):
     """Scale every kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what
     the same counter reads for the calibration kernel of the --counters pass
     (an elementwise multiply that reads and writes COPY_BYTES bytes). Writes
     the index-score kernel's traffic for bench.py and a per-kernel table."""
     import statistics
-    out = {"workload": workload, "kernel": "msa_score_kernel", "copy_bytes": COPY_BYTES,
+    name = tag(workload, index)
+    out = {"workload": name, "kernel": "msa_score_kernel", "copy_bytes": COPY_BYTES,
            "kernel_source_hash": source_hash()}
     table = {}
     total = 0.0
@@ -431,19 +456,22 @@ def summarize_counters(workload, fetch_dir, write_dir):
                 per.setdefault(_short(k), []).append(v)
         for k, vals in per.items():
             table.setdefault(k, {})[counter] = statistics.median(vals) * 1024.0 * factor
-        s_kib = statistics.median(per["msa_score_kernel"])
+        score_key = next(k for k in per if k.startswith("msa_score_kernel"))
+        s_kib = statistics.median(per[score_key])
         out[counter] = {"calibration_kib_per_dispatch": c_kib, "score_kib_per_dispatch": s_kib,
                         "scale_factor": factor, "score_bytes": s_kib * 1024.0 * factor}
         total += s_kib * 1024.0 * factor
     out["bytes_per_launch"] = total
     prof = os.path.join(ROOT, "profiles")
-    with open(os.path.join(prof, TRAFFIC_FILE.format(workload)), "w") as fh:
+    with open(os.path.join(prof, TRAFFIC_FILE.format(name)), "w") as fh:
         json.dump(out, fh, indent=1)
-    lines = [f"# HBM traffic per dispatch, {workload} workload", "",
+    fl = _index_flag(index)
+    lines = [f"# HBM traffic per dispatch, {name} workload", "",
              "Commands (one counter per run, outputs in <out>):", "",
-             "    " + PMC_CMD.format(counter="FETCH_SIZE", workload=workload),
-             "    " + PMC_CMD.format(counter="WRITE_SIZE", workload=workload),
-             "    python3 bench.py --workload {} --summarize-counters <fetch-out> <write-out>".format(workload), "",
+             "    " + PMC_CMD.format(counter="FETCH_SIZE", workload=workload, index=fl),
+             "    " + PMC_CMD.format(counter="WRITE_SIZE", workload=workload, index=fl),
+             "    python3 bench.py --workload {}{} --summarize-counters <fetch-out> <write-out>".format(workload, fl),
+             "",
              "Calibration: an elementwise multiply over {} MiB reads FETCH_SIZE {:.0f} KiB and WRITE_SIZE "
              "{:.0f} KiB per dispatch, so the counters are scaled by {:.3f} (fetch) and {:.3f} (write)."
              .format(COPY_BYTES >> 20, out["FETCH_SIZE"]["calibration_kib_per_dispatch"],
@@ -453,20 +481,21 @@ def summarize_counters(workload, fetch_dir, write_dir):
     for k, v in sorted(table.items()):
         lines.append(f"| {k} | {v.get('FETCH_SIZE', float('nan')) / 1e6:.3f} | {v.get('WRITE_SIZE', float('nan')) / 1e6:.3f} |")
     lines += ["", f"Kernel source hash (msa_score.hip + msa_internal.h): {out['kernel_source_hash']}"]
-    with open(os.path.join(prof, f"counters_{workload}.md"), "w") as fh:
+    with open(os.path.join(prof, f"counters_{name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(json.dumps(out))
 
 
-def summarize_trace(workload, trace_dir):
+def summarize_trace(workload, index, trace_dir):
     """Per-kernel duration table from a rocprofv3 --stats csv output."""
     import csv
     import glob
     f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not f:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
-    lines = [f"# Kernel durations, {workload} workload", "", "Command:", "",
-             "    " + TRACE_CMD.format(workload=workload), "",
+    name = tag(workload, index)
+    lines = [f"# Kernel durations, {name} workload", "", "Command:", "",
+             "    " + TRACE_CMD.format(workload=workload, index=_index_flag(index)), "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     with open(f[0]) as fh:
         for rec in csv.DictReader(fh):
@@ -474,7 +503,7 @@ def summarize_trace(workload, trace_dir):
                 continue
             lines.append(f"| {_short(rec['Name'])} | {rec['Calls']} | {float(rec['AverageNs']) / 1e3:.2f} | "
                          f"{float(rec['MinNs']) / 1e3:.2f} | {float(rec['MaxNs']) / 1e3:.2f} |")
-    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
 

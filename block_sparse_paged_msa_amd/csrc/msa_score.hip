@@ -75,7 +75,12 @@ struct IndexPage {
   }
   __device__ __forceinline__ bf16x8 op(int tt, int kc) const {
     if constexpr (IDX_FP8 != 0) {
-      const u32x2 lo = fp8x4_to_bf16x4(k[tt][kc].x), hi = fp8x4_to_bf16x4(k[tt][kc].y);
+      // widened where it is used: the empty asm keeps the compiler from
+      // hoisting all 32 widened operands (128 registers) out of the row loop,
+      // which leaves room for three waves per SIMD instead of two
+      u32x2 r = k[tt][kc];
+      asm volatile("" : "+v"(r));
+      const u32x2 lo = fp8x4_to_bf16x4(r.x), hi = fp8x4_to_bf16x4(r.y);
       return __builtin_bit_cast(bf16x8, (u32x4{lo.x, lo.y, hi.x, hi.y}));
     } else {
       return k[tt][kc];
