@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-decode query rows/sec + achieved HBM GB/s (% of MI355X peak)"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 WORKLOAD_DESC = {
     "tiny": "tiny decode: 1 request x 1 row, L=2048, top-k 4, 8 q heads / 1 kv head, bf16",
     "bf16_batch": "bf16 decode batch: 8 requests x 1 row, L~U{8192..32768}, permuted pages, top-k 16, "
@@ -358,6 +359,16 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},
     }
+    if (b.query_lens > 64).any():
+        # requests of more than 64 rows are scored by the MFMA tile kernel:
+        # 2 * 128 flops per (row, visible token) over every row of the launch
+        pos = b.seq_lens.astype(np.int64) - b.query_lens.astype(np.int64)
+        vis = sum(int(ql) * int(p0) + int(ql) * (int(ql) + 1) // 2 for p0, ql in zip(pos, b.query_lens))
+        tflops = 2 * 128 * vis / (t_score * 1e-6) / 1e12
+        res["score_mfma"] = {"kernels": "msa_score_kernel + msa_score_tile_kernel (one msa_index_score call)",
+                             "bound": "mfma", "algorithmic_flop": 2 * 128 * vis, "us_per_call": t_score,
+                             "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tflops / PEAK_BF16_TFLOPS}
     res["cache_insert"] = time_insert(msa, torch)
 
     # the same step through msa_sparse_decode_ex: LSE written, per-head sinks

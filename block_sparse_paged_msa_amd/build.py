@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.hip", "msa_meta.hip", "msa_score.hip", "msa_topk.hip", "msa_attn.hip", "msa_insert.hip"]
+SOURCES = ["msa_api.hip", "msa_meta.hip", "msa_score.hip", "msa_score_tile.hip", "msa_topk.hip", "msa_attn.hip",
+           "msa_insert.hip"]
 ARCH = "gfx950"
 
 

@@ -150,17 +150,25 @@ msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, 
   a.num_pages = b->num_pages;
   a.len_cap = len_cap(b);
   a.write_meta = write_meta ? 1 : 0;
-  a.xcd_remap = b->num_rows > kRowsPerUnit ? 1 : 0;
-  // first-group slots r*S + j, S = ceil(len_cap/128); extra row groups are at
-  // most S * floor(N/64) (sum_r (ceil(ql_r/64) - 1) <= N/64)
+  // a launch that may hold a request of more than 64 rows leaves such
+  // requests to the tile kernel, launched right after on the same stream
+  const bool tiles = b->num_rows > kRowsPerUnit;
+  a.skip_big = tiles ? 1 : 0;
+  // first-group slots r*S + j, S = ceil(len_cap/128)
   const int64_t S = ceil_div(a.len_cap, kPage) > 0 ? ceil_div(a.len_cap, kPage) : 1;
   a.blocks_per_req = static_cast<int32_t>(S);
-  const int64_t units = S * b->num_reqs + S * (b->num_rows / kRowsPerUnit);
+  const int64_t units = S * b->num_reqs;
   int64_t wgs = ceil_div(units, 4);
   const int64_t cap = 8LL * cu_count();
   if (wgs > cap) wgs = cap;
   if (wgs < 1) wgs = 1;
-  return hip_status(msa_launch_score(a, static_cast<int>(wgs), s));
+  hipError_t e = msa_launch_score(a, static_cast<int>(wgs), s);
+  if (e != hipSuccess || !tiles) return hip_status(e);
+  int64_t twgs = msa_score_tile_items_bound(b->num_rows, S);
+  const int64_t tcap = cu_count();  // one 512-thread workgroup per compute unit
+  if (twgs > tcap) twgs = tcap;
+  if (twgs < 1) twgs = 1;
+  return hip_status(msa_launch_score_tile(a, static_cast<int>(twgs), s));
 }
 
 msa_status launch_topk(hipStream_t s, const msa_batch* b, const float* scores, int32_t ld_s, int32_t topk,

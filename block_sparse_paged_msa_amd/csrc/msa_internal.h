@@ -125,18 +125,6 @@ __device__ __forceinline__ int block256_exclusive_scan(int v, int* scratch, int*
   return base + x - v;
 }
 
-// The hardware deals workgroups to the 8 XCDs round-robin (index b goes to
-// XCD b % 8, each XCD with its own L2). This gives each XCD a contiguous range
-// of logical workgroup indices instead, so that neighbouring work (pages or
-// blocks shared by nearby rows) meets in one L2.
-constexpr int kNumXcd = 8;
-__device__ __forceinline__ int xcd_local_block() {
-  const int b = blockIdx.x, g = gridDim.x;
-  const int x = b % kNumXcd, k = b / kNumXcd;
-  const int q = g / kNumXcd, rmd = g % kNumXcd;
-  return x * q + (x < rmd ? x : rmd) + k;
-}
-
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 }  // namespace msa
@@ -182,9 +170,12 @@ struct MsaScoreArgs {
   int32_t len_cap;
   int32_t blocks_per_req;  // host bound S on any request's blocks: slot r*S + j
   int32_t write_meta;
-  int32_t xcd_remap;       // number workgroups per XCD (prefill: row groups of a page meet in one L2)
+  int32_t skip_big;        // requests with more than 64 rows are left to the tile kernel
 };
 hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s);
+// Requests with more than 64 query rows: 256-row x 8-page MFMA tiles.
+hipError_t msa_launch_score_tile(const MsaScoreArgs& a, int num_wgs, hipStream_t s);
+int msa_score_tile_items_bound(int64_t num_rows, int64_t blocks_bound);
 
 struct MsaTopkArgs {
   const float* scores;

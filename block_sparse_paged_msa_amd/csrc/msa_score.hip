@@ -3,6 +3,8 @@
 // real block count, index-K tiles shared by all query rows of a request).
 //
 // Work unit = (request r, page j, group g of up to 64 query rows of r).
+// When the launch leaves requests of more than 64 rows to the tile kernel
+// (msa_score_tile.hip), their units are skipped here.
 // Units with g = 0 are numbered by a fixed stride, slot = r*S + j with S the
 // host bound on a request's blocks, so a wave knows its page from its slot
 // alone and requests the page before anything else; slots with j past the
@@ -162,7 +164,7 @@ __device__ __forceinline__ Unit slot_unit(const MsaScoreArgs& a, int u) {
   w.g = 0;
   w.L = clampi(a.seq_lens[w.r], 0, a.len_cap);
   w.ql = clampi(a.query_lens[w.r], 0, w.L);
-  w.valid = w.ql > 0 && w.j * kPage < w.L;
+  w.valid = w.ql > 0 && w.j * kPage < w.L && !(a.skip_big && w.ql > kRowsPerUnit);
   return w;
 }
 
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   const bool writer = a.write_meta && blockIdx.x == 0;
   const int slots_a = R * a.blocks_per_req;
   const int nwaves = gridDim.x * kWavesPerWg;
-  int u = (a.xcd_remap ? xcd_local_block() : static_cast<int>(blockIdx.x)) * kWavesPerWg + wave;
+  int u = static_cast<int>(blockIdx.x) * kWavesPerWg + wave;
 
   // Decode-only launches (at most 64 rows in all, so no request has a row
   // group past the first) with no metadata to write need no prefix: a wave
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
     }
     const int nb = (L + kPage - 1) / kPage;
     const int groups = (ql + kRowsPerUnit - 1) / kRowsPerUnit;
-    int x[5] = {ql, L, nb, nb * groups, nb * max(groups - 1, 0)};
+    int x[5] = {ql, L, nb, nb * groups, a.skip_big ? 0 : nb * max(groups - 1, 0)};
 #pragma unroll
     for (int c = 0; c < 5; ++c) x[c] = wave_inclusive_scan(x[c]);
     if (lane == 63) {
