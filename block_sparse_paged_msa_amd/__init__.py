@@ -30,7 +30,7 @@ EXPORTS = (
     "msa_build_metadata", "msa_index_score", "msa_topk_block_table", "msa_sparse_paged_attn",
     "msa_sparse_decode", "msa_index_score_ex", "msa_sparse_paged_attn_ex", "msa_sparse_decode_ex",
     "msa_cache_insert", "msa_cache_insert_ex",
-    "msa_workspace_bytes", "msa_status_string", "msa_version",
+    "msa_workspace_bytes", "msa_decode_workspace_bytes", "msa_status_string", "msa_version",
 )
 
 
@@ -86,6 +86,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "msa_cache_insert": ([vp, i32, vp, vp, vp, kp, vp, vp], i32),
         "msa_cache_insert_ex": ([vp, i32, vp, vp, vp, kp, vp, vp, vp], i32),
         "msa_workspace_bytes": ([i32, i32, i32, i32], sz),
+        "msa_decode_workspace_bytes": ([i32, i32, i32, i32], sz),
         "msa_status_string": ([i32], ctypes.c_char_p),
         "msa_version": ([], i32),
     }
@@ -210,6 +211,10 @@ def msa_cache_insert_ex(num_tokens: int, slot_mapping, k_new, v_new, kv: MsaKV, 
 
 def msa_workspace_bytes(num_rows: int, num_q_heads: int, max_ctx: int, ld_s: int) -> int:
     return int(load().msa_workspace_bytes(num_rows, num_q_heads, max_ctx, ld_s))
+
+
+def msa_decode_workspace_bytes(num_rows: int, num_q_heads: int, topk: int, ld_s: int) -> int:
+    return int(load().msa_decode_workspace_bytes(num_rows, num_q_heads, topk, ld_s))
 
 
 def msa_version() -> int:

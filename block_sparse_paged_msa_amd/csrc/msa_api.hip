@@ -76,6 +76,30 @@ WsLayout ws_layout(int num_rows, int num_q_heads, int max_ctx, int ld_s) {
   return w;
 }
 
+// Block-major attention for the fused step (launches of at least this many
+// rows, given the larger workspace): block partials for every row's topk
+// slots, the selected block ids, then the scores as above.
+constexpr int32_t kBlockMajorRows = 2048;
+
+struct BmLayout {
+  size_t partials, sel, scores, total;
+};
+
+BmLayout bm_layout(int num_rows, int num_q_heads, int topk, int ld_s) {
+  const size_t hgroups = static_cast<size_t>(ceil_div(num_q_heads, kHeadTile));
+  BmLayout w;
+  size_t off = 0;
+  w.partials = off;
+  off += align256(sizeof(float) * static_cast<size_t>(num_rows) * hgroups * static_cast<size_t>(topk) *
+                  (2 * kHeadTile + kHeadTile * kDim));
+  w.sel = off;
+  off += align256(sizeof(int32_t) * static_cast<size_t>(num_rows) * static_cast<size_t>(topk));
+  w.scores = off;
+  if (ld_s > 0) off += align256(sizeof(float) * static_cast<size_t>(num_rows) * ld_s);
+  w.total = off;
+  return w;
+}
+
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 msa_status check_batch(const msa_batch* b, bool need_meta_outputs) {
@@ -315,9 +339,45 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
   if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
   if (kv->num_pages != batch->num_pages) return MSA_ERR_INVALID_ARG;
   const int32_t max_ctx = kPage * topk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch->num_rows >= kBlockMajorRows) {
+    const BmLayout bw = bm_layout(batch->num_rows, num_q_heads, topk, block_scores ? 0 : ld_s);
+    if (workspace && workspace_bytes >= bw.total) {
+      // 1) metadata + index scores, 2) top-k + table + ctx + selected blocks,
+      // 3) block-major attention, 4) merge of the block partials
+      char* wsb = static_cast<char*>(workspace);
+      float* scores = block_scores ? block_scores : reinterpret_cast<float*>(wsb + bw.scores);
+      int32_t* sel = sel_blocks ? sel_blocks : reinterpret_cast<int32_t*>(wsb + bw.sel);
+      st = launch_score(s, batch, index_q, index_k, index_k_scale, scores, ld_s, true);
+      if (st != MSA_OK) return st;
+      st = launch_topk(s, batch, scores, ld_s, topk, sparse_table, ctx_lens, sel);
+      if (st != MSA_OK) return st;
+      MsaAttnArgs a = attn_args(q, batch->num_rows, num_q_heads, kv, 8 * topk, max_ctx, sm_scale, out, workspace);
+      a.partials = reinterpret_cast<float*>(wsb + bw.partials);
+      a.nsplit = topk;  // one partial slot per selected block
+      a.split_tok = kPage;
+      a.ctx_in = ctx_lens;
+      a.block_table = batch->block_table;
+      a.ld_bt = batch->ld_bt;
+      a.sinks = sinks;
+      a.lse_out = lse;
+      MsaBlockArgs bk;
+      bk.sel = sel;
+      bk.cu_q = batch->cu_seqlens_q;
+      bk.seq_lens = batch->seq_lens;
+      bk.num_reqs = batch->num_reqs;
+      bk.topk = topk;
+      bk.len_cap = len_cap(batch);
+      bk.vec_sel = (topk <= 32 && topk % 4 == 0 && reinterpret_cast<uintptr_t>(sel) % 16 == 0) ? 1 : 0;
+      int64_t wgs = static_cast<int64_t>(batch->num_reqs) * batch->ld_bt;
+      if (wgs > 2LL * cu_count()) wgs = 2LL * cu_count();
+      st = hip_status(msa_launch_attn_block(a, bk, kv->kv_dtype, kv->scale_mode, static_cast<int>(wgs), s));
+      if (st != MSA_OK) return st;
+      return hip_status(msa_launch_merge(a, s));
+    }
+  }
   const WsLayout w = ws_layout(batch->num_rows, num_q_heads, max_ctx, block_scores ? 0 : ld_s);
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MSA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores);
   // 1) metadata + index scores, 2) per-row selection + attention, 3) split merge
   st = launch_score(s, batch, index_q, index_k, index_k_scale, scores, ld_s, true);
@@ -378,6 +438,14 @@ msa_status msa_cache_insert_ex(msa_stream_t stream, int32_t num_tokens, const in
 size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ctx, int32_t ld_s) {
   if (num_rows < 0 || num_q_heads < 1 || max_ctx < 0 || ld_s < 0) return 0;
   return ws_layout(num_rows, num_q_heads, max_ctx, ld_s).total;
+}
+
+size_t msa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t topk, int32_t ld_s) {
+  if (num_rows < 0 || num_q_heads < 1 || topk < 1 || ld_s < 0) return 0;
+  const size_t per_row = ws_layout(num_rows, num_q_heads, kPage * topk, ld_s).total;
+  if (num_rows < kBlockMajorRows) return per_row;
+  const size_t bm = bm_layout(num_rows, num_q_heads, topk, ld_s).total;
+  return bm > per_row ? bm : per_row;
 }
 
 const char* msa_status_string(msa_status status) {

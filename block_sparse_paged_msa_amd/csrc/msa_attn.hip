@@ -123,16 +123,17 @@ __device__ __forceinline__ void attend_pair(WaveState& st, SubPage<KV_FP8, SCALE
   }
   const float m_new = fmaxf(st.m, max_across_rows(mloc));  // finite: token 0 of sub-page 0 is valid
   const float alpha = fast_exp2(st.m - m_new);
-  float psum = 0.f;
-  i16x4 p0, p1;
+  float psum = 0.f, e0[4], e1[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float e0 = fast_exp2(z0[i] - m_new);
-    const float e1 = fast_exp2(z1[i] - m_new);
-    psum += e0 + e1;
-    p0[i] = static_cast<short>(f32_to_bf16(e0 * sp[0].vs[i]));
-    p1[i] = static_cast<short>(f32_to_bf16(e1 * sp[1].vs[i]));
+    e0[i] = fast_exp2(z0[i] - m_new);
+    e1[i] = fast_exp2(z1[i] - m_new);
+    psum += e0[i] + e1[i];
   }
+  const i16x4 p0 = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e0[0] * sp[0].vs[0], e0[1] * sp[0].vs[1]),
+                                                    pk_bf16(e0[2] * sp[0].vs[2], e0[3] * sp[0].vs[3])}));
+  const i16x4 p1 = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e1[0] * sp[1].vs[0], e1[1] * sp[1].vs[1]),
+                                                    pk_bf16(e1[2] * sp[1].vs[2], e1[3] * sp[1].vs[3])}));
   st.l = st.l * alpha + psum;
   st.m = m_new;
   // V slots past the context can hold anything (even NaN codes): zero them so
@@ -161,12 +162,8 @@ struct MergeLds {
 };
 
 __device__ __forceinline__ u32x4 pack_bf16x8(f32x4 a, f32x4 b, float s) {
-  u32x4 pk;
-  pk.x = f32_to_bf16(a.x * s) | (static_cast<uint32_t>(f32_to_bf16(a.y * s)) << 16);
-  pk.y = f32_to_bf16(a.z * s) | (static_cast<uint32_t>(f32_to_bf16(a.w * s)) << 16);
-  pk.z = f32_to_bf16(b.x * s) | (static_cast<uint32_t>(f32_to_bf16(b.y * s)) << 16);
-  pk.w = f32_to_bf16(b.z * s) | (static_cast<uint32_t>(f32_to_bf16(b.w * s)) << 16);
-  return pk;
+  return u32x4{pk_bf16(a.x * s, a.y * s), pk_bf16(a.z * s, a.w * s), pk_bf16(b.x * s, b.y * s),
+               pk_bf16(b.z * s, b.w * s)};
 }
 
 // Attention of (row n, head group hgi, split) over tokens
@@ -566,6 +563,262 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   }
 }
 
+// Block-major attention for prefill-sized fused steps. A work item is
+// (request r, block b of r): the workgroup copies the block's K and V (one
+// contiguous run each: its 8 sub-pages are consecutive) into LDS once, finds
+// the rows of r whose selection holds b (binary search in each row's
+// ascending selection, 256 rows per pass), and every wave takes one of those
+// rows at a time: all 128 tokens' logits from LDS, the block's softmax
+// statistics, and the PV products. A row whose selection is this one block
+// gets its output here; otherwise the block's partial (max, sum, unnormalised
+// output) goes to the row's slot for the block's rank, and msa_merge_kernel
+// combines the slots in rank order, as it does for token splits.
+constexpr int kBlockThreads = 256;
+
+// The block in LDS is always bf16 (fp8 codes are widened once, when staged).
+struct BlockLds {
+  static constexpr int kPlane = kPage * kDim * 2;                   // bytes of one bf16 plane of a block
+  __attribute__((aligned(16))) uint8_t k[kPlane];                   // 8 shuffled K tiles
+  __attribute__((aligned(16))) uint8_t v[kPlane];                   // 8 dim-major V sub-pages
+  float ks[kPage], vs[kPage];
+  int row[kBlockThreads];                                           // rows of this pass
+  int rank[kBlockThreads];                                          // rank of the block in each
+  int ctx[kBlockThreads];                                           // and its context length
+  int wcount[4];
+};
+
+__device__ __forceinline__ bf16x8 lds_k_op(const BlockLds& sh, int i, int kc, int lane) {
+  const int e = i * (kSub * kDim) + (kc * 64 + lane) * 8;  // element offset of the operand
+  return *reinterpret_cast<const bf16x8*>(sh.k + 2 * e);
+}
+
+__device__ __forceinline__ i16x4 lds_v_op(const BlockLds& sh, int i, int dt, int lane) {
+  const int e = i * (kSub * kDim) + (dt * 16 + (lane & 15)) * kSub + (lane >> 4) * 4;
+  return *reinterpret_cast<const i16x4*>(sh.v + 2 * e);
+}
+
+template <int KV_FP8, int SCALE_MODE>
+__global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAttnArgs a, MsaBlockArgs bk) {
+  __shared__ BlockLds sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tok0 = 4 * (lane >> 4);
+  float kscal = 1.f, vscal = 1.f;
+  if constexpr (SCALE_MODE == 1) {
+    kscal = a.k_scale[0];
+    vscal = a.v_scale[0];
+  }
+  const float zscale = a.scale_log2 * kscal;
+  const int pmax = a.num_subpages / kSubsPerPage - 1;
+  const int items = bk.num_reqs * a.ld_bt;
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int r = item / a.ld_bt, blk = item - r * a.ld_bt;
+    const int L = clampi(bk.seq_lens[r], 0, bk.len_cap);
+    const int q0 = bk.cu_q[r], q1 = bk.cu_q[r + 1];
+    if (blk * kPage >= L || q1 <= q0) continue;
+    const int page = clampi(a.block_table[static_cast<size_t>(r) * a.ld_bt + blk], 0, pmax);
+
+    __syncthreads();  // the previous item's readers are done with the block
+    {
+      // 16-byte pieces of the stored planes: 32 KiB of bf16 or 16 KiB of codes
+      constexpr int kSrcPlane = kPage * kDim * (KV_FP8 ? 1 : 2);
+      constexpr int kPieces = kSrcPlane / 16 / kBlockThreads;  // 8 or 4
+      const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k_cache) +
+                                                       static_cast<size_t>(page) * kSrcPlane);
+      const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v_cache) +
+                                                       static_cast<size_t>(page) * kSrcPlane);
+      u32x4 kr[kPieces], vr[kPieces];
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        kr[i] = __builtin_nontemporal_load(kg + tid + kBlockThreads * i);
+        vr[i] = __builtin_nontemporal_load(vg + tid + kBlockThreads * i);
+      }
+      if constexpr (SCALE_MODE == 2) {
+        if (tid < kPage) {
+          sh.ks[tid] = a.k_scale[static_cast<size_t>(page) * kPage + tid];
+          sh.vs[tid] = a.v_scale[static_cast<size_t>(page) * kPage + tid];
+        }
+      }
+      u32x4* kd = reinterpret_cast<u32x4*>(sh.k);
+      u32x4* vd = reinterpret_cast<u32x4*>(sh.v);
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int q = tid + kBlockThreads * i;
+        if constexpr (KV_FP8 != 0) {  // 16 codes -> 16 bf16 values (exact), same element order
+          auto widen16 = [](u32x4 w, u32x4& lo, u32x4& hi) {
+            const u32x2 a0 = fp8x4_to_bf16x4(w.x), a1 = fp8x4_to_bf16x4(w.y);
+            const u32x2 a2 = fp8x4_to_bf16x4(w.z), a3 = fp8x4_to_bf16x4(w.w);
+            lo = u32x4{a0.x, a0.y, a1.x, a1.y};
+            hi = u32x4{a2.x, a2.y, a3.x, a3.y};
+          };
+          u32x4 lo, hi;
+          widen16(kr[i], lo, hi);
+          kd[2 * q] = lo;
+          kd[2 * q + 1] = hi;
+          widen16(vr[i], lo, hi);
+          vd[2 * q] = lo;
+          vd[2 * q + 1] = hi;
+          asm volatile("" ::: "memory");  // one piece at a time (fewer live registers)
+        } else {
+          kd[q] = kr[i];
+          vd[q] = vr[i];
+        }
+      }
+    }
+
+    for (int c0 = q0; c0 < q1; c0 += kBlockThreads) {
+      // which of these 256 rows selected the block, and at which rank: up to
+      // 32 selected ids are read in one round of 16-byte loads, longer
+      // selections by binary search
+      const int n = c0 + tid;
+      int j = -1, ctx_n = 0;
+      if (n < q1) {
+        const int32_t* srow = bk.sel + static_cast<size_t>(n) * bk.topk;
+        if (bk.vec_sel) {
+          u32x4 piece[8];
+          ctx_n = a.ctx_in[n];
+#pragma unroll
+          for (int p = 0; p < 8; ++p)
+            if (4 * p < bk.topk) piece[p] = *reinterpret_cast<const u32x4*>(srow + 4 * p);
+          const int kk = min((clampi(ctx_n, 0, kPage * bk.topk) + kPage - 1) / kPage, bk.topk);
+#pragma unroll
+          for (int p = 7; p >= 0; --p)
+            if (4 * p < bk.topk)
+#pragma unroll
+              for (int t = 3; t >= 0; --t)
+                if (4 * p + t < kk && static_cast<int>(piece[p][t]) == blk) j = 4 * p + t;
+        } else {
+          ctx_n = a.ctx_in[n];
+          const int kk = min((clampi(ctx_n, 0, kPage * bk.topk) + kPage - 1) / kPage, bk.topk);
+          int lo = 0, hi = kk;  // first rank whose block is >= blk
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (srow[mid] < blk) lo = mid + 1; else hi = mid;
+          }
+          if (lo < kk && srow[lo] == blk) j = lo;
+        }
+      }
+      const uint64_t hit = __ballot(j >= 0);
+      const int before = __popcll(hit & ((1ull << lane) - 1ull));
+      if (lane == 0) sh.wcount[wave] = __popcll(hit);
+      __syncthreads();  // counts, and the block's K / V in LDS
+      int base = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = sh.wcount[w];
+        base += (w < wave) ? c : 0;
+        total += c;
+      }
+      if (j >= 0) {
+        sh.row[base + before] = n;
+        sh.rank[base + before] = j;
+        sh.ctx[base + before] = ctx_n;
+      }
+      __syncthreads();
+
+      // each wave takes every fourth (row, head group); the next one's query
+      // is requested before the current one's products
+      const int nent = total * a.num_hgroups;
+      auto entry_q = [&](int e, bf16x8 (&qv)[4]) {
+        const int ee = min(e, max(nent - 1, 0));
+        load_q(a, sh.row[ee / a.num_hgroups], ee % a.num_hgroups, qv);
+      };
+      bf16x8 qnext[4];
+      if (wave < nent) entry_q(wave, qnext);
+      for (int e = wave; e < nent; e += 4) {
+        const int row = sh.row[e / a.num_hgroups], rank = sh.rank[e / a.num_hgroups];
+        const int hgi = e - (e / a.num_hgroups) * a.num_hgroups;
+        bf16x8 qb[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) qb[kc] = qnext[kc];
+        if (e + 4 < nent) entry_q(e + 4, qnext);
+        const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
+        const int ctx = clampi(sh.ctx[e / a.num_hgroups], 0, kPage * bk.topk);
+        const int kk = (ctx + kPage - 1) / kPage;
+        const int nval = min(kPage, ctx - rank * kPage);  // tokens of the block the row sees
+        const float sink2 =
+            (a.sinks && (lane & 15) < nheads) ? a.sinks[hgi * kHeadTile + (lane & 15)] * kLog2e : -INFINITY;
+        // pass 1: the block's 128 logits (S^T per sub-page: token rows, head
+        // columns) and their max; the empty asm keeps the compiler from
+        // pulling every sub-page's LDS operands into registers at once
+        const bool part_blk = nval < kPage;
+        float z[8][4];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) sacc = mfma_16x16x32(lds_k_op(sh, i, kc, lane), qb[kc], sacc);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int tok = i * kSub + tok0 + t;
+            z[i][t] = sacc[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[tok] : 1.f);
+            if (part_blk && tok >= nval) z[i][t] = -INFINITY;
+            mloc = fmaxf(mloc, z[i][t]);
+          }
+          asm volatile("" ::: "memory");
+        }
+        const float m = max_across_rows(mloc);  // finite: token 0 is visible
+        // pass 2: probabilities and O^T += V^T P^T per sub-page
+        float lsum = 0.f;
+        f32x4 o[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float e[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            e[t] = fast_exp2(z[i][t] - m);
+            lsum += e[t];
+            if constexpr (SCALE_MODE == 2) e[t] *= sh.vs[i * kSub + tok0 + t];
+          }
+          const i16x4 p = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3])}));
+          const bool vmask = part_blk && (i * kSub + tok0 + 3 >= nval);  // slots past the row's tokens
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            i16x4 vop = lds_v_op(sh, i, dt, lane);
+            if (vmask) {  // they can hold anything, even NaN codes
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (i * kSub + tok0 + t >= nval) vop[t] = 0;
+            }
+            o[dt] = mfma_16x16x16(vop, p, o[dt]);
+          }
+          asm volatile("" ::: "memory");
+        }
+        const float l = sum_across_rows(lsum);
+        const int head = lane & 15;
+        if (kk <= 1) {  // the row's only block: its output
+          const float den = l + fast_exp2(sink2 - m);
+          const float inv = vscal / den;
+          if (head < nheads) {
+            uint16_t* orow = a.out + (static_cast<size_t>(row) * a.num_q_heads + hgi * kHeadTile + head) * kDim;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              *reinterpret_cast<u32x2*>(orow + dt * 16 + tok0) =
+                  u32x2{pk_bf16(o[dt][0] * inv, o[dt][1] * inv), pk_bf16(o[dt][2] * inv, o[dt][3] * inv)};
+            }
+            if (a.lse_out && lane < 16)
+              a.lse_out[static_cast<size_t>(row) * a.num_q_heads + hgi * kHeadTile + head] = (m + log2f(l)) * kLn2;
+          }
+        } else {  // partial of the block's rank; a scalar V scale is folded in
+          float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kPartStride;
+          if (lane < 16) {
+            part[head] = m;
+            part[kHeadTile + head] = l;
+          }
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<f32x4*>(part + 2 * kHeadTile + head * kDim + dt * 16 + tok0) = o[dt] * vscal;
+        }
+      }
+      __syncthreads();  // the row list is reused by the next pass
+    }
+  }
+}
+
 template <int KV_FP8, int SCALE_MODE>
 hipError_t launch(const MsaAttnArgs& a, hipStream_t s) {
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups * a.nsplit;
@@ -600,6 +853,20 @@ hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, h
   }
   if (scale_mode == 1) return launch<1, 1>(a, s);
   return launch<1, 2>(a, s);
+}
+
+hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, int kv_dtype, int scale_mode,
+                                 int num_wgs, hipStream_t s) {
+  const dim3 g(static_cast<unsigned>(num_wgs)), t(kBlockThreads);
+  if (kv_dtype == 0) {
+    if (scale_mode == 0) hipLaunchKernelGGL((msa_attn_block_kernel<0, 0>), g, t, 0, s, a, b);
+    else if (scale_mode == 1) hipLaunchKernelGGL((msa_attn_block_kernel<0, 1>), g, t, 0, s, a, b);
+    else hipLaunchKernelGGL((msa_attn_block_kernel<0, 2>), g, t, 0, s, a, b);
+  } else {
+    if (scale_mode == 1) hipLaunchKernelGGL((msa_attn_block_kernel<1, 1>), g, t, 0, s, a, b);
+    else hipLaunchKernelGGL((msa_attn_block_kernel<1, 2>), g, t, 0, s, a, b);
+  }
+  return hipGetLastError();
 }
 
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {

@@ -27,13 +27,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+// Two floats -> two bf16 (round to nearest even, denormals kept, NaN stays a
+// quiet NaN), low half first: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// float -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(pk_bf16(f, 0.f)); }
 
 // Four e4m3fn codes (one dword) -> four bf16 values packed in two dwords.
 // e4m3 values are exactly representable in bf16, so taking the top half of
@@ -255,3 +259,20 @@ hipError_t msa_launch_insert(const MsaInsertArgs& a, hipStream_t s);
 constexpr int kMaxSplitTokens = 8192;
 hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, hipStream_t s);
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s);
+// Block-major attention (prefill-sized fused steps): one workgroup per
+// (request, block) serves every row of the request that selected the block,
+// from the selection written by the top-k kernel (sel ascending per row, ctx).
+// Uses from MsaAttnArgs: q, caches and scales, block_table, ld_bt, ctx_in,
+// out, lse_out, sinks, partials (nsplit = topk slots per row and head group),
+// num_q_heads, num_hgroups, num_subpages, scale_log2.
+struct MsaBlockArgs {
+  const int32_t* sel;        // [N][topk] selected blocks, ascending, -1 tail
+  const int32_t* cu_q;       // [R+1] query-row prefix
+  const int32_t* seq_lens;   // [R]
+  int32_t num_reqs;
+  int32_t topk;
+  int32_t len_cap;
+  int32_t vec_sel;           // topk <= 32, a multiple of 4, and sel 16-byte aligned: rows read whole
+};
+hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, int kv_dtype, int scale_mode,
+                                 int num_wgs, hipStream_t s);

@@ -208,6 +208,13 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  *   workspace. ld_s >= ceil(max_seq_len/128).
  *   workspace: >= msa_workspace_bytes(num_rows, num_q_heads, 128*topk,
  *   block_scores ? 0 : ld_s) bytes (NULL allowed when that is 0).
+ *   Launches of at least 2048 rows (prefill-sized) given a workspace of
+ *   msa_decode_workspace_bytes(num_rows, num_q_heads, topk, block_scores ? 0
+ *   : ld_s) bytes take the block-major path instead: the top-k step runs on
+ *   its own (4 launches), then one workgroup per (request, selected block)
+ *   attends every row that chose the block from one copy of its K/V, and the
+ *   per-block partials are merged. Same results up to rounding order; with
+ *   the smaller workspace the per-row path runs.
  * Errors: union of the errors of the steps.
  */
 msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q,
@@ -306,6 +313,16 @@ msa_status msa_cache_insert_ex(msa_stream_t stream, int32_t num_tokens,
  * the workspace) on the current device. Returns 0 for invalid arguments.
  */
 size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ctx, int32_t ld_s);
+
+/*
+ * msa_decode_workspace_bytes — workspace that lets msa_sparse_decode(_ex)
+ * take the block-major path on launches of at least 2048 rows: per row,
+ * num_q_heads/16 (rounded up) x topk partials of 8320 bytes plus topk block
+ * ids, and the scores when ld_s > 0. For fewer rows it equals
+ * msa_workspace_bytes(num_rows, num_q_heads, 128*topk, ld_s). Returns 0 for
+ * invalid arguments.
+ */
+size_t msa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t topk, int32_t ld_s);
 
 /* Human-readable name of a status code (static storage). */
 const char* msa_status_string(msa_status status);

@@ -1,0 +1,74 @@
+"""GPU parity of the block-major path of the fused step (launches of at
+least 2048 rows given msa_decode_workspace_bytes): selections, tables and
+context lengths bit-exact against the oracle selector on the device's scores;
+attention (with LSE and sinks) against the oracle on the device's own table,
+to the same bars as the per-row path; and the per-row path on the same
+inputs (smaller workspace) within the same bars."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_paged_msa_amd as msa
+import msa_synth as syn
+from oracle import msa_oracle as O
+from tests import helpers as H
+from tests.test_gpu_parity import check_metadata, check_selection, _sample_rows
+
+pytestmark = pytest.mark.gpu
+
+ATOL = {syn.KV_BF16: 2e-2, syn.KV_FP8: 6e-2}
+ATOL_LSE = 1e-3
+
+CASES = [
+    # (lengths, query rows, top-k, q heads, kv dtype, scale mode): prefill
+    # requests among decode rows; short requests whose rows select one block
+    # (their output is written by the block kernel itself); two head groups
+    ([16384, 16384, 6000, 9000], [1, 1, 2100, 1000], 16, 16, syn.KV_BF16, syn.SCALE_NONE),
+    ([100, 4000, 20000, 300], [100, 1800, 3, 250], 8, 16, syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD),
+    ([3000, 12000], [1500, 600], 24, 24, syn.KV_FP8, syn.SCALE_SCALAR),
+]
+
+
+def _sinks(seed, hq):
+    s = syn.SplitMix64(seed).uniform(hq) * 6.0 - 1.0
+    s[0] = -np.inf
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("with_extras", [False, True])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_block_major_step(gpu_lib, case, with_extras):
+    L, ql, topk, hq, kv, sm = CASES[case]
+    b = syn.make_batch("bm", 800 + case, L, ql, topk=topk, num_q_heads=hq, kv_dtype=kv, scale_mode=sm)
+    assert b.num_rows >= 2048
+    print(f"[block-major] case {case} rows={b.num_rows} extras={with_extras}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, hq, topk, 0)
+    assert wsb > o.wsb
+    o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")  # garbage on entry
+    o.wsb = wsb
+    sinks = _sinks(810 + case, hq) if with_extras else None
+    lse = H.run_decode_lse(d, o, sinks)
+    torch.cuda.synchronize()
+    check_metadata(b, H.read_metadata(d))
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    check_selection(b, scores, table, ctx, sel, range(b.num_rows))
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    rows = _sample_rows(b, 16, 820 + case)
+    # rows whose selection is one block are written by the block kernel itself
+    rows += [n for n in range(b.num_rows) if ctx[n] <= 128][:8]
+    rows = sorted(set(rows))
+    ref_out, ref_lse = O.attention_lse_from_table(b, table, ctx, rows, sinks)
+    err = np.abs(out[rows] - ref_out).max()
+    assert err <= ATOL[kv], f"attention max abs err {err}"
+    lerr = np.abs(lse[rows] - ref_lse).max()
+    assert lerr <= ATOL_LSE, f"lse max abs err {lerr}"
+    # the per-row path on the same inputs (the smaller workspace selects it)
+    o2 = H.alloc_decode(d)
+    H.run_decode_lse(d, o2, sinks)
+    assert torch.equal(o2.table, o.table) and torch.equal(o2.ctx, o.ctx)
+    d_out = np.abs(H.bf16_to_np(o2.out) - out).max()
+    assert d_out <= ATOL[kv], f"block-major vs per-row max abs diff {d_out}"
