@@ -90,8 +90,9 @@ BmLayout bm_layout(int num_rows, int num_q_heads, int topk, int ld_s) {
   BmLayout w;
   size_t off = 0;
   w.partials = off;
-  off += align256(sizeof(float) * static_cast<size_t>(num_rows) * hgroups * static_cast<size_t>(topk) *
-                  (2 * kHeadTile + kHeadTile * kDim));
+  // one slot per (row, head group, selected block): m[16], l[16] fp32 + fp16 acc[16][128]
+  off += align256(static_cast<size_t>(num_rows) * hgroups * static_cast<size_t>(topk) *
+                  (sizeof(float) * 2 * kHeadTile + sizeof(uint16_t) * kHeadTile * kDim));
   w.sel = off;
   off += align256(sizeof(int32_t) * static_cast<size_t>(num_rows) * static_cast<size_t>(topk));
   w.scores = off;
@@ -355,6 +356,7 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
       MsaAttnArgs a = attn_args(q, batch->num_rows, num_q_heads, kv, 8 * topk, max_ctx, sm_scale, out, workspace);
       a.partials = reinterpret_cast<float*>(wsb + bw.partials);
       a.nsplit = topk;  // one partial slot per selected block
+      a.half_partials = 1;
       a.split_tok = kPage;
       a.ctx_in = ctx_lens;
       a.block_table = batch->block_table;

@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kPartStride = 2 * kHeadTile + kHeadTile * kDim;  // m[16], l[16], acc[16][128]
+constexpr int kHalfPartStride = 2 * kHeadTile + kHeadTile * kDim / 2;  // m[16], l[16], fp16 acc[16][128]
 constexpr int kLdsRow = kDim + 4;                               // padded [head][dim] rows
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / kPage;
 
@@ -500,13 +501,15 @@ __device__ __forceinline__ MergeState merge_partner(const MergeState& x) {
   return r;
 }
 
+template <bool HALF>
 __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a, const int32_t* ctxp) {
+  constexpr int kStride = HALF ? kHalfPartStride : kPartStride;
   const int lane = threadIdx.x;
   const int head = blockIdx.x % a.num_q_heads;
   const int n = blockIdx.x / a.num_q_heads;
   const int hgi = head / kHeadTile, th = head % kHeadTile;
   const int sg = lane >> 4, td = (lane & 15) * 8;
-  const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kPartStride;
+  const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kStride;
   // the first thirty-two partials are requested in the same round as ctx
   // (every slot below nsplit exists in the workspace; unused ones are ignored)
   constexpr int kPer = 8;  // splits per lane per round
@@ -515,11 +518,18 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   auto fetch = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const float* ps = base + static_cast<size_t>(min(s0 + sg + 4 * j, a.nsplit - 1)) * kPartStride;
+      const float* ps = base + static_cast<size_t>(min(s0 + sg + 4 * j, a.nsplit - 1)) * kStride;
       ms[j] = ps[th];
       ls[j] = ps[kHeadTile + th];
-      x0[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td);
-      x1[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4);
+      if constexpr (HALF) {
+        const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ps + 2 * kHeadTile) +
+                                                          th * kDim + td);
+        x0[j] = f32x4{f16_lo(h.x), f16_hi(h.x), f16_lo(h.y), f16_hi(h.y)};
+        x1[j] = f32x4{f16_lo(h.z), f16_hi(h.z), f16_lo(h.w), f16_hi(h.w)};
+      } else {
+        x0[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td);
+        x1[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4);
+      }
     }
   };
   fetch(0);
@@ -803,15 +813,29 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
             if (a.lse_out && lane < 16)
               a.lse_out[static_cast<size_t>(row) * a.num_q_heads + hgi * kHeadTile + head] = (m + log2f(l)) * kLn2;
           }
-        } else {  // partial of the block's rank; a scalar V scale is folded in
-          float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kPartStride;
-          if (lane < 16) {
-            part[head] = m;
-            part[kHeadTile + head] = l;
-          }
+        } else {
+          // partial of the block's rank, the accumulator in fp16: a scalar V
+          // scale is folded in, then the head's accumulator is scaled by 2^-e
+          // so that its largest magnitude is below 1 and e is folded into the
+          // log2-domain max and the sum (2^(m+e) * l*2^-e = 2^m * l), so the
+          // merge weighs the slots exactly as it weighs fp32 partials
+          float mx = 0.f;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
-            *reinterpret_cast<f32x4*>(part + 2 * kHeadTile + head * kDim + dt * 16 + tok0) = o[dt] * vscal;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fabsf(o[dt][t]));
+          mx = max_across_rows(mx) * fabsf(vscal);
+          const int e = (mx > 0.f) ? clampi(__builtin_amdgcn_frexp_expf(mx), -kHalfExpRange, kHalfExpRange) : 0;
+          const float f = ldexpf(vscal, -e);
+          float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kHalfPartStride;
+          if (lane < 16) {
+            part[head] = m + static_cast<float>(e);
+            part[kHeadTile + head] = ldexpf(l, -e);
+          }
+          uint32_t* acc = reinterpret_cast<uint32_t*>(part + 2 * kHeadTile) + (head * kDim + tok0) / 2;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<u32x2*>(acc + dt * 8) = u32x2{pk_f16(o[dt][0] * f, o[dt][1] * f), pk_f16(o[dt][2] * f, o[dt][3] * f)};
         }
       }
       __syncthreads();  // the row list is reused by the next pass
@@ -872,7 +896,10 @@ hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, in
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {
   if (a.nsplit <= 1) return hipSuccess;
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_q_heads;
-  hipLaunchKernelGGL(msa_merge_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMergeThreads), 0, s, a,
-                     a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in);
+  const int32_t* ctxp = a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in;
+  if (a.half_partials)
+    hipLaunchKernelGGL(msa_merge_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kMergeThreads), 0, s, a, ctxp);
+  else
+    hipLaunchKernelGGL(msa_merge_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kMergeThreads), 0, s, a, ctxp);
   return hipGetLastError();
 }

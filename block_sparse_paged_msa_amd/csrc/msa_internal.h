@@ -39,6 +39,24 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 // float -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(pk_bf16(f, 0.f)); }
 
+// Two floats -> two IEEE fp16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+// fp16 partial accumulators are scaled by 2^-e with |e| capped here: the
+// sums they are folded into stay normal fp32 numbers, and accumulators up to
+// 2^(kHalfExpRange+16) in magnitude stay finite.
+constexpr int kHalfExpRange = 100;
+
 // Four e4m3fn codes (one dword) -> four bf16 values packed in two dwords.
 // e4m3 values are exactly representable in bf16, so taking the top half of
 // the exact fp32 conversion is exact.
@@ -219,7 +237,8 @@ struct MsaAttnArgs {
   uint16_t* out;
   float* lse_out;      // [rows][Hq] natural-log LSE, or null
   const float* sinks;  // [Hq] per-head sink logits, or null
-  float* partials;     // [rows][hgroups][nsplit][16*2 + 16*128]
+  float* partials;     // [rows][hgroups][nsplit] slots: m[16], l[16] fp32, then acc[16][128]
+  int32_t half_partials;  // acc stored as fp16 scaled by a power of two (block-major path), else fp32
   int32_t ld_table;    // row stride of the table (8*topk in fused mode)
   int32_t ld_s;
   int32_t ld_bt;

@@ -213,8 +213,11 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  *   : ld_s) bytes take the block-major path instead: the top-k step runs on
  *   its own (4 launches), then one workgroup per (request, selected block)
  *   attends every row that chose the block from one copy of its K/V, and the
- *   per-block partials are merged. Same results up to rounding order; with
- *   the smaller workspace the per-row path runs.
+ *   per-block partials are merged. Each partial keeps its max and sum in fp32
+ *   and its 16x128 accumulator in fp16, scaled by a power of two so that its
+ *   largest magnitude is below 1 (the error this adds to an output is at most
+ *   2^-11 of the largest |V| entry the row attends). Same results up to that
+ *   and rounding order; with the smaller workspace the per-row path runs.
  * Errors: union of the errors of the steps.
  */
 msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q,
@@ -317,7 +320,7 @@ size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ct
 /*
  * msa_decode_workspace_bytes — workspace that lets msa_sparse_decode(_ex)
  * take the block-major path on launches of at least 2048 rows: per row,
- * num_q_heads/16 (rounded up) x topk partials of 8320 bytes plus topk block
+ * num_q_heads/16 (rounded up) x topk partials of 4224 bytes plus topk block
  * ids, and the scores when ld_s > 0. For fewer rows it equals
  * msa_workspace_bytes(num_rows, num_q_heads, 128*topk, ld_s). Returns 0 for
  * invalid arguments.

@@ -72,3 +72,30 @@ def test_block_major_step(gpu_lib, case, with_extras):
     assert torch.equal(o2.table, o.table) and torch.equal(o2.ctx, o.ctx)
     d_out = np.abs(H.bf16_to_np(o2.out) - out).max()
     assert d_out <= ATOL[kv], f"block-major vs per-row max abs diff {d_out}"
+
+
+@pytest.mark.parametrize("vexp", [40, -60])
+def test_block_major_extreme_values(gpu_lib, vexp):
+    """V scaled by 2^vexp (exact in bf16): the fp16 block partials are scaled
+    by a power of two chosen from their own magnitude, so the outputs scale
+    with V and stay within the bars relative to it."""
+    L, ql, topk, hq = [9000, 3000], [1800, 400], 16, 16
+    b = syn.make_batch("bm_scale", 830 + (vexp & 7), L, ql, topk=topk, num_q_heads=hq,
+                       kv_dtype=syn.KV_BF16, scale_mode=syn.SCALE_NONE)
+    f = (b.v_cache.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** vexp)
+    b.v_cache = (f.view(np.uint32) >> 16).astype(np.uint16)
+    print(f"[block-major] V x 2^{vexp} rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, hq, topk, 0)
+    o.ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    o.wsb = wsb
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    table, ctx = o.table.cpu().numpy(), o.ctx.cpu().numpy()
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    rows = sorted(set(_sample_rows(b, 16, 840)))
+    ref = O.attention_from_table(b, table, ctx, rows)
+    err = np.abs(out[rows] - ref).max() / 2.0 ** vexp
+    assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err} (in units of 2^{vexp})"
