@@ -77,7 +77,25 @@ def algorithmic_bytes(b, ctx):
     kv = int(np.asarray(ctx, dtype=np.int64).sum()) * kv_tok
     qo = N * hq * 128 * 2 * 2
     small = N * ld_s * 4 * 2 + N * 8 * topk * 4 + N * 4 + N * topk * 4 + b.num_reqs * 4 * 6 + N * 8
-    return {"step": idx_k + N * 256 + kv + qo + small, "score": score_launch, "attn": kv + qo + N * 8 * topk * 4}
+    return {"step": idx_k + N * 256 + kv + qo + small, "score": score_launch, "attn": kv + qo + N * 8 * topk * 4,
+            "kv": kv}
+
+
+def unique_kv_bytes(b, table, ctx):
+    """K/V bytes of a step when each sub-page that any row of a request
+    attends is read once for the request (the rows' page-16 tables give the
+    sub-pages: the first ceil(ctx/16) entries of each row), the K/V term of
+    the step's minimum traffic once rows of one request share blocks."""
+    import numpy as np
+    elt = 2 if b.kv_dtype == 0 else 1
+    kv_tok = 2 * 128 * elt + (8 if b.scale_mode == 2 else 0)
+    cu = np.concatenate([[0], np.cumsum(b.query_lens.astype(np.int64))])
+    total = 0
+    for r in range(b.num_reqs):
+        parts = [table[n, :(int(ctx[n]) + 15) // 16] for n in range(cu[r], cu[r + 1])]
+        if parts:
+            total += int(np.unique(np.concatenate(parts)).size) * 16 * kv_tok
+    return total
 
 
 def cpu_baseline(b, rows, budget_s=10.0):
@@ -256,6 +274,7 @@ def main():
         return
     ctx_host = ctx.cpu().numpy()
     nbytes = algorithmic_bytes(b, ctx_host)
+    kv_unique = unique_kv_bytes(b, table.cpu().numpy(), ctx_host)
 
     if args.eager:
         def run_steps(k0, k):
@@ -355,6 +374,10 @@ def main():
         "step_hbm_gbps": nbytes["step"] / sec / 1e9,
         "step_hbm_frac": nbytes["step"] / sec / 1e9 / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": nbytes["step"],
+        # the same with each request's attended K/V counted once (rows of one
+        # request that select the same blocks share them)
+        "step_unique_bytes": nbytes["step"] - nbytes["kv"] + kv_unique,
+        "step_unique_hbm_frac": (nbytes["step"] - nbytes["kv"] + kv_unique) / sec / 1e9 / PEAK_HBM_GBPS,
         "roofline": {"kernel": "msa_score_kernel (msa_index_score)", "bound": "hbm", "achieved": score_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},

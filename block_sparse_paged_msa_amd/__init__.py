@@ -70,6 +70,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_paged_msa_amd.build`")
+    # torch carries its own HIP runtime under the same soname: load torch
+    # first so that the library binds to that runtime instead of bringing in
+    # a second one (kernels of one runtime are invalid in the other)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     bp, kp = ctypes.POINTER(MsaBatch), ctypes.POINTER(MsaKV)
