@@ -241,7 +241,7 @@ def main():
     table = torch.empty((N, 8 * topk), **i32)
     ctx = torch.empty((N,), **i32)
     scores = torch.empty((N, ld_s), dtype=torch.float32, device=dev)
-    wsb = msa.msa_decode_workspace_bytes(N, hq, topk, 0)  # prefill-sized steps: the block-major path
+    wsb = msa.msa_decode_workspace_bytes(N, b.max_seq_len, hq, topk, 0)  # prefill-sized: block-major path
     ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
 
     def step(c):

@@ -93,7 +93,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "msa_cache_insert": ([vp, i32, vp, vp, vp, kp, vp, vp], i32),
         "msa_cache_insert_ex": ([vp, i32, vp, vp, vp, kp, vp, vp, vp], i32),
         "msa_workspace_bytes": ([i32, i32, i32, i32], sz),
-        "msa_decode_workspace_bytes": ([i32, i32, i32, i32], sz),
+        "msa_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "msa_status_string": ([i32], ctypes.c_char_p),
         "msa_version": ([], i32),
     }
@@ -220,8 +220,8 @@ def msa_workspace_bytes(num_rows: int, num_q_heads: int, max_ctx: int, ld_s: int
     return int(load().msa_workspace_bytes(num_rows, num_q_heads, max_ctx, ld_s))
 
 
-def msa_decode_workspace_bytes(num_rows: int, num_q_heads: int, topk: int, ld_s: int) -> int:
-    return int(load().msa_decode_workspace_bytes(num_rows, num_q_heads, topk, ld_s))
+def msa_decode_workspace_bytes(num_rows: int, max_seq_len: int, num_q_heads: int, topk: int, ld_s: int) -> int:
+    return int(load().msa_decode_workspace_bytes(num_rows, max_seq_len, num_q_heads, topk, ld_s))
 
 
 def msa_version() -> int:

@@ -80,12 +80,18 @@ WsLayout ws_layout(int num_rows, int num_q_heads, int max_ctx, int ld_s) {
 // rows, given the larger workspace): block partials for every row's topk
 // slots, the selected block ids, then the scores as above.
 constexpr int32_t kBlockMajorRows = 2048;
+constexpr int32_t kBlockMajorMaxRows = 1 << 18;  // rows fit the row field of a list entry
 
 struct BmLayout {
-  size_t partials, sel, scores, total;
+  size_t partials, words, scores, total;
 };
 
-BmLayout bm_layout(int num_rows, int num_q_heads, int topk, int ld_s) {
+// Block-major workspace: partial slots, each row's selection words (one
+// 8-byte word per 32 blocks of ceil(max_seq_len / 128)), then the scores when
+// the caller passes no score buffer.
+int bm_words(int nbmax) { return (nbmax + 31) / 32; }
+
+BmLayout bm_layout(int num_rows, int nbmax, int num_q_heads, int topk, int ld_s) {
   const size_t hgroups = static_cast<size_t>(ceil_div(num_q_heads, kHeadTile));
   BmLayout w;
   size_t off = 0;
@@ -93,8 +99,8 @@ BmLayout bm_layout(int num_rows, int num_q_heads, int topk, int ld_s) {
   // one slot per (row, head group, selected block): m[16], l[16] fp32 + fp16 acc[16][128]
   off += align256(static_cast<size_t>(num_rows) * hgroups * static_cast<size_t>(topk) *
                   (sizeof(float) * 2 * kHeadTile + sizeof(uint16_t) * kHeadTile * kDim));
-  w.sel = off;
-  off += align256(sizeof(int32_t) * static_cast<size_t>(num_rows) * static_cast<size_t>(topk));
+  w.words = off;
+  off += align256(sizeof(uint64_t) * static_cast<size_t>(num_rows) * bm_words(nbmax));
   w.scores = off;
   if (ld_s > 0) off += align256(sizeof(float) * static_cast<size_t>(num_rows) * ld_s);
   w.total = off;
@@ -196,9 +202,9 @@ msa_status launch_score(hipStream_t s, const msa_batch* b, const void* index_q, 
   return hip_status(msa_launch_score_tile(a, static_cast<int>(twgs), s));
 }
 
-msa_status launch_topk(hipStream_t s, const msa_batch* b, const float* scores, int32_t ld_s, int32_t topk,
-                       int32_t* table, int32_t* ctx, int32_t* sel) {
-  MsaTopkArgs a;
+MsaTopkArgs topk_args(const msa_batch* b, const float* scores, int32_t ld_s, int32_t topk, int32_t* table,
+                      int32_t* ctx, int32_t* sel) {
+  MsaTopkArgs a = {};
   a.scores = scores;
   a.block_table = b->block_table;
   a.row_req = b->row_req;
@@ -211,7 +217,12 @@ msa_status launch_topk(hipStream_t s, const msa_batch* b, const float* scores, i
   a.topk = topk;
   a.num_rows = b->num_rows;
   a.num_reqs = b->num_reqs;
-  return hip_status(msa_launch_topk(a, s));
+  return a;
+}
+
+msa_status launch_topk(hipStream_t s, const msa_batch* b, const float* scores, int32_t ld_s, int32_t topk,
+                       int32_t* table, int32_t* ctx, int32_t* sel) {
+  return hip_status(msa_launch_topk(topk_args(b, scores, ld_s, topk, table, ctx, sel), s));
 }
 
 MsaAttnArgs attn_args(const void* q, int32_t num_rows, int32_t num_q_heads, const msa_kv* kv, int32_t ld_table,
@@ -341,17 +352,21 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
   if (kv->num_pages != batch->num_pages) return MSA_ERR_INVALID_ARG;
   const int32_t max_ctx = kPage * topk;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (batch->num_rows >= kBlockMajorRows) {
-    const BmLayout bw = bm_layout(batch->num_rows, num_q_heads, topk, block_scores ? 0 : ld_s);
+  if (batch->num_rows >= kBlockMajorRows && batch->num_rows <= kBlockMajorMaxRows) {
+    const int nbmax = blocks_bound(batch);
+    const BmLayout bw = bm_layout(batch->num_rows, nbmax, num_q_heads, topk, block_scores ? 0 : ld_s);
     if (workspace && workspace_bytes >= bw.total) {
-      // 1) metadata + index scores, 2) top-k + table + ctx + selected blocks,
-      // 3) block-major attention, 4) merge of the block partials
+      // 1) metadata + index scores, 2) top-k + table + ctx + selection
+      // words, 3) block-major attention, 4) merge of the block partials
       char* wsb = static_cast<char*>(workspace);
       float* scores = block_scores ? block_scores : reinterpret_cast<float*>(wsb + bw.scores);
-      int32_t* sel = sel_blocks ? sel_blocks : reinterpret_cast<int32_t*>(wsb + bw.sel);
+      uint64_t* words = reinterpret_cast<uint64_t*>(wsb + bw.words);
       st = launch_score(s, batch, index_q, index_k, index_k_scale, scores, ld_s, true);
       if (st != MSA_OK) return st;
-      st = launch_topk(s, batch, scores, ld_s, topk, sparse_table, ctx_lens, sel);
+      MsaTopkArgs t = topk_args(batch, scores, ld_s, topk, sparse_table, ctx_lens, sel_blocks);
+      t.row_words = words;
+      t.row_words_ld = bm_words(nbmax);
+      st = hip_status(msa_launch_topk(t, s));
       if (st != MSA_OK) return st;
       MsaAttnArgs a = attn_args(q, batch->num_rows, num_q_heads, kv, 8 * topk, max_ctx, sm_scale, out, workspace);
       a.partials = reinterpret_cast<float*>(wsb + bw.partials);
@@ -364,14 +379,15 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
       a.sinks = sinks;
       a.lse_out = lse;
       MsaBlockArgs bk;
-      bk.sel = sel;
+      bk.row_words = words;
       bk.cu_q = batch->cu_seqlens_q;
       bk.seq_lens = batch->seq_lens;
+      bk.row_words_ld = bm_words(nbmax);
+      bk.nbmax = nbmax;
       bk.num_reqs = batch->num_reqs;
       bk.topk = topk;
       bk.len_cap = len_cap(batch);
-      bk.vec_sel = (topk <= 32 && topk % 4 == 0 && reinterpret_cast<uintptr_t>(sel) % 16 == 0) ? 1 : 0;
-      int64_t wgs = static_cast<int64_t>(batch->num_reqs) * batch->ld_bt;
+      int64_t wgs = static_cast<int64_t>(batch->num_reqs) * nbmax;
       if (wgs > 2LL * cu_count()) wgs = 2LL * cu_count();
       st = hip_status(msa_launch_attn_block(a, bk, kv->kv_dtype, kv->scale_mode, static_cast<int>(wgs), s));
       if (st != MSA_OK) return st;
@@ -442,11 +458,13 @@ size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ct
   return ws_layout(num_rows, num_q_heads, max_ctx, ld_s).total;
 }
 
-size_t msa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t topk, int32_t ld_s) {
-  if (num_rows < 0 || num_q_heads < 1 || topk < 1 || ld_s < 0) return 0;
+size_t msa_decode_workspace_bytes(int32_t num_rows, int32_t max_seq_len, int32_t num_q_heads, int32_t topk,
+                                  int32_t ld_s) {
+  if (num_rows < 0 || max_seq_len < 0 || num_q_heads < 1 || topk < 1 || ld_s < 0) return 0;
   const size_t per_row = ws_layout(num_rows, num_q_heads, kPage * topk, ld_s).total;
-  if (num_rows < kBlockMajorRows) return per_row;
-  const size_t bm = bm_layout(num_rows, num_q_heads, topk, ld_s).total;
+  if (num_rows < kBlockMajorRows || num_rows > kBlockMajorMaxRows) return per_row;
+  const int nbmax = static_cast<int>(ceil_div(max_seq_len, kPage));
+  const size_t bm = bm_layout(num_rows, nbmax, num_q_heads, topk, ld_s).total;
   return bm > per_row ? bm : per_row;
 }
 
@@ -461,6 +479,6 @@ const char* msa_status_string(msa_status status) {
   return "MSA_ERR_UNKNOWN";
 }
 
-int32_t msa_version(void) { return 100; }
+int32_t msa_version(void) { return 200; }
 
 }  // extern "C"

@@ -187,6 +187,17 @@ __device__ __forceinline__ void load_q(const MsaAttnArgs& a, int n, int hgi, bf1
   }
 }
 
+// Same loads in every lane: lanes past the group's heads read the group's last
+// head instead of zeros (their columns are never read back), so the loads are
+// issued with no branch around them.
+__device__ __forceinline__ void load_q_any(const MsaAttnArgs& a, int n, int hgi, bf16x8 (&qb)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int h = min(lane & 15, a.num_q_heads - hgi * kHeadTile - 1);
+  const uint16_t* qp = a.q + (static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + h) * kDim + (lane >> 4) * 8;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) qb[kc] = *reinterpret_cast<const bf16x8*>(qp + kc * 32);
+}
+
 template <int KV_FP8, int SCALE_MODE, typename GetSub>
 __device__ __forceinline__ void attend_split(const MsaAttnArgs& a, MergeLds& ml, int n, int hgi, int split, int ctx,
                                              const bf16x8 (&qb)[4], GetSub get_sub) {
@@ -536,7 +547,9 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   const float sink2 = a.sinks ? a.sinks[head] * kLog2e : -INFINITY;
   const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
   const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
-  if (nsplit_n <= 1) return;
+  // per-row partials: a row of one split was written by the attention
+  // kernel; block partials: every row is written here (none listed: zeros)
+  if (!HALF && nsplit_n <= 1) return;
   MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < nsplit_n; s0 += 4 * kPer) {
     if (s0 > 0) fetch(s0);
@@ -574,16 +587,21 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
 }
 
 // Block-major attention for prefill-sized fused steps. A work item is
-// (request r, block b of r): the workgroup copies the block's K and V (one
-// contiguous run each: its 8 sub-pages are consecutive) into LDS once, finds
-// the rows of r whose selection holds b (binary search in each row's
-// ascending selection, 256 rows per pass), and every wave takes one of those
-// rows at a time: all 128 tokens' logits from LDS, the block's softmax
-// statistics, and the PV products. A row whose selection is this one block
-// gets its output here; otherwise the block's partial (max, sum, unnormalised
-// output) goes to the row's slot for the block's rank, and msa_merge_kernel
-// combines the slots in rank order, as it does for token splits.
+// (request r, block b of r) that at least one row of r selected: the
+// workgroup copies the block's K and V (one contiguous run each: its 8
+// sub-pages are consecutive) into LDS once, reads the list of (row, rank)
+// entries the top-k step wrote for the block, and every wave takes one
+// (row, head group) at a time: all 128 tokens' logits from LDS, the block's
+// softmax statistics, and the PV products. The block's partial (max, sum,
+// unnormalised output) goes to the row's slot for the block's rank, and
+// msa_merge_kernel combines the slots in rank order (one slot too), as it
+// does for token splits, and applies sinks and the LSE output. The order of
+// a list does not matter: every entry writes its own slot.
 constexpr int kBlockThreads = 256;
+constexpr int kRowChunk = 1024;                           // rows of a request examined per pass
+constexpr int kListRankShift = 18;                        // entry = row within the request | rank << 18
+constexpr uint32_t kListRowMask = (1u << kListRankShift) - 1u;
+constexpr int kListRankMax = (1 << (31 - kListRankShift)) - 1;
 
 // The block in LDS is always bf16 (fp8 codes are widened once, when staged).
 struct BlockLds {
@@ -591,10 +609,8 @@ struct BlockLds {
   __attribute__((aligned(16))) uint8_t k[kPlane];                   // 8 shuffled K tiles
   __attribute__((aligned(16))) uint8_t v[kPlane];                   // 8 dim-major V sub-pages
   float ks[kPage], vs[kPage];
-  int row[kBlockThreads];                                           // rows of this pass
-  int rank[kBlockThreads];                                          // rank of the block in each
-  int ctx[kBlockThreads];                                           // and its context length
-  int wcount[4];
+  int ent[kRowChunk];                                               // (row, rank) entries of a chunk
+  int nsel[2];                                                      // entry counters of alternate chunks
 };
 
 __device__ __forceinline__ bf16x8 lds_k_op(const BlockLds& sh, int i, int kc, int lane) {
@@ -620,146 +636,145 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
   }
   const float zscale = a.scale_log2 * kscal;
   const int pmax = a.num_subpages / kSubsPerPage - 1;
-  const int items = bk.num_reqs * a.ld_bt;
+  const int items = bk.num_reqs * bk.nbmax;
+  if (tid == 0) sh.nsel[0] = sh.nsel[1] = 0;
+  int chunk_no = 0;  // running chunk count of this workgroup: picks the counter of a chunk
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int r = item / a.ld_bt, blk = item - r * a.ld_bt;
+    const int r = item / bk.nbmax, blk = item - r * bk.nbmax;
     const int L = clampi(bk.seq_lens[r], 0, bk.len_cap);
-    const int q0 = bk.cu_q[r], q1 = bk.cu_q[r + 1];
+    const int q0 = clampi(bk.cu_q[r], 0, a.num_rows), q1 = clampi(bk.cu_q[r + 1], q0, a.num_rows);
     if (blk * kPage >= L || q1 <= q0) continue;
+    const int pos0 = L - (q1 - q0);  // absolute position of the request's first row
     const int page = clampi(a.block_table[static_cast<size_t>(r) * a.ld_bt + blk], 0, pmax);
+    const int word = blk >> 5, bit = blk & 31;
+    bool staged = false;
 
-    __syncthreads();  // the previous item's readers are done with the block
-    {
-      // 16-byte pieces of the stored planes: 32 KiB of bf16 or 16 KiB of codes
-      constexpr int kSrcPlane = kPage * kDim * (KV_FP8 ? 1 : 2);
-      constexpr int kPieces = kSrcPlane / 16 / kBlockThreads;  // 8 or 4
-      const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k_cache) +
-                                                       static_cast<size_t>(page) * kSrcPlane);
-      const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v_cache) +
-                                                       static_cast<size_t>(page) * kSrcPlane);
-      u32x4 kr[kPieces], vr[kPieces];
+    // The rows of r that selected the block, kRowChunk rows at a time: the
+    // top-k step left each row's selection as bit words (block b is bit b%32
+    // of word b/32) with the count of selected blocks below each word, so one
+    // 8-byte load per row gives both whether the row selected the block and
+    // the block's rank in the row's selection.
+    for (int c0 = q0; c0 < q1; c0 += kRowChunk, ++chunk_no) {
+      const int nc = min(kRowChunk, q1 - c0);
+      uint64_t wd[kRowChunk / kBlockThreads];
 #pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        kr[i] = __builtin_nontemporal_load(kg + tid + kBlockThreads * i);
-        vr[i] = __builtin_nontemporal_load(vg + tid + kBlockThreads * i);
+      for (int k = 0; k < kRowChunk / kBlockThreads; ++k) {
+        const int n = c0 + min(tid + kBlockThreads * k, nc - 1);
+        wd[k] = bk.row_words[static_cast<size_t>(n) * bk.row_words_ld + word];
       }
-      if constexpr (SCALE_MODE == 2) {
-        if (tid < kPage) {
-          sh.ks[tid] = a.k_scale[static_cast<size_t>(page) * kPage + tid];
-          sh.vs[tid] = a.v_scale[static_cast<size_t>(page) * kPage + tid];
+      const int cur = chunk_no & 1;
+      __syncthreads();  // the previous chunk's entries and the block are no longer read
+      if (tid == 0) sh.nsel[cur ^ 1] = 0;  // the next chunk's counter (its last reader is past this barrier)
+#pragma unroll
+      for (int k = 0; k < kRowChunk / kBlockThreads; ++k) {
+        const int i = tid + kBlockThreads * k;
+        const uint32_t lo = static_cast<uint32_t>(wd[k]), hi = static_cast<uint32_t>(wd[k] >> 32);
+        const bool hit = i < nc && ((lo >> bit) & 1u);
+        const uint64_t mask = __ballot(hit);
+        int base = 0;
+        if (lane == 0 && mask) base = atomicAdd(&sh.nsel[cur], __popcll(mask));
+        base = __shfl(base, 0);
+        if (hit) {
+          const int rank = static_cast<int>(hi) + __popc(lo & ((1u << bit) - 1u));
+          sh.ent[base + __popcll(mask & ((1ull << lane) - 1ull))] =
+              static_cast<int>((c0 - q0 + i) | (min(rank, kListRankMax) << kListRankShift));
         }
-      }
-      u32x4* kd = reinterpret_cast<u32x4*>(sh.k);
-      u32x4* vd = reinterpret_cast<u32x4*>(sh.v);
-#pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        const int q = tid + kBlockThreads * i;
-        if constexpr (KV_FP8 != 0) {  // 16 codes -> 16 bf16 values (exact), same element order
-          auto widen16 = [](u32x4 w, u32x4& lo, u32x4& hi) {
-            const u32x2 a0 = fp8x4_to_bf16x4(w.x), a1 = fp8x4_to_bf16x4(w.y);
-            const u32x2 a2 = fp8x4_to_bf16x4(w.z), a3 = fp8x4_to_bf16x4(w.w);
-            lo = u32x4{a0.x, a0.y, a1.x, a1.y};
-            hi = u32x4{a2.x, a2.y, a3.x, a3.y};
-          };
-          u32x4 lo, hi;
-          widen16(kr[i], lo, hi);
-          kd[2 * q] = lo;
-          kd[2 * q + 1] = hi;
-          widen16(vr[i], lo, hi);
-          vd[2 * q] = lo;
-          vd[2 * q + 1] = hi;
-          asm volatile("" ::: "memory");  // one piece at a time (fewer live registers)
-        } else {
-          kd[q] = kr[i];
-          vd[q] = vr[i];
-        }
-      }
-    }
-
-    for (int c0 = q0; c0 < q1; c0 += kBlockThreads) {
-      // which of these 256 rows selected the block, and at which rank: up to
-      // 32 selected ids are read in one round of 16-byte loads, longer
-      // selections by binary search
-      const int n = c0 + tid;
-      int j = -1, ctx_n = 0;
-      if (n < q1) {
-        const int32_t* srow = bk.sel + static_cast<size_t>(n) * bk.topk;
-        if (bk.vec_sel) {
-          u32x4 piece[8];
-          ctx_n = a.ctx_in[n];
-#pragma unroll
-          for (int p = 0; p < 8; ++p)
-            if (4 * p < bk.topk) piece[p] = *reinterpret_cast<const u32x4*>(srow + 4 * p);
-          const int kk = min((clampi(ctx_n, 0, kPage * bk.topk) + kPage - 1) / kPage, bk.topk);
-#pragma unroll
-          for (int p = 7; p >= 0; --p)
-            if (4 * p < bk.topk)
-#pragma unroll
-              for (int t = 3; t >= 0; --t)
-                if (4 * p + t < kk && static_cast<int>(piece[p][t]) == blk) j = 4 * p + t;
-        } else {
-          ctx_n = a.ctx_in[n];
-          const int kk = min((clampi(ctx_n, 0, kPage * bk.topk) + kPage - 1) / kPage, bk.topk);
-          int lo = 0, hi = kk;  // first rank whose block is >= blk
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (srow[mid] < blk) lo = mid + 1; else hi = mid;
-          }
-          if (lo < kk && srow[lo] == blk) j = lo;
-        }
-      }
-      const uint64_t hit = __ballot(j >= 0);
-      const int before = __popcll(hit & ((1ull << lane) - 1ull));
-      if (lane == 0) sh.wcount[wave] = __popcll(hit);
-      __syncthreads();  // counts, and the block's K / V in LDS
-      int base = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int c = sh.wcount[w];
-        base += (w < wave) ? c : 0;
-        total += c;
-      }
-      if (j >= 0) {
-        sh.row[base + before] = n;
-        sh.rank[base + before] = j;
-        sh.ctx[base + before] = ctx_n;
       }
       __syncthreads();
-
-      // each wave takes every fourth (row, head group); the next one's query
-      // is requested before the current one's products
+      const int total = sh.nsel[cur];
+      if (total == 0) continue;
+      if (!staged) {  // the block's K and V, once per item, only when some row selected it
+        staged = true;
+        {
+          // 16-byte pieces of the stored planes: 32 KiB of bf16 or 16 KiB of codes
+          constexpr int kSrcPlane = kPage * kDim * (KV_FP8 ? 1 : 2);
+          constexpr int kPieces = kSrcPlane / 16 / kBlockThreads;  // 8 or 4
+          const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k_cache) +
+                                                           static_cast<size_t>(page) * kSrcPlane);
+          const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v_cache) +
+                                                           static_cast<size_t>(page) * kSrcPlane);
+          u32x4 kr[kPieces], vr[kPieces];
+#pragma unroll
+          for (int i = 0; i < kPieces; ++i) {
+            kr[i] = __builtin_nontemporal_load(kg + tid + kBlockThreads * i);
+            vr[i] = __builtin_nontemporal_load(vg + tid + kBlockThreads * i);
+          }
+          if constexpr (SCALE_MODE == 2) {
+            if (tid < kPage) {
+              sh.ks[tid] = a.k_scale[static_cast<size_t>(page) * kPage + tid];
+              sh.vs[tid] = a.v_scale[static_cast<size_t>(page) * kPage + tid];
+            }
+          }
+          u32x4* kd = reinterpret_cast<u32x4*>(sh.k);
+          u32x4* vd = reinterpret_cast<u32x4*>(sh.v);
+#pragma unroll
+          for (int i = 0; i < kPieces; ++i) {
+            const int q = tid + kBlockThreads * i;
+            if constexpr (KV_FP8 != 0) {  // 16 codes -> 16 bf16 values (exact), same element order
+              auto widen16 = [](u32x4 w, u32x4& lo, u32x4& hi) {
+                const u32x2 a0 = fp8x4_to_bf16x4(w.x), a1 = fp8x4_to_bf16x4(w.y);
+                const u32x2 a2 = fp8x4_to_bf16x4(w.z), a3 = fp8x4_to_bf16x4(w.w);
+                lo = u32x4{a0.x, a0.y, a1.x, a1.y};
+                hi = u32x4{a2.x, a2.y, a3.x, a3.y};
+              };
+              u32x4 lo, hi;
+              widen16(kr[i], lo, hi);
+              kd[2 * q] = lo;
+              kd[2 * q + 1] = hi;
+              widen16(vr[i], lo, hi);
+              vd[2 * q] = lo;
+              vd[2 * q + 1] = hi;
+              asm volatile("" ::: "memory");  // one piece at a time (fewer live registers)
+            } else {
+              kd[q] = kr[i];
+              vd[q] = vr[i];
+            }
+          }
+        }
+        __syncthreads();
+      }
+      // each wave takes every fourth (row, head group)
       const int nent = total * a.num_hgroups;
       auto entry_q = [&](int e, bf16x8 (&qv)[4]) {
         const int ee = min(e, max(nent - 1, 0));
-        load_q(a, sh.row[ee / a.num_hgroups], ee % a.num_hgroups, qv);
+        const int rl = min(static_cast<int>(static_cast<uint32_t>(sh.ent[ee / a.num_hgroups]) & kListRowMask),
+                           q1 - q0 - 1);
+        load_q_any(a, q0 + rl, ee % a.num_hgroups, qv);
       };
-      bf16x8 qnext[4];
-      if (wave < nent) entry_q(wave, qnext);
-      for (int e = wave; e < nent; e += 4) {
-        const int row = sh.row[e / a.num_hgroups], rank = sh.rank[e / a.num_hgroups];
+      // The query of the next entry is requested before the current entry's
+      // products and its partial stores, and every entry issues the same
+      // loads and stores, so the wait for that query leaves the stores in
+      // flight. The first entry is peeled off so that the loop is entered with
+      // the counters in the same state as from its own back edge.
+      bf16x8 qa[4], qb[4];
+      auto do_entry = [&](int e, const bf16x8 (&qv)[4]) {
+        const uint32_t ent = static_cast<uint32_t>(sh.ent[e / a.num_hgroups]);
+        const int rloc = min(static_cast<int>(ent & kListRowMask), q1 - q0 - 1);
+        const int row = q0 + rloc, rank = min(static_cast<int>(ent >> kListRankShift), bk.topk - 1);
         const int hgi = e - (e / a.num_hgroups) * a.num_hgroups;
-        bf16x8 qb[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) qb[kc] = qnext[kc];
-        if (e + 4 < nent) entry_q(e + 4, qnext);
-        const int nheads = min(kHeadTile, a.num_q_heads - hgi * kHeadTile);
-        const int ctx = clampi(sh.ctx[e / a.num_hgroups], 0, kPage * bk.topk);
-        const int kk = (ctx + kPage - 1) / kPage;
-        const int nval = min(kPage, ctx - rank * kPage);  // tokens of the block the row sees
-        const float sink2 =
-            (a.sinks && (lane & 15) < nheads) ? a.sinks[hgi * kHeadTile + (lane & 15)] * kLog2e : -INFINITY;
+        const int vis = pos0 + rloc + 1;  // keys the row sees
+        const int nval = clampi(vis - blk * kPage, 1, kPage);  // tokens of this block it sees
         // pass 1: the block's 128 logits (S^T per sub-page: token rows, head
         // columns) and their max; the empty asm keeps the compiler from
-        // pulling every sub-page's LDS operands into registers at once
+        // pulling every sub-page's LDS operands into registers at once; the
+        // next sub-page's operands are read while the current one's products
+        // run
         const bool part_blk = nval < kPage;
         float z[8][4];
         float mloc = -INFINITY;
+        bf16x8 kop[2][4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kop[0][kc] = lds_k_op(sh, 0, kc, lane);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          if (i + 1 < 8) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) kop[(i + 1) & 1][kc] = lds_k_op(sh, i + 1, kc, lane);
+          }
           f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc) sacc = mfma_16x16x32(lds_k_op(sh, i, kc, lane), qb[kc], sacc);
+          for (int kc = 0; kc < 4; ++kc) sacc = mfma_16x16x32(kop[i & 1][kc], qv[kc], sacc);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int tok = i * kSub + tok0 + t;
@@ -775,70 +790,89 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         f32x4 o[8];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // two sub-pages per 16x16x32 product: K index 8g+j of lane group g
+        // is token 4g+j of the first sub-page for j < 4 and token 4g+j-4 of
+        // the second for j >= 4, in the V operand and the probabilities alike
+        i16x4 vreg[2][2][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float e[4];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            e[t] = fast_exp2(z[i][t] - m);
-            lsum += e[t];
-            if constexpr (SCALE_MODE == 2) e[t] *= sh.vs[i * kSub + tok0 + t];
+          for (int dt = 0; dt < 8; ++dt) vreg[0][h][dt] = lds_v_op(sh, h, dt, lane);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const int b = (i >> 1) & 1;
+          if (i + 2 < 8) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int dt = 0; dt < 8; ++dt) vreg[b ^ 1][h][dt] = lds_v_op(sh, i + 2 + h, dt, lane);
           }
-          const i16x4 p = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3])}));
-          const bool vmask = part_blk && (i * kSub + tok0 + 3 >= nval);  // slots past the row's tokens
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int tok = (i + (j >> 2)) * kSub + tok0 + (j & 3);
+            e[j] = fast_exp2(z[i + (j >> 2)][j & 3] - m);
+            lsum += e[j];
+            if constexpr (SCALE_MODE == 2) e[j] *= sh.vs[tok];
+          }
+          const bf16x8 p = __builtin_bit_cast(bf16x8, (u32x4{pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3]),
+                                                             pk_bf16(e[4], e[5]), pk_bf16(e[6], e[7])}));
+          const bool vmask = part_blk && ((i + 1) * kSub + tok0 + 3 >= nval);  // slots past the row's tokens
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            i16x4 vop = lds_v_op(sh, i, dt, lane);
+            i16x4 v0 = vreg[b][0][dt], v1 = vreg[b][1][dt];
             if (vmask) {  // they can hold anything, even NaN codes
 #pragma unroll
-              for (int t = 0; t < 4; ++t)
-                if (i * kSub + tok0 + t >= nval) vop[t] = 0;
+              for (int t = 0; t < 4; ++t) {
+                if (i * kSub + tok0 + t >= nval) v0[t] = 0;
+                if ((i + 1) * kSub + tok0 + t >= nval) v1[t] = 0;
+              }
             }
-            o[dt] = mfma_16x16x16(vop, p, o[dt]);
+            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+            o[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, (u32x4{w0.x, w0.y, w1.x, w1.y})), p, o[dt]);
           }
           asm volatile("" ::: "memory");
         }
         const float l = sum_across_rows(lsum);
+        // the block's partial in the row's slot for the block's rank, the
+        // accumulator in fp16: a scalar V scale is folded in, then the head's
+        // accumulator is scaled by 2^-e so that its largest magnitude is below
+        // 1, and e is folded into the log2-domain max and the sum
+        // (2^(m+e) * l*2^-e = 2^m * l), so the merge weighs the slots exactly
+        // as it weighs fp32 partials. Every path stores the same instructions
+        // (the four lanes of a head store the same m and l), so the wait for
+        // the next entry's query never has to wait for these stores.
         const int head = lane & 15;
-        if (kk <= 1) {  // the row's only block: its output
-          const float den = l + fast_exp2(sink2 - m);
-          const float inv = vscal / den;
-          if (head < nheads) {
-            uint16_t* orow = a.out + (static_cast<size_t>(row) * a.num_q_heads + hgi * kHeadTile + head) * kDim;
+        float mx = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-              *reinterpret_cast<u32x2*>(orow + dt * 16 + tok0) =
-                  u32x2{pk_bf16(o[dt][0] * inv, o[dt][1] * inv), pk_bf16(o[dt][2] * inv, o[dt][3] * inv)};
-            }
-            if (a.lse_out && lane < 16)
-              a.lse_out[static_cast<size_t>(row) * a.num_q_heads + hgi * kHeadTile + head] = (m + log2f(l)) * kLn2;
-          }
-        } else {
-          // partial of the block's rank, the accumulator in fp16: a scalar V
-          // scale is folded in, then the head's accumulator is scaled by 2^-e
-          // so that its largest magnitude is below 1 and e is folded into the
-          // log2-domain max and the sum (2^(m+e) * l*2^-e = 2^m * l), so the
-          // merge weighs the slots exactly as it weighs fp32 partials
-          float mx = 0.f;
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
+          for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fabsf(o[dt][t]));
+        mx = max_across_rows(mx) * fabsf(vscal);
+        const int ex = (mx > 0.f) ? clampi(__builtin_amdgcn_frexp_expf(mx), -kHalfExpRange, kHalfExpRange) : 0;
+        const float f = ldexpf(vscal, -ex);
+        float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kHalfPartStride;
+        part[head] = m + static_cast<float>(ex);
+        part[kHeadTile + head] = ldexpf(l, -ex);
+        uint32_t* acc = reinterpret_cast<uint32_t*>(part + 2 * kHeadTile) + (head * kDim + tok0) / 2;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fabsf(o[dt][t]));
-          mx = max_across_rows(mx) * fabsf(vscal);
-          const int e = (mx > 0.f) ? clampi(__builtin_amdgcn_frexp_expf(mx), -kHalfExpRange, kHalfExpRange) : 0;
-          const float f = ldexpf(vscal, -e);
-          float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kHalfPartStride;
-          if (lane < 16) {
-            part[head] = m + static_cast<float>(e);
-            part[kHeadTile + head] = ldexpf(l, -e);
-          }
-          uint32_t* acc = reinterpret_cast<uint32_t*>(part + 2 * kHeadTile) + (head * kDim + tok0) / 2;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            *reinterpret_cast<u32x2*>(acc + dt * 8) = u32x2{pk_f16(o[dt][0] * f, o[dt][1] * f), pk_f16(o[dt][2] * f, o[dt][3] * f)};
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<u32x2*>(acc + dt * 8) = u32x2{pk_f16(o[dt][0] * f, o[dt][1] * f), pk_f16(o[dt][2] * f, o[dt][3] * f)};
+      };
+      if (wave < nent) {
+        // two query buffers in turn (no register copies, which would wait
+        // for the loads early)
+        entry_q(wave, qa);
+        entry_q(wave + 4, qb);  // clamped to the last entry: always issued
+        do_entry(wave, qa);
+        for (int e = wave + 4; e < nent; e += 8) {
+          entry_q(e + 4, qa);
+          do_entry(e, qb);
+          if (e + 4 >= nent) break;
+          entry_q(e + 8, qb);
+          do_entry(e + 4, qa);
         }
       }
-      __syncthreads();  // the row list is reused by the next pass
     }
   }
 }

@@ -207,6 +207,13 @@ struct MsaTopkArgs {
   int32_t* table;
   int32_t* ctx;
   int32_t* sel;        // may be null
+  // Optional selection words (block-major attention): row n's kept blocks
+  // as bits, block b at bit b%32 of word b/32, each 64-bit entry holding the
+  // word in its low half and the number of kept blocks below the word in its
+  // high half: row_words[n * row_words_ld + w] for every w < row_words_ld.
+  // Null: not written.
+  uint64_t* row_words;
+  int32_t row_words_ld;
   int32_t ld_s;
   int32_t ld_bt;
   int32_t topk;
@@ -214,6 +221,7 @@ struct MsaTopkArgs {
   int32_t num_reqs;
 };
 hipError_t msa_launch_topk(const MsaTopkArgs& a, hipStream_t s);
+
 
 // Attention over a page-16 table. Table mode: table_in / ctx_in give each
 // row's sub-pages. Fused mode (scores != null): every workgroup selects its
@@ -280,18 +288,19 @@ hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, h
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s);
 // Block-major attention (prefill-sized fused steps): one workgroup per
 // (request, block) serves every row of the request that selected the block,
-// from the selection written by the top-k kernel (sel ascending per row, ctx).
-// Uses from MsaAttnArgs: q, caches and scales, block_table, ld_bt, ctx_in,
-// out, lse_out, sinks, partials (nsplit = topk slots per row and head group),
-// num_q_heads, num_hgroups, num_subpages, scale_log2.
+// found from the selection words written by the top-k kernel.
+// Uses from MsaAttnArgs: q, caches and scales, block_table, ld_bt, out,
+// lse_out, sinks, partials (nsplit = topk slots per row and head group),
+// num_rows, num_q_heads, num_hgroups, num_subpages, scale_log2.
 struct MsaBlockArgs {
-  const int32_t* sel;        // [N][topk] selected blocks, ascending, -1 tail
+  const uint64_t* row_words; // [N][row_words_ld] selection words written by the top-k kernel
   const int32_t* cu_q;       // [R+1] query-row prefix
   const int32_t* seq_lens;   // [R]
+  int32_t row_words_ld;
+  int32_t nbmax;             // blocks per request covered by the items
   int32_t num_reqs;
   int32_t topk;
   int32_t len_cap;
-  int32_t vec_sel;           // topk <= 32, a multiple of 4, and sel 16-byte aligned: rows read whole
 };
 hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, int kv_dtype, int scale_mode,
                                  int num_wgs, hipStream_t s);

@@ -6,7 +6,8 @@
 //
 // One 256-thread workgroup per query row: the row's scores are read once into
 // LDS as keys, selected by select_row (msa_select.h), and every kept block j
-// (ascending) is expanded to its 8 sub-pages 8*page + i.
+// (ascending) is expanded to its 8 sub-pages 8*page + i. For block-major
+// attention the kernel also writes the row's kept blocks as bit words.
 #include "msa_select.h"
 
 using namespace msa;
@@ -26,6 +27,8 @@ __global__ __launch_bounds__(kSelectThreads) void msa_topk_kernel(MsaTopkArgs a)
   int32_t* trow = a.table + static_cast<size_t>(n) * (8 * a.topk);
   int32_t* selrow = a.sel ? a.sel + static_cast<size_t>(n) * a.topk : nullptr;
 
+  __shared__ uint32_t s_bits[kMaxBlocksPerRow / 32];  // kept blocks as bits, for the selection words
+  if (a.row_words && tid < kMaxBlocksPerRow / 32) s_bits[tid] = 0u;
   for (int e = tid; e < nb; e += kSelectThreads) s_key[e] = order_key(srow[e]);
   __syncthreads();
 
@@ -35,7 +38,18 @@ __global__ __launch_bounds__(kSelectThreads) void msa_topk_kernel(MsaTopkArgs a)
 #pragma unroll
     for (int i = 0; i < 8; ++i) trow[8 * pos + i] = sub0 + i;
     if (selrow) selrow[pos] = e;
+    if (a.row_words) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
   }, &ctx, [] {});
+
+  if (a.row_words) {  // every word of the row, with the kept count below it
+    __syncthreads();
+    for (int w = tid; w < a.row_words_ld; w += kSelectThreads) {
+      uint32_t below = 0, bits = 0;
+      for (int u = 0; u < min(w, kMaxBlocksPerRow / 32); ++u) below += __popc(s_bits[u]);
+      if (w < kMaxBlocksPerRow / 32) bits = s_bits[w];
+      a.row_words[static_cast<size_t>(n) * a.row_words_ld + w] = (static_cast<uint64_t>(below) << 32) | bits;
+    }
+  }
 
   // zero tail of the table row, -1 tail of the selection, never past 8*topk
   for (int m = 8 * kk + tid; m < 8 * a.topk; m += kSelectThreads) trow[m] = 0;

@@ -208,13 +208,14 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  *   workspace. ld_s >= ceil(max_seq_len/128).
  *   workspace: >= msa_workspace_bytes(num_rows, num_q_heads, 128*topk,
  *   block_scores ? 0 : ld_s) bytes (NULL allowed when that is 0).
- *   Launches of at least 2048 rows (prefill-sized) given a workspace of
- *   msa_decode_workspace_bytes(num_rows, num_q_heads, topk, block_scores ? 0
- *   : ld_s) bytes take the block-major path instead: the top-k step runs on
- *   its own (4 launches), then one workgroup per (request, selected block)
- *   attends every row that chose the block from one copy of its K/V, and the
- *   per-block partials are merged. Each partial keeps its max and sum in fp32
- *   and its 16x128 accumulator in fp16, scaled by a power of two so that its
+ *   Launches of 2048 to 262144 rows (prefill-sized) given a workspace of
+ *   msa_decode_workspace_bytes(num_rows, max_seq_len, num_q_heads, topk,
+ *   block_scores ? 0 : ld_s) bytes take the block-major path instead: the
+ *   top-k step runs on its own and also leaves each row's selection as bit
+ *   words (4 launches in all); then one workgroup per (request, block) that
+ *   some row of the request selected attends every such row from one copy of
+ *   the block's K/V, and the per-block partials are merged. Each partial
+ *   keeps its max and sum in fp32 and its 16x128 accumulator in fp16, scaled by a power of two so that its
  *   largest magnitude is below 1 (the error this adds to an output is at most
  *   2^-11 of the largest |V| entry the row attends). Same results up to that
  *   and rounding order; with the smaller workspace the per-row path runs.
@@ -319,13 +320,15 @@ size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ct
 
 /*
  * msa_decode_workspace_bytes — workspace that lets msa_sparse_decode(_ex)
- * take the block-major path on launches of at least 2048 rows: per row,
- * num_q_heads/16 (rounded up) x topk partials of 4224 bytes plus topk block
- * ids, and the scores when ld_s > 0. For fewer rows it equals
- * msa_workspace_bytes(num_rows, num_q_heads, 128*topk, ld_s). Returns 0 for
- * invalid arguments.
+ * take the block-major path on launches of 2048 to 262144 rows (the batch's
+ * num_rows and max_seq_len): per row, num_q_heads/16 (rounded up) x topk
+ * partials of 4224 bytes and one 8-byte selection word per 32 blocks of
+ * ceil(max_seq_len/128); and the scores when ld_s > 0. For other row counts
+ * it equals msa_workspace_bytes(num_rows, num_q_heads, 128*topk, ld_s).
+ * Returns 0 for invalid arguments.
  */
-size_t msa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t topk, int32_t ld_s);
+size_t msa_decode_workspace_bytes(int32_t num_rows, int32_t max_seq_len, int32_t num_q_heads, int32_t topk,
+                                  int32_t ld_s);
 
 /* Human-readable name of a status code (static storage). */
 const char* msa_status_string(msa_status status);

@@ -44,7 +44,7 @@ def test_block_major_step(gpu_lib, case, with_extras):
     print(f"[block-major] case {case} rows={b.num_rows} extras={with_extras}", flush=True)
     d = H.upload(b)
     o = H.alloc_decode(d)
-    wsb = msa.msa_decode_workspace_bytes(b.num_rows, hq, topk, 0)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0)
     assert wsb > o.wsb
     o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")  # garbage on entry
     o.wsb = wsb
@@ -87,7 +87,7 @@ def test_block_major_extreme_values(gpu_lib, vexp):
     print(f"[block-major] V x 2^{vexp} rows={b.num_rows}", flush=True)
     d = H.upload(b)
     o = H.alloc_decode(d)
-    wsb = msa.msa_decode_workspace_bytes(b.num_rows, hq, topk, 0)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0)
     o.ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
     o.wsb = wsb
     H.run_decode(d, o)
