@@ -55,6 +55,9 @@ def parse():
                         "the traffic summary under profiles/")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="turn a rocprofv3 --kernel-trace --stats csv output into a summary under profiles/")
+    p.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                   help="turn a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE output "
+                        "into a per-kernel MFMA-utilisation summary under profiles/")
     return p.parse_args()
 
 
@@ -186,6 +189,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.workload, args.index, args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.workload, args.index, args.summarize_mfma)
         return
 
     import numpy as np
@@ -538,6 +544,39 @@ def summarize_trace(workload, index, trace_dir):
             lines.append(f"| {_short(rec['Name'])} | {rec['Calls']} | {float(rec['AverageNs']) / 1e3:.2f} | "
                          f"{float(rec['MinNs']) / 1e3:.2f} | {float(rec['MaxNs']) / 1e3:.2f} |")
     with open(os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+MFMA_CMD = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+            "-d <out> -o run -- python3 -u bench.py --workload {workload}{index} --steps 3 --warmup 1 --eager "
+            "--no-cpu-baseline")
+NUM_XCD, NUM_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_mfma(workload, index, pmc_dir):
+    """Per-kernel MFMA busy fraction from one --pmc pass: the MFMA busy cycles
+    summed over every SIMD, divided by the kernel's active cycles (GRBM_GUI_ACTIVE
+    is summed over the 8 XCDs, so it is divided by 8) times the 1024 SIMDs."""
+    import statistics
+    name = tag(workload, index)
+    per = {}
+    for k, c, v in _counter_rows(pmc_dir):
+        if "msa_" in k:
+            per.setdefault(_short(k), {}).setdefault(c, []).append(v)
+    lines = [f"# MFMA utilisation per kernel, {name} workload", "", "Command:", "",
+             "    " + MFMA_CMD.format(workload=workload, index=_index_flag(index)),
+             f"    python3 bench.py --workload {workload}{_index_flag(index)} --summarize-mfma <out>", "",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), medians over "
+             "dispatches; active us = GRBM_GUI_ACTIVE / 8 at 2.4 GHz.", "",
+             "| kernel | dispatches | active us | MFMA busy |", "|---|---|---|---|"]
+    for k, cs in sorted(per.items()):
+        if "GRBM_GUI_ACTIVE" not in cs or "SQ_VALU_MFMA_BUSY_CYCLES" not in cs:
+            continue
+        act = statistics.median(cs["GRBM_GUI_ACTIVE"]) / NUM_XCD
+        busy = statistics.median(cs["SQ_VALU_MFMA_BUSY_CYCLES"])
+        lines.append(f"| {k} | {len(cs['GRBM_GUI_ACTIVE'])} | {act / 2400:.1f} | "
+                     f"{100.0 * busy / max(act * NUM_SIMD, 1.0):.1f}% |")
+    with open(os.path.join(ROOT, "profiles", f"mfma_{name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
 
