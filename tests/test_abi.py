@@ -28,7 +28,7 @@ def test_header_declares_the_path_entry_points():
     for want in ("msa_build_metadata", "msa_index_score", "msa_topk_block_table",
                  "msa_sparse_paged_attn", "msa_sparse_decode", "msa_index_score_ex",
                  "msa_sparse_paged_attn_ex", "msa_sparse_decode_ex", "msa_cache_insert",
-                 "msa_cache_insert_ex", "msa_workspace_bytes"):
+                 "msa_cache_insert_ex", "msa_workspace_bytes", "msa_decode_workspace_bytes"):
         assert want in names
 
 
@@ -61,6 +61,27 @@ def test_workspace_bytes_monotone_and_aligned():
     assert 0 < a < b <= c
     assert a % 256 == 0 and b % 256 == 0
     assert msa.msa_workspace_bytes(-1, 16, 1, 0) == 0
+
+
+def test_decode_workspace_bytes_block_major_layout():
+    # below 2048 rows the fused step's per-row workspace; from 2048 rows the
+    # block-major one: per row and head group, topk slots of 32 fp32 (m, l)
+    # and 16x128 fp16, plus one 8-byte selection word per 32 blocks, each
+    # region rounded up to 256 bytes, then the scores when ld_s > 0
+    def up(x):
+        return (x + 255) // 256 * 256
+    assert msa.msa_decode_workspace_bytes(100, 32768, 16, 32, 0) == msa.msa_workspace_bytes(100, 16, 128 * 32, 0)
+    n, L, hq, topk, ld_s = 8198, 32768, 16, 32, 256
+    slots = up(n * 1 * topk * (32 * 4 + 16 * 128 * 2))
+    words = up(n * ((L // 128 + 31) // 32) * 8)
+    got = msa.msa_decode_workspace_bytes(n, L, hq, topk, 0)
+    assert got == max(slots + words, msa.msa_workspace_bytes(n, hq, 128 * topk, 0))
+    with_scores = msa.msa_decode_workspace_bytes(n, L, hq, topk, ld_s)
+    assert with_scores == max(slots + words + up(n * ld_s * 4), msa.msa_workspace_bytes(n, hq, 128 * topk, ld_s))
+    # two head groups double the slots
+    assert msa.msa_decode_workspace_bytes(n, L, 24, topk, 0) >= 2 * slots
+    for bad in ((-1, L, hq, topk, 0), (n, -1, hq, topk, 0), (n, L, 0, topk, 0), (n, L, hq, 0, 0), (n, L, hq, topk, -1)):
+        assert msa.msa_decode_workspace_bytes(*bad) == 0
 
 
 @pytest.fixture(autouse=True)

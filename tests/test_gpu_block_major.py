@@ -99,3 +99,30 @@ def test_block_major_extreme_values(gpu_lib, vexp):
     ref = O.attention_from_table(b, table, ctx, rows)
     err = np.abs(out[rows] - ref).max() / 2.0 ** vexp
     assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err} (in units of 2^{vexp})"
+
+
+def test_block_major_scores_in_workspace(gpu_lib):
+    """No caller score buffer: the block-major workspace also holds the
+    scores (ld_s > 0 in msa_decode_workspace_bytes); same outputs, tables and
+    context lengths as with a caller buffer."""
+    L, ql, topk, hq = [7000, 5000, 300], [1200, 900, 1], 8, 16
+    b = syn.make_batch("bm_ws", 850, L, ql, topk=topk, num_q_heads=hq, kv_dtype=syn.KV_BF16,
+                       scale_mode=syn.SCALE_NONE)
+    print(f"[block-major] scores in workspace rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    outs = []
+    for with_scores in (True, False):
+        o = H.alloc_decode(d)
+        wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0 if with_scores else b.ld_s)
+        o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+        o.wsb = wsb
+        H.run_decode(d, o, with_scores=with_scores)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0].table, outs[1].table) and torch.equal(outs[0].ctx, outs[1].ctx)
+    assert torch.equal(outs[0].out, outs[1].out)
+    ctx = outs[0].ctx.cpu().numpy()
+    rows = sorted(set(_sample_rows(b, 12, 851)))
+    ref = O.attention_from_table(b, outs[0].table.cpu().numpy(), ctx, rows)
+    err = np.abs(H.bf16_to_np(outs[1].out)[rows] - ref).max()
+    assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err}"
