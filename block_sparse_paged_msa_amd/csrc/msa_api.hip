@@ -5,7 +5,7 @@
 #include <atomic>
 
 #include "msa.h"
-#include "msa_internal.h"
+#include "msa_kernels.h"
 
 namespace {
 

@@ -17,7 +17,7 @@
 // An FP8 index cache (the optional FP8 index storage named on the vLLM PR
 // #54682 page, 相关 PRs) takes each token's index key by the per-token rule:
 // s = max|x| / 448 over its 128 values, codes e4m3fn RNE of clamp(x / s).
-#include "msa_internal.h"
+#include "msa_kernels.h"
 
 using namespace msa;
 

@@ -10,7 +10,7 @@
 // so the caller receives the selection in ascending block-id order.
 #pragma once
 
-#include "msa_internal.h"
+#include "msa_kernels.h"
 
 namespace msa {
 
