@@ -928,7 +928,7 @@ hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, in
 }
 
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {
-  if (a.nsplit <= 1) return hipSuccess;
+  if (a.nsplit <= 1 && !a.half_partials) return hipSuccess;  // block partials: always merged, one slot too
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_q_heads;
   const int32_t* ctxp = a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in;
   if (a.half_partials)

@@ -26,6 +26,8 @@ CASES = [
     ([16384, 16384, 6000, 9000], [1, 1, 2100, 1000], 16, 16, syn.KV_BF16, syn.SCALE_NONE),
     ([100, 4000, 20000, 300], [100, 1800, 3, 250], 8, 16, syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD),
     ([3000, 12000], [1500, 600], 24, 24, syn.KV_FP8, syn.SCALE_SCALAR),
+    # top-k 1: every row has a single slot, merged (normalised) by the merge kernel
+    ([5000, 3000], [1500, 700], 1, 16, syn.KV_BF16, syn.SCALE_NONE),
 ]
 
 
