@@ -618,8 +618,15 @@ __device__ __forceinline__ bf16x8 lds_k_op(const BlockLds& sh, int i, int kc, in
   return *reinterpret_cast<const bf16x8*>(sh.k + 2 * e);
 }
 
+// V sub-pages sit in LDS dim-major ([128 dims][16 tokens], 32 B a dim) with
+// the four 8-byte token groups of dim d stored at position g ^ ((d >> 2) & 3):
+// the 16 lanes that read one token group of 16 consecutive dims then hit 16
+// different bank pairs instead of 4.
+__device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
+
 __device__ __forceinline__ i16x4 lds_v_op(const BlockLds& sh, int i, int dt, int lane) {
-  const int e = i * (kSub * kDim) + (dt * 16 + (lane & 15)) * kSub + (lane >> 4) * 4;
+  const int d = dt * 16 + (lane & 15);
+  const int e = i * (kSub * kDim) + d * kSub + 4 * ((lane >> 4) ^ v_swz(d));
   return *reinterpret_cast<const i16x4*>(sh.v + 2 * e);
 }
 
@@ -723,12 +730,24 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
               kd[2 * q] = lo;
               kd[2 * q + 1] = hi;
               widen16(vr[i], lo, hi);
-              vd[2 * q] = lo;
-              vd[2 * q + 1] = hi;
+              // a whole dim (16 tokens): token group p of the stored row is
+              // group p ^ f of the dim
+              const int f = v_swz(q);
+              const u32x2 c0 = {lo.x, lo.y}, c1 = {lo.z, lo.w}, c2 = {hi.x, hi.y}, c3 = {hi.z, hi.w};
+              const u32x2 t0 = (f & 1) ? c1 : c0, t1 = (f & 1) ? c0 : c1;
+              const u32x2 t2 = (f & 1) ? c3 : c2, t3 = (f & 1) ? c2 : c3;
+              const u32x2 o0 = (f & 2) ? t2 : t0, o1 = (f & 2) ? t3 : t1;
+              const u32x2 o2 = (f & 2) ? t0 : t2, o3 = (f & 2) ? t1 : t3;
+              vd[2 * q] = u32x4{o0.x, o0.y, o1.x, o1.y};
+              vd[2 * q + 1] = u32x4{o2.x, o2.y, o3.x, o3.y};
               asm volatile("" ::: "memory");  // one piece at a time (fewer live registers)
             } else {
               kd[q] = kr[i];
-              vd[q] = vr[i];
+              // half hh of dim row q/2 (groups 2hh, 2hh+1) goes to half
+              // hh ^ (f >> 1) of the row, its two groups swapped when f & 1
+              const int f = v_swz(q >> 1);
+              const u32x4 w = vr[i];
+              vd[(q & ~1) | ((q & 1) ^ (f >> 1))] = (f & 1) ? u32x4{w.z, w.w, w.x, w.y} : w;
             }
           }
         }

@@ -28,6 +28,8 @@ CASES = [
     ([3000, 12000], [1500, 600], 24, 24, syn.KV_FP8, syn.SCALE_SCALAR),
     # top-k 1: every row has a single slot, merged (normalised) by the merge kernel
     ([5000, 3000], [1500, 700], 1, 16, syn.KV_BF16, syn.SCALE_NONE),
+    # bf16 K/V with per-token-head scales
+    ([6000, 2500], [1400, 900], 12, 16, syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD),
 ]
 
 
