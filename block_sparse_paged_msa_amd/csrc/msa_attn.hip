@@ -131,10 +131,17 @@ __device__ __forceinline__ void attend_pair(WaveState& st, SubPage<KV_FP8, SCALE
     e1[i] = fast_exp2(z1[i] - m_new);
     psum += e0[i] + e1[i];
   }
-  const i16x4 p0 = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e0[0] * sp[0].vs[0], e0[1] * sp[0].vs[1]),
-                                                    pk_bf16(e0[2] * sp[0].vs[2], e0[3] * sp[0].vs[3])}));
-  const i16x4 p1 = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e1[0] * sp[1].vs[0], e1[1] * sp[1].vs[1]),
-                                                    pk_bf16(e1[2] * sp[1].vs[2], e1[3] * sp[1].vs[3])}));
+  if constexpr (SCALE_MODE == 2) {
+    // per-token V scales; a hidden token's scale can be anything (even NaN),
+    // so its probability is set to zero rather than scaled
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e0[i] = (tok0 + i < nval0) ? e0[i] * sp[0].vs[i] : 0.f;
+      e1[i] = (tok0 + i < nval1) ? e1[i] * sp[1].vs[i] : 0.f;
+    }
+  }
+  const i16x4 p0 = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e0[0], e0[1]), pk_bf16(e0[2], e0[3])}));
+  const i16x4 p1 = __builtin_bit_cast(i16x4, (u32x2{pk_bf16(e1[0], e1[1]), pk_bf16(e1[2], e1[3])}));
   st.l = st.l * alpha + psum;
   st.m = m_new;
   // V slots past the context can hold anything (even NaN codes): zero them so
@@ -654,6 +661,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
     if (blk * kPage >= L || q1 <= q0) continue;
     const int pos0 = L - (q1 - q0);  // absolute position of the request's first row
     const int page = clampi(a.block_table[static_cast<size_t>(r) * a.ld_bt + blk], 0, pmax);
+    const int nreq = min(kPage, L - blk * kPage);  // tokens of the block the request holds
     const int word = blk >> 5, bit = blk & 31;
     bool staged = false;
 
@@ -710,7 +718,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
           if constexpr (SCALE_MODE == 2) {
             if (tid < kPage) {
               sh.ks[tid] = a.k_scale[static_cast<size_t>(page) * kPage + tid];
-              sh.vs[tid] = a.v_scale[static_cast<size_t>(page) * kPage + tid];
+              sh.vs[tid] = (tid < nreq) ? a.v_scale[static_cast<size_t>(page) * kPage + tid] : 0.f;
             }
           }
           u32x4* kd = reinterpret_cast<u32x4*>(sh.k);
@@ -730,6 +738,17 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
               kd[2 * q] = lo;
               kd[2 * q + 1] = hi;
               widen16(vr[i], lo, hi);
+              if (nreq < kPage) {  // slots past the request's last token can hold anything
+                const int t0 = (q >> 7) * kSub;  // first token of the row's sub-page
+                uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                  if (t0 + 2 * u >= nreq) w[u] &= 0xffff0000u;
+                  if (t0 + 2 * u + 1 >= nreq) w[u] &= 0x0000ffffu;
+                }
+                lo = u32x4{w[0], w[1], w[2], w[3]};
+                hi = u32x4{w[4], w[5], w[6], w[7]};
+              }
               // a whole dim (16 tokens): token group p of the stored row is
               // group p ^ f of the dim
               const int f = v_swz(q);
@@ -746,7 +765,17 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
               // half hh of dim row q/2 (groups 2hh, 2hh+1) goes to half
               // hh ^ (f >> 1) of the row, its two groups swapped when f & 1
               const int f = v_swz(q >> 1);
-              const u32x4 w = vr[i];
+              u32x4 w = vr[i];
+              if (nreq < kPage) {  // slots past the request's last token can hold anything
+                const int t0 = (q >> 8) * kSub + 8 * (q & 1);  // first token of the piece
+                uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  if (t0 + 2 * u >= nreq) x[u] &= 0xffff0000u;
+                  if (t0 + 2 * u + 1 >= nreq) x[u] &= 0x0000ffffu;
+                }
+                w = u32x4{x[0], x[1], x[2], x[3]};
+              }
               vd[(q & ~1) | ((q & 1) ^ (f >> 1))] = (f & 1) ? u32x4{w.z, w.w, w.x, w.y} : w;
             }
           }
@@ -836,18 +865,11 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
           }
           const bf16x8 p = __builtin_bit_cast(bf16x8, (u32x4{pk_bf16(e[0], e[1]), pk_bf16(e[2], e[3]),
                                                              pk_bf16(e[4], e[5]), pk_bf16(e[6], e[7])}));
-          const bool vmask = part_blk && ((i + 1) * kSub + tok0 + 3 >= nval);  // slots past the row's tokens
+          // tokens the row does not see have p = 0 and finite values (slots
+          // past the request's last token were zeroed when staged)
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            i16x4 v0 = vreg[b][0][dt], v1 = vreg[b][1][dt];
-            if (vmask) {  // they can hold anything, even NaN codes
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                if (i * kSub + tok0 + t >= nval) v0[t] = 0;
-                if ((i + 1) * kSub + tok0 + t >= nval) v1[t] = 0;
-              }
-            }
-            const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+            const u32x2 w0 = __builtin_bit_cast(u32x2, vreg[b][0][dt]), w1 = __builtin_bit_cast(u32x2, vreg[b][1][dt]);
             o[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, (u32x4{w0.x, w0.y, w1.x, w1.y})), p, o[dt]);
           }
           asm volatile("" ::: "memory");

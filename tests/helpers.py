@@ -209,3 +209,32 @@ def run_decode_lse(d: DeviceBatch, o: DecodeOut, sinks: np.ndarray | None) -> np
                              b.sm_scale, s, o.out, lse, o.table, o.ctx, o.sel, o.scores, b.ld_s, o.ws, o.wsb)
     assert guards_intact(lfull, SENTINEL_F32), "decode wrote outside its lse"
     return lse.view(b.num_rows, b.num_q_heads).cpu().numpy().astype(np.float64)
+
+
+def plant_nan_tails(b: syn.Batch) -> int:
+    """Write NaN into every cache slot past each request's last token (the
+    rest of its last page): index keys (and their fp8 scales), K, V and
+    per-token-head K/V scales. Those slots are never visible, so no output may
+    change; returns the number of slots planted."""
+    bf16_nan, fp8_nan = np.uint16(0x7FC0), np.uint8(0x7F)
+    planted = 0
+    for r in range(b.num_reqs):
+        L = int(b.seq_lens[r])
+        if L % 128 == 0:
+            continue
+        page = int(b.block_table[r, (L - 1) // 128])
+        for t in range(L % 128, 128):
+            sub, ts = 8 * page + t // 16, t % 16
+            if b.index_scale is None:
+                b.index_k[page, t // 16, :, :, ts, :] = bf16_nan
+            else:
+                b.index_k[page, t // 16, :, :, ts, :] = fp8_nan
+                b.index_scale.reshape(-1)[page * 128 + t] = np.float32(np.nan)
+            nan = bf16_nan if b.kv_dtype == syn.KV_BF16 else fp8_nan
+            b.k_cache[sub, :, :, :, ts, :] = nan
+            b.v_cache[sub, :, :, ts] = nan
+            if b.scale_mode == syn.SCALE_PER_TOKEN_HEAD:
+                b.k_scale[sub, ts, :] = np.float32(np.nan)
+                b.v_scale[sub, ts, :] = np.float32(np.nan)
+            planted += 1
+    return planted
