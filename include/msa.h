@@ -107,7 +107,10 @@ typedef struct msa_batch {
   int32_t num_pages;          /* host: P, physical pages in index_k / k_cache / v_cache */
 } msa_batch;
 
-/* K/V cache description (host struct with device pointers). */
+/* K/V cache description (host struct with device pointers). Slots of a
+ * request's pages at or past its seq_len (the rest of its last page) are
+ * never visible and may hold any bits, NaN codes and NaN scales included, in
+ * the K/V caches, their scales and the index cache: no output depends on them. */
 typedef struct msa_kv {
   const void* k_cache;   /* [8P][Hkv][4][4][16][8] */
   const void* v_cache;   /* [8P][Hkv][128][16] */
