@@ -523,8 +523,13 @@ template <bool HALF>
 __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a, const int32_t* ctxp) {
   constexpr int kStride = HALF ? kHalfPartStride : kPartStride;
   const int lane = threadIdx.x;
-  const int head = blockIdx.x % a.num_q_heads;
-  const int n = blockIdx.x / a.num_q_heads;
+  // workgroups go to the 8 XCDs in turn: the heads of row n are numbered so
+  // that they all land on XCD n % 8 and share its L2 copy of each slot's
+  // m / l line
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int head = local % a.num_q_heads;
+  const int n = (local / a.num_q_heads) * 8 + xcd;
+  if (n >= a.num_rows) return;
   const int hgi = head / kHeadTile, th = head % kHeadTile;
   const int sg = lane >> 4, td = (lane & 15) * 8;
   const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kStride;
@@ -970,7 +975,7 @@ hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, in
 
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {
   if (a.nsplit <= 1 && !a.half_partials) return hipSuccess;  // block partials: always merged, one slot too
-  const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_q_heads;
+  const int64_t grid = (static_cast<int64_t>(a.num_rows) + 7) / 8 * 8 * a.num_q_heads;
   const int32_t* ctxp = a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in;
   if (a.half_partials)
     hipLaunchKernelGGL(msa_merge_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kMergeThreads), 0, s, a, ctxp);
