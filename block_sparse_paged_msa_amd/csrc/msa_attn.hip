@@ -813,27 +813,29 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         // pulling every sub-page's LDS operands into registers at once; the
         // next sub-page's operands are read while the current one's products
         // run
-        const bool part_blk = nval < kPage;
         float z[8][4];
         float mloc = -INFINITY;
-        bf16x8 kop[2][4];
+        // two sub-pages at a time, their two product chains interleaved
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kop[0][kc] = lds_k_op(sh, 0, kc, lane);
+        for (int i = 0; i < 8; i += 2) {
+          bf16x8 ka[4], kb[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i + 1 < 8) {
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) kop[(i + 1) & 1][kc] = lds_k_op(sh, i + 1, kc, lane);
+          for (int kc = 0; kc < 4; ++kc) {
+            ka[kc] = lds_k_op(sh, i, kc, lane);
+            kb[kc] = lds_k_op(sh, i + 1, kc, lane);
           }
-          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+          f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc) sacc = mfma_16x16x32(kop[i & 1][kc], qv[kc], sacc);
+          for (int kc = 0; kc < 4; ++kc) {
+            sa = mfma_16x16x32(ka[kc], qv[kc], sa);
+            sb = mfma_16x16x32(kb[kc], qv[kc], sb);
+          }
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const int tok = i * kSub + tok0 + t;
-            z[i][t] = sacc[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[tok] : 1.f);
-            if (part_blk && tok >= nval) z[i][t] = -INFINITY;
-            mloc = fmaxf(mloc, z[i][t]);
+            const int ta = i * kSub + tok0 + t, tb = ta + kSub;
+            z[i][t] = (ta < nval) ? sa[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[ta] : 1.f) : -INFINITY;
+            z[i + 1][t] = (tb < nval) ? sb[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[tb] : 1.f) : -INFINITY;
+            mloc = fmaxf(mloc, fmaxf(z[i][t], z[i + 1][t]));
           }
           asm volatile("" ::: "memory");
         }
