@@ -121,6 +121,47 @@ def cpu_baseline(b, rows, budget_s=10.0):
                       f"full step (metadata, scores, pooling, selection, table, attention), {dt:.1f} s"}
 
 
+_PAR_BATCH = None  # the batch the parallel oracle workers read (inherited through fork)
+
+
+def _oracle_row(n):
+    from oracle import msa_oracle as O
+    O.decode_step(_PAR_BATCH, rows=[n])
+    return n
+
+
+def _single_thread_worker():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def cpu_baseline_parallel(b, rows, budget_s=10.0):
+    """The oracle as it stands, one row per task over a pool of single-thread
+    worker processes (one per host core the process may use, at most one per
+    row), repeated until about budget_s seconds. Runs before the GPU is
+    touched: the workers are forked from this process."""
+    import concurrent.futures
+    import multiprocessing
+    global _PAR_BATCH
+    _PAR_BATCH = b
+    cores = max(1, min(len(rows), len(os.sched_getaffinity(0)), 16))
+    ctx = multiprocessing.get_context("fork")
+    with concurrent.futures.ProcessPoolExecutor(cores, mp_context=ctx, initializer=_single_thread_worker) as ex:
+        list(ex.map(_oracle_row, rows))  # workers up and warm
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(_oracle_row, rows))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+    _PAR_BATCH = None
+    return {"value": passes * len(rows) / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} passes over {len(rows)} of {b.num_rows} rows of the {b.name} workload, one row per "
+                      f"task on {cores} single-thread worker processes, full step per row, {dt:.1f} s"}
+
+
 def time_insert(msa, torch, tokens=8192, copies=32, reps=32):
     """msa_cache_insert of a prefill chunk (two sequences of 4096 new tokens, the
     mixed workload's prefill shape) into fp8 e4m3fn caches with per-token-head
@@ -200,10 +241,14 @@ def main():
     import block_sparse_paged_msa_amd as msa
     import msa_synth as syn
 
-    torch.cuda.set_device(0)
-    msa.load()
     idx_fp8 = args.index == "fp8"
     b = syn.config(args.workload, index_dtype=syn.INDEX_FP8 if idx_fp8 else syn.INDEX_BF16)
+    cpu_par = None
+    if not args.no_cpu_baseline:  # before the GPU is touched (the pool forks this process)
+        print("[bench] cpu baseline, all cores (oracle) ...", file=sys.stderr, flush=True)
+        cpu_par = cpu_baseline_parallel(b, list(range(min(b.num_rows, 8))))
+    torch.cuda.set_device(0)
+    msa.load()
     N, R, P, hq, topk, ld_s = b.num_rows, b.num_reqs, b.num_pages, b.num_q_heads, b.topk, b.ld_s
     per_copy = b.index_k.nbytes + b.k_cache.nbytes + b.v_cache.nbytes + (b.index_scale.nbytes if idx_fp8 else 0)
     copies = args.copies or max(2, math.ceil(768e6 / per_copy))
@@ -322,6 +367,28 @@ def main():
     print(f"[bench] {args.workload}: {sec * 1e6:.2f} us/step over {args.steps} steps, {copies} copies",
           file=sys.stderr, flush=True)
 
+    # Per-step latency distribution: single steps, each bracketed by HIP
+    # events on the launching stream, cycling the cache copies (a replay of a
+    # one-step graph, or the eager launches); the first replays are warm-up.
+    lat_stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+    for i in range(10 + len(ev)):
+        c = i % copies
+        if i >= 10:
+            ev[i - 10][0].record(lat_stream)
+        if args.eager:
+            step(c)
+        else:
+            graphs[c].replay()
+        if i >= 10:
+            ev[i - 10][1].record(lat_stream)
+    torch.cuda.synchronize()
+    lat = np.sort(np.array([a.elapsed_time(b_) * 1e3 for a, b_ in ev]))
+    step_lat = {"p10_us": float(np.percentile(lat, 10)), "p50_us": float(np.percentile(lat, 50)),
+                "p90_us": float(np.percentile(lat, 90)), "samples": int(lat.size),
+                "note": "each step a separate replay between two events: includes the per-replay launch "
+                        "overhead that back-to-back steps (ms_per_step) hide"}
+
     # Dominant kernel: back-to-back msa_index_score launches (cycling the cache
     # copies) captured in one graph and bracketed by HIP events on the
     # launching stream, so the per-launch figure is the kernel's own duration
@@ -377,6 +444,7 @@ def main():
                    "requests": R, "rows": N, "top_k": topk,
                    "q_heads": hq, "kv_heads": 1, "head_dim": 128, "seq_lens_sum": int(b.seq_lens.sum()),
                    "cache_copies_cycled": copies, "graphs": not args.eager},
+        "step_latency": step_lat,
         "step_hbm_gbps": nbytes["step"] / sec / 1e9,
         "step_hbm_frac": nbytes["step"] / sec / 1e9 / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": nbytes["step"],
@@ -436,6 +504,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, list(range(min(N, 8))))
+        res["cpu_baseline_all_cores"] = cpu_par
     print(json.dumps(res), flush=True)
 
 
