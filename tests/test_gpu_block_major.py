@@ -130,3 +130,40 @@ def test_block_major_scores_in_workspace(gpu_lib):
     ref = O.attention_from_table(b, outs[0].table.cpu().numpy(), ctx, rows)
     err = np.abs(H.bf16_to_np(outs[1].out)[rows] - ref).max()
     assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err}"
+
+
+def test_block_major_repeat_and_graph_replay_bitwise(gpu_lib):
+    """The block-major step is deterministic (every (row, block) entry writes
+    its own slot; the merge takes slots in rank order), and a captured step
+    replays bit for bit with garbage left in the workspace between replays."""
+    b = syn.make_batch("bm_graph", 860, [9000, 20000, 700], [1600, 600, 1], topk=16, num_q_heads=16,
+                       kv_dtype=syn.KV_FP8, scale_mode=syn.SCALE_PER_TOKEN_HEAD)
+    print(f"[block-major] graph replay rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, 16, b.topk, 0)
+    o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+    o.wsb = wsb
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o.out, o.table, o.ctx, o.sel, o.scores)]
+    H.run_decode(d, o)
+    for t, r in zip((o.out, o.table, o.ctx, o.sel, o.scores), ref):
+        assert torch.equal(t, r)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        H.run_decode(d, o)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        H.run_decode(d, o)
+    for rep in range(3):
+        o.out.zero_()
+        o.table.fill_(-1)
+        o.ws.fill_(0x3F3F3F3F)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((o.out, o.table, o.ctx, o.sel, o.scores), ref):
+            assert torch.equal(t, r), f"replay {rep}"
