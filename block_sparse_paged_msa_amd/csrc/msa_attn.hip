@@ -599,16 +599,18 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
 }
 
 // Block-major attention for prefill-sized fused steps. A work item is
-// (request r, block b of r) that at least one row of r selected: the
-// workgroup copies the block's K and V (one contiguous run each: its 8
-// sub-pages are consecutive) into LDS once, reads the list of (row, rank)
-// entries the top-k step wrote for the block, and every wave takes one
-// (row, head group) at a time: all 128 tokens' logits from LDS, the block's
-// softmax statistics, and the PV products. The block's partial (max, sum,
-// unnormalised output) goes to the row's slot for the block's rank, and
-// msa_merge_kernel combines the slots in rank order (one slot too), as it
-// does for token splits, and applies sinks and the LSE output. The order of
-// a list does not matter: every entry writes its own slot.
+// (request r, block b of r): the workgroup finds the rows of r that selected
+// b from the selection words the top-k step wrote (one 8-byte word per row
+// gives both the bit and the block's rank in the row's selection), compacts
+// them into an LDS list, copies the block's K and V (one contiguous run
+// each: its 8 sub-pages are consecutive) into LDS once if the list is not
+// empty, and every wave takes one (row, head group) of the list at a time:
+// all 128 tokens' logits from LDS, the block's softmax statistics, and the
+// PV products. The block's partial (max, sum, unnormalised output) goes to
+// the row's slot for the block's rank, and msa_merge_kernel combines the
+// slots in rank order (one slot too), as it does for token splits, and
+// applies sinks and the LSE output. The order of a list does not matter:
+// every entry writes its own slot.
 constexpr int kBlockThreads = 256;
 constexpr int kRowChunk = 1024;                           // rows of a request examined per pass
 constexpr int kListRankShift = 18;                        // entry = row within the request | rank << 18
@@ -809,13 +811,11 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         const int vis = pos0 + rloc + 1;  // keys the row sees
         const int nval = clampi(vis - blk * kPage, 1, kPage);  // tokens of this block it sees
         // pass 1: the block's 128 logits (S^T per sub-page: token rows, head
-        // columns) and their max; the empty asm keeps the compiler from
-        // pulling every sub-page's LDS operands into registers at once; the
-        // next sub-page's operands are read while the current one's products
-        // run
+        // columns) and their max, two sub-pages at a time with their two
+        // product chains interleaved; the empty asm keeps the compiler from
+        // pulling every sub-page's LDS operands into registers at once
         float z[8][4];
         float mloc = -INFINITY;
-        // two sub-pages at a time, their two product chains interleaved
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           bf16x8 ka[4], kb[4];
