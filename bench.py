@@ -101,6 +101,17 @@ def unique_kv_bytes(b, table, ctx):
     return total
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(b, rows, budget_s=10.0):
     """The oracle as it stands, single-threaded, on `rows` of the workload,
     repeated until about budget_s seconds of CPU work."""
@@ -118,7 +129,7 @@ def cpu_baseline(b, rows, budget_s=10.0):
                 break
     return {"value": passes * len(rows) / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} passes over {len(rows)} of {b.num_rows} rows of the {b.name} workload, "
-                      f"full step (metadata, scores, pooling, selection, table, attention), {dt:.1f} s"}
+                      f"full step (metadata, scores, pooling, selection, table, attention), {dt:.1f} s, {cpu_model()}"}
 
 
 _PAR_BATCH = None  # the batch the parallel oracle workers read (inherited through fork)
@@ -159,7 +170,7 @@ def cpu_baseline_parallel(b, rows, budget_s=10.0):
     _PAR_BATCH = None
     return {"value": passes * len(rows) / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": f"{passes} passes over {len(rows)} of {b.num_rows} rows of the {b.name} workload, one row per "
-                      f"task on {cores} single-thread worker processes, full step per row, {dt:.1f} s"}
+                      f"task on {cores} single-thread worker processes, full step per row, {dt:.1f} s, {cpu_model()}"}
 
 
 def time_insert(msa, torch, tokens=8192, copies=32, reps=32):
