@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_paged_msa_amd as msa
 import msa_synth as syn
 from oracle import msa_oracle as O
 from tests import helpers as H
@@ -451,11 +452,28 @@ def _sample_rows(b, k, seed):
     ("mixed_prefill", None, syn.INDEX_FP8),
 ])
 def test_workload_parity(gpu_lib, name, scale_mode, index_dtype):
+    _workload_parity(name, scale_mode, index_dtype, bench_workspace=False)
+
+
+@pytest.mark.parametrize("name,index_dtype", [("mixed_prefill", 0), ("mixed_prefill", syn.INDEX_FP8),
+                                              ("bf16_batch", 0), ("fp8_kv", 0)])
+def test_workload_parity_bench_launch(gpu_lib, name, index_dtype):
+    """The launch bench.py times: the workspace from msa_decode_workspace_bytes,
+    which sends the mixed workload's 8198 rows down the block-major path."""
+    scale_mode = syn.SCALE_PER_TOKEN_HEAD if name == "fp8_kv" else None
+    _workload_parity(name, scale_mode, index_dtype, bench_workspace=True)
+
+
+def _workload_parity(name, scale_mode, index_dtype, bench_workspace):
     b = _config(name, scale_mode, index_dtype)
     print(f"[workload] {name} scale_mode={scale_mode} index_dtype={index_dtype} rows={b.num_rows} "
-          f"pages={b.num_pages}", flush=True)
+          f"pages={b.num_pages} bench_workspace={bench_workspace}", flush=True)
     d = H.upload(b)
     o = H.alloc_decode(d)
+    if bench_workspace:
+        wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, b.num_q_heads, b.topk, 0)
+        o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+        o.wsb = wsb
     H.run_decode(d, o)
     torch.cuda.synchronize()
     check_metadata(b, H.read_metadata(d))  # as written by the fused step itself
