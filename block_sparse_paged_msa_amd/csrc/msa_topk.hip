@@ -14,8 +14,11 @@ using namespace msa;
 
 namespace {
 
+// The row's keys live in dynamic LDS sized for the launch's block bound, so
+// rows of a few hundred blocks leave room for many workgroups per compute
+// unit (a static 8192-key array allowed four).
 __global__ __launch_bounds__(kSelectThreads) void msa_topk_kernel(MsaTopkArgs a) {
-  __shared__ uint32_t s_key[kMaxBlocksPerRow];
+  extern __shared__ uint32_t s_key[];  // [min(ld_s, ld_bt, kMaxBlocksPerRow)]
   __shared__ SelectLds sl;
   const int tid = threadIdx.x;
   const int n = blockIdx.x;
@@ -61,6 +64,8 @@ __global__ __launch_bounds__(kSelectThreads) void msa_topk_kernel(MsaTopkArgs a)
 }  // namespace
 
 hipError_t msa_launch_topk(const MsaTopkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(msa_topk_kernel, dim3(a.num_rows), dim3(kSelectThreads), 0, s, a);
+  const int nbmax = a.ld_s < a.ld_bt ? a.ld_s : a.ld_bt;
+  const size_t key_bytes = sizeof(uint32_t) * static_cast<size_t>(nbmax < kMaxBlocksPerRow ? nbmax : kMaxBlocksPerRow);
+  hipLaunchKernelGGL(msa_topk_kernel, dim3(a.num_rows), dim3(kSelectThreads), key_bytes, s, a);
   return hipGetLastError();
 }
