@@ -389,8 +389,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int hgi = rest % a.num_hgroups;
   const int n = rest / a.num_hgroups;
   const int nbmax = min(min(a.ld_s, a.ld_bt), 256 * KC);
-  // round 1: the row's keys, its request and position, and Q (indices
-  // clamped so that every load issues unconditionally); round 2: the
+  // first batch of loads: the row's keys, its request and position, and Q
+  // (indices clamped so that every load issues unconditionally); second: the
   // block-table entries, which arrive during the radix passes
   const float* srow = a.scores + static_cast<size_t>(n) * a.ld_s;
   float kraw[KC];
