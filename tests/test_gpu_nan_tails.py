@@ -54,3 +54,21 @@ def test_nan_in_unused_slots(gpu_lib, case):
     ref = O.attention_from_table(b, table, ctx, rows)
     err = np.abs(out[rows] - ref).max()
     assert err <= ATOL[kv], f"attention max abs err {err}"
+
+
+@pytest.mark.parametrize("kv,sm", [(syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD), (syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD),
+                                   (syn.KV_FP8, syn.SCALE_SCALAR)])
+def test_nan_in_unused_slots_table_mode(gpu_lib, kv, sm):
+    """msa_sparse_paged_attn on the oracle's own table and context lengths,
+    with NaN in every slot past each request's last token."""
+    b = syn.make_batch("nan_tab", 890 + kv + 2 * sm, [3001, 17777, 129], [1, 2, 1], topk=16, num_q_heads=16,
+                       kv_dtype=kv, scale_mode=sm)
+    H.plant_nan_tails(b)
+    print(f"[nan tails] table mode kv={kv} scale_mode={sm} rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    ref = O.decode_step(b)
+    out = H.run_attn(d, ref["table"], ref["ctx"])
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all(), "non-finite output"
+    err = np.abs(out - ref["out"]).max()
+    assert err <= ATOL[kv], f"attention max abs err {err}"
