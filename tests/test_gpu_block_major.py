@@ -32,6 +32,8 @@ CASES = [
     ([6000, 2500], [1400, 900], 12, 16, syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD),
     # requests with no query rows around a prefill request
     ([4000, 9000, 500, 7000], [0, 2100, 0, 0], 8, 16, syn.KV_BF16, syn.SCALE_NONE),
+    # three head groups, the last one partial
+    ([5000, 3000], [1300, 800], 8, 40, syn.KV_BF16, syn.SCALE_NONE),
 ]
 
 

@@ -268,6 +268,8 @@ FUSED_SHAPES = [
     ("topk300", [140000, 70000], [1, 2], 300, 16),
     ("hq24", [9000, 3000, 20000], [1, 3, 2], 24, 24),
     ("hq8", [5000, 129, 70000], [2, 1, 1], 40, 8),
+    # the most query heads the library takes: eight head groups
+    ("hq128", [6000, 20000], [1, 2], 16, 128),
 ]
 
 
