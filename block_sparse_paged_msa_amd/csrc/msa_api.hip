@@ -389,6 +389,7 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
       bk.len_cap = len_cap(batch);
       int64_t wgs = static_cast<int64_t>(batch->num_reqs) * nbmax;
       if (wgs > 2LL * cu_count()) wgs = 2LL * cu_count();
+      if (wgs < 1) wgs = 1;  // max_seq_len 0: no item, but a valid launch
       st = hip_status(msa_launch_attn_block(a, bk, kv->kv_dtype, kv->scale_mode, static_cast<int>(wgs), s));
       if (st != MSA_OK) return st;
       return hip_status(msa_launch_merge(a, s));
