@@ -189,10 +189,11 @@ __device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_e
 
 template <int IDX_FP8>
 __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a) {
-  extern __shared__ int s_dyn[];  // [R+1] row prefix, [R+1] extra-group prefix
+  extern __shared__ int s_dyn[];  // [R+1] row prefix, [R+1] extra-group prefix, [R] context lengths
   __shared__ int s_tot[kWavesPerWg][5];
   int* s_cuq = s_dyn;
   int* s_extra = s_dyn + a.num_reqs + 1;
+  int* s_ctx0 = s_dyn + 2 * (a.num_reqs + 1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = a.num_reqs;
@@ -273,6 +274,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
     if (r < R) {
       s_cuq[r + 1] = pre[0] + x[0];
       s_extra[r + 1] = pre[4] + x[4];
+      s_ctx0[r] = L - ql;
       if (writer) {
         a.cu_q[r + 1] = pre[0] + x[0];
         a.cu_k[r + 1] = pre[1] + x[1];
@@ -292,10 +294,11 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
         const int mid = (lo + hi) >> 1;
         if (s_cuq[mid] <= n) lo = mid; else hi = mid;
       }
-      const int L = clampi(a.seq_lens[lo], 0, a.len_cap);
+      // context_len + i from LDS (no dependent global load per row);
+      // rows past the request's query rows stay on its last position
       const int ql = s_cuq[lo + 1] - s_cuq[lo];
       a.row_req[n] = lo;
-      a.row_pos[n] = clampi(L - ql + (n - s_cuq[lo]), -1, L - 1);
+      a.row_pos[n] = s_ctx0[lo] + min(n - s_cuq[lo], ql - 1);
     }
   }
 
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
 }  // namespace
 
 hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s) {
-  const size_t lds = sizeof(int) * 2 * static_cast<size_t>(a.num_reqs + 1);
+  const size_t lds = sizeof(int) * 3 * static_cast<size_t>(a.num_reqs + 1);
   if (a.index_scale)
     hipLaunchKernelGGL(msa_score_kernel<1>, dim3(num_wgs), dim3(kScoreThreads), lds, s, a);
   else
