@@ -491,3 +491,35 @@ def _workload_parity(name, scale_mode, index_dtype, bench_workspace):
     print(f"[workload] {name}: max attention err {err:.3e} over rows {rows[:8]}...", flush=True)
     # every row that selected anything produced a finite output
     assert np.isfinite(out).all()
+
+
+@functools.lru_cache(maxsize=1)
+def _most_requests_batch():
+    return syn.random_batch(177, num_reqs=4096, max_len=130, topk=3)
+
+
+@pytest.mark.parametrize("block_major", [False, True])
+def test_fused_decode_most_requests(gpu_lib, block_major):
+    """The most requests a batch may hold (4096), one row each, through the
+    fused step: the metadata the score kernel writes, every row's selection,
+    table and context length bit-exact; attention on sampled rows. With the
+    larger workspace the 4096 rows take the block-major path."""
+    b = _most_requests_batch()
+    print(f"[fused] most requests rows={b.num_rows} block_major={block_major}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    if block_major:
+        wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, b.num_q_heads, b.topk, 0)
+        o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+        o.wsb = wsb
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    check_metadata(b, H.read_metadata(d))
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    check_selection(b, scores, table, ctx, sel, range(b.num_rows))
+    rows = _sample_rows(b, 16, 178)
+    check_scores(b, scores, rows)
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    assert check_attention(b, out, table, ctx, rows) <= 2e-2
