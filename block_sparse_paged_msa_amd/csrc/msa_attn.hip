@@ -291,14 +291,15 @@ __device__ __forceinline__ void attend_split(const MsaAttnArgs& a, MergeLds& ml,
       a.lse_out[static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + th] = (M + log2f(Lsum)) * kLn2;
     return;
   }
-  // partial: a scalar V scale is folded in here (the merge is linear in acc)
+  // partial: a scalar V scale is folded in here (the merge is linear in acc);
+  // it is read once, by the merge, so it is stored non-temporal
   float* part = a.partials + ((static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit + split) * kPartStride;
   if ((tid & 15) == 0) {
     part[th] = M;
     part[kHeadTile + th] = Lsum;
   }
-  *reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td) = acc0 * vscal;
-  *reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td + 4) = acc1 * vscal;
+  __builtin_nontemporal_store(acc0 * vscal, reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td));
+  __builtin_nontemporal_store(acc1 * vscal, reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td + 4));
 }
 
 __device__ __forceinline__ void write_zero_row(const MsaAttnArgs& a, int n, int hgi) {
@@ -534,7 +535,9 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   const int sg = lane >> 4, td = (lane & 15) * 8;
   const float* base = a.partials + (static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit * kStride;
   // the first thirty-two partials are requested in the same round as ctx
-  // (every slot below nsplit exists in the workspace; unused ones are ignored)
+  // (every slot below nsplit exists in the workspace; unused ones are ignored).
+  // Accumulators are read once: non-temporal loads (the max / sum line of a
+  // slot is shared by the row's heads and stays cached)
   constexpr int kPer = 8;  // splits per lane per round
   float ms[kPer], ls[kPer];
   f32x4 x0[kPer], x1[kPer];
@@ -545,13 +548,13 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
       ms[j] = ps[th];
       ls[j] = ps[kHeadTile + th];
       if constexpr (HALF) {
-        const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ps + 2 * kHeadTile) +
-                                                          th * kDim + td);
+        const u32x4 h = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ps + 2 * kHeadTile) + th * kDim + td));
         x0[j] = f32x4{f16_lo(h.x), f16_hi(h.x), f16_lo(h.y), f16_hi(h.y)};
         x1[j] = f32x4{f16_lo(h.z), f16_hi(h.z), f16_lo(h.w), f16_hi(h.w)};
       } else {
-        x0[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td);
-        x1[j] = *reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4);
+        x0[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td));
+        x1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4));
       }
     }
   };
