@@ -4,6 +4,8 @@ context lengths bit-exact against the oracle selector on the device's scores;
 attention (with LSE and sinks) against the oracle on the device's own table,
 to the same bars as the per-row path; and the per-row path on the same
 inputs (smaller workspace) within the same bars."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -12,7 +14,7 @@ import block_sparse_paged_msa_amd as msa
 import msa_synth as syn
 from oracle import msa_oracle as O
 from tests import helpers as H
-from tests.test_gpu_parity import check_metadata, check_selection, _sample_rows
+from tests.test_gpu_parity import check_metadata, check_scores, check_selection, _sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -171,3 +173,47 @@ def test_block_major_repeat_and_graph_replay_bitwise(gpu_lib):
         torch.cuda.synchronize()
         for t, r in zip((o.out, o.table, o.ctx, o.sel, o.scores), ref):
             assert torch.equal(t, r), f"replay {rep}"
+
+
+@pytest.mark.parametrize("topk", [1, 8, 16])
+def test_block_major_tied_scores(gpu_lib, topk):
+    """Index queries and keys in {-1, 0, 1}: integer token scores, so many
+    blocks share their pooled maximum and the cut falls inside a tie (the
+    lowest block ids are kept); the selection words the top-k step leaves
+    for the block kernel carry the same choice as the oracle's, and the
+    per-row path on the same inputs gives the same table."""
+    L, ql = [9000, 5000, 300, 2047], [1500, 700, 1, 1]
+    b = syn.make_batch("bm_ties", 870 + topk, L, ql, topk=topk, num_q_heads=16, kv_dtype=syn.KV_BF16,
+                       scale_mode=syn.SCALE_NONE)
+    tern = lambda x: syn.to_bf16_bits(np.clip(np.round(O.bf16_to_f64(x)), -1.0, 1.0))
+    b = dataclasses.replace(b, index_q=tern(b.index_q), index_k=tern(b.index_k))
+    assert b.num_rows >= 2048
+    print(f"[block-major] ties topk={topk} rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, 16, topk, 0)
+    o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+    o.wsb = wsb
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    meta = O.build_metadata(b.seq_lens, b.query_lens)
+    straddled = 0
+    for n in range(b.num_rows):
+        nb = O.num_blocks(O.visible_keys(meta["row_pos"][n]))
+        row = scores[n][:nb].astype(np.float64)
+        assert np.array_equal(row, np.round(row)), f"row {n}: scores are not integers"
+        if topk < nb:
+            srt = np.sort(row)[::-1]
+            straddled += int(srt[topk - 1] == srt[topk])
+    assert straddled >= 1, "the crafted inputs should put the cut inside a tie"
+    check_selection(b, scores, table, ctx, sel, range(b.num_rows))
+    rows = sorted(set(_sample_rows(b, 12, 880 + topk)))
+    check_scores(b, scores, rows)
+    ref = O.attention_from_table(b, table, ctx, rows)
+    err = np.abs(H.bf16_to_np(o.out)[rows] - ref).max()
+    assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err}"
+    o2 = H.alloc_decode(d)
+    H.run_decode(d, o2)
+    assert torch.equal(o2.table, o.table) and torch.equal(o2.ctx, o.ctx)
