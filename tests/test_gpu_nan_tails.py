@@ -24,6 +24,9 @@ CASES = [
     ([5001, 913, 20000 - 3], [2, 1, 3], 16, syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD, syn.INDEX_FP8),
     ([6100, 2900, 333], [1500, 700, 1], 16, syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD, syn.INDEX_BF16),
     ([4500, 3100], [1300, 900], 8, syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD, syn.INDEX_FP8),
+    # block-major with no K/V scales and with a scalar pair
+    ([7000, 2500, 90], [1400, 800, 1], 8, syn.KV_BF16, syn.SCALE_NONE, syn.INDEX_BF16),
+    ([5100, 2300], [1200, 1000], 12, syn.KV_FP8, syn.SCALE_SCALAR, syn.INDEX_BF16),
 ]
 
 
