@@ -624,7 +624,7 @@ constexpr int kListRankMax = (1 << (31 - kListRankShift)) - 1;
 struct BlockLds {
   static constexpr int kPlane = kPage * kDim * 2;                   // bytes of one bf16 plane of a block
   __attribute__((aligned(16))) uint8_t k[kPlane];                   // 8 shuffled K tiles
-  __attribute__((aligned(16))) uint8_t v[kPlane];                   // 8 dim-major V sub-pages
+  __attribute__((aligned(16))) uint8_t v[kPlane];                   // V sub-pages, dim-major, pairs interleaved
   float ks[kPage], vs[kPage];
   int ent[kRowChunk];                                               // (row, rank) entries of a chunk
   int nsel[2];                                                      // entry counters of alternate chunks
@@ -635,15 +635,24 @@ __device__ __forceinline__ bf16x8 lds_k_op(const BlockLds& sh, int i, int kc, in
   return *reinterpret_cast<const bf16x8*>(sh.k + 2 * e);
 }
 
-// V sub-pages sit in LDS dim-major ([128 dims][16 tokens], 32 B a dim) with
-// the four 8-byte token groups of dim d stored at position g ^ ((d >> 2) & 3):
-// the 16 lanes that read one token group of 16 consecutive dims then hit 16
-// different bank pairs instead of 4.
+// V sub-pages sit in LDS dim-major, 32 B a dim (16 tokens), with the four
+// 8-byte token groups of dim d stored at position g ^ ((d >> 2) & 3): the 16
+// lanes that read one token group of 16 consecutive dims then hit 16
+// different bank pairs instead of 4. The rows are ordered [sub-page pair]
+// [16-dim tile][sub-page of the pair][16 dims], so the two halves of a PV
+// operand (the same dims in sub-pages 2p and 2p+1) are 512 B apart and the
+// closest pair of reads: the compiler merges exactly those two into one
+// read2st64 whose destination is the operand, with no register moves.
 __device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
+
+// Row (32 B) of dim d of sub-page i.
+__device__ __forceinline__ int v_row(int i, int d) {
+  return (i >> 1) * (2 * kDim) + (d >> 4) * 32 + (i & 1) * 16 + (d & 15);
+}
 
 __device__ __forceinline__ i16x4 lds_v_op(const BlockLds& sh, int i, int dt, int lane) {
   const int d = dt * 16 + (lane & 15);
-  const int e = i * (kSub * kDim) + d * kSub + 4 * ((lane >> 4) ^ v_swz(d));
+  const int e = v_row(i, d) * kSub + 4 * ((lane >> 4) ^ v_swz(d));
   return *reinterpret_cast<const i16x4*>(sh.v + 2 * e);
 }
 
@@ -767,8 +776,9 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
               const u32x2 t2 = (f & 1) ? c3 : c2, t3 = (f & 1) ? c2 : c3;
               const u32x2 o0 = (f & 2) ? t2 : t0, o1 = (f & 2) ? t3 : t1;
               const u32x2 o2 = (f & 2) ? t0 : t2, o3 = (f & 2) ? t1 : t3;
-              vd[2 * q] = u32x4{o0.x, o0.y, o1.x, o1.y};
-              vd[2 * q + 1] = u32x4{o2.x, o2.y, o3.x, o3.y};
+              const int vrow = v_row(q >> 7, q & (kDim - 1));
+              vd[2 * vrow] = u32x4{o0.x, o0.y, o1.x, o1.y};
+              vd[2 * vrow + 1] = u32x4{o2.x, o2.y, o3.x, o3.y};
               asm volatile("" ::: "memory");  // one piece at a time (fewer live registers)
             } else {
               kd[q] = kr[i];
@@ -786,7 +796,8 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
                 }
                 w = u32x4{x[0], x[1], x[2], x[3]};
               }
-              vd[(q & ~1) | ((q & 1) ^ (f >> 1))] = (f & 1) ? u32x4{w.z, w.w, w.x, w.y} : w;
+              vd[2 * v_row(q >> 8, (q >> 1) & (kDim - 1)) + ((q & 1) ^ (f >> 1))] =
+                  (f & 1) ? u32x4{w.z, w.w, w.x, w.y} : w;
             }
           }
         }
@@ -817,31 +828,41 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         // columns) and their max, two sub-pages at a time with their two
         // product chains interleaved; the empty asm keeps the compiler from
         // pulling every sub-page's LDS operands into registers at once
+        // (the row sees the whole block in all but its last selected block:
+        // that case is compiled without the per-token visibility selects)
         float z[8][4];
         float mloc = -INFINITY;
+        auto pass1 = [&](auto whole) {
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          bf16x8 ka[4], kb[4];
+          for (int i = 0; i < 8; i += 2) {
+            bf16x8 ka[4], kb[4];
 #pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            ka[kc] = lds_k_op(sh, i, kc, lane);
-            kb[kc] = lds_k_op(sh, i + 1, kc, lane);
+            for (int kc = 0; kc < 4; ++kc) {
+              ka[kc] = lds_k_op(sh, i, kc, lane);
+              kb[kc] = lds_k_op(sh, i + 1, kc, lane);
+            }
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+              sa = mfma_16x16x32(ka[kc], qv[kc], sa);
+              sb = mfma_16x16x32(kb[kc], qv[kc], sb);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int ta = i * kSub + tok0 + t, tb = ta + kSub;
+              const float za = sa[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[ta] : 1.f);
+              const float zb = sb[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[tb] : 1.f);
+              z[i][t] = (decltype(whole)::value || ta < nval) ? za : -INFINITY;
+              z[i + 1][t] = (decltype(whole)::value || tb < nval) ? zb : -INFINITY;
+              mloc = fmaxf(mloc, fmaxf(z[i][t], z[i + 1][t]));
+            }
+            asm volatile("" ::: "memory");
           }
-          f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            sa = mfma_16x16x32(ka[kc], qv[kc], sa);
-            sb = mfma_16x16x32(kb[kc], qv[kc], sb);
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int ta = i * kSub + tok0 + t, tb = ta + kSub;
-            z[i][t] = (ta < nval) ? sa[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[ta] : 1.f) : -INFINITY;
-            z[i + 1][t] = (tb < nval) ? sb[t] * zscale * ((SCALE_MODE == 2) ? sh.ks[tb] : 1.f) : -INFINITY;
-            mloc = fmaxf(mloc, fmaxf(z[i][t], z[i + 1][t]));
-          }
-          asm volatile("" ::: "memory");
-        }
+        };
+        if (nval == kPage)
+          pass1(std::true_type{});
+        else
+          pass1(std::false_type{});
         const float m = max_across_rows(mloc);  // finite: token 0 is visible
         // pass 2: probabilities and O^T += V^T P^T per sub-page
         float lsum = 0.f;
