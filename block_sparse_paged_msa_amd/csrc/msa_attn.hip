@@ -626,6 +626,7 @@ struct BlockLds {
   __attribute__((aligned(16))) uint8_t k[kPlane];                   // 8 shuffled K tiles
   __attribute__((aligned(16))) uint8_t v[kPlane];                   // V sub-pages, dim-major, pairs interleaved
   float ks[kPage], vs[kPage];
+  uint32_t vmax[4];                                                 // per wave: largest |V| bits (bf16, no scales)
   int ent[kRowChunk];                                               // (row, rank) entries of a chunk
   int nsel[2];                                                      // entry counters of alternate chunks
 };
@@ -729,6 +730,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
           const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v_cache) +
                                                            static_cast<size_t>(page) * kSrcPlane);
           u32x4 kr[kPieces], vr[kPieces];
+          uint32_t vabs = 0u;  // largest |V| as bf16 magnitude bits (order-preserving)
 #pragma unroll
           for (int i = 0; i < kPieces; ++i) {
             kr[i] = __builtin_nontemporal_load(kg + tid + kBlockThreads * i);
@@ -798,10 +800,29 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
               }
               vd[2 * v_row(q >> 8, (q >> 1) & (kDim - 1)) + ((q & 1) ^ (f >> 1))] =
                   (f & 1) ? u32x4{w.z, w.w, w.x, w.y} : w;
+              if constexpr (SCALE_MODE == 0) {
+                const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vabs = max(vabs, max(x[u] & 0x7fffu, (x[u] >> 16) & 0x7fffu));
+              }
             }
+          }
+          if constexpr (SCALE_MODE == 0) {
+            vabs = wave_extreme_u32<true>(vabs);
+            if (lane == 0) sh.vmax[wave] = vabs;
           }
         }
         __syncthreads();
+      }
+      // bf16 V with no scales: one power of two for all of the block's
+      // partials, 2^ex > 128 max|V| >= |sum_t p_t v_t| (p_t <= 1), folded
+      // into the softmax max, so the accumulators come out of the products
+      // already scaled for fp16
+      int blk_ex = 0;
+      if constexpr (SCALE_MODE == 0) {
+        const uint32_t vmb = max(max(sh.vmax[0], sh.vmax[1]), max(sh.vmax[2], sh.vmax[3]));
+        if (vmb != 0u)
+          blk_ex = clampi(__builtin_amdgcn_frexp_expf(__uint_as_float(vmb << 16)) + 7, -kHalfExpRange, kHalfExpRange);
       }
       // each wave takes every fourth (row, head group)
       const int nent = total * a.num_hgroups;
@@ -864,6 +885,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         else
           pass1(std::false_type{});
         const float m = max_across_rows(mloc);  // finite: token 0 is visible
+        const float mb = m + static_cast<float>(blk_ex);
         // pass 2: probabilities and O^T += V^T P^T per sub-page
         float lsum = 0.f;
         f32x4 o[8];
@@ -890,7 +912,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int tok = (i + (j >> 2)) * kSub + tok0 + (j & 3);
-            e[j] = fast_exp2(z[i + (j >> 2)][j & 3] - m);
+            e[j] = fast_exp2(z[i + (j >> 2)][j & 3] - mb);
             lsum += e[j];
             if constexpr (SCALE_MODE == 2) e[j] *= sh.vs[tok];
           }
@@ -915,6 +937,16 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         // (the four lanes of a head store the same m and l), so the wait for
         // the next entry's query never has to wait for these stores.
         const int head = lane & 15;
+        float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kHalfPartStride;
+        uint32_t* acc = reinterpret_cast<uint32_t*>(part + 2 * kHeadTile) + (head * kDim + tok0) / 2;
+        if constexpr (SCALE_MODE == 0) {  // already scaled by 2^-blk_ex
+          part[head] = mb;
+          part[kHeadTile + head] = l;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<u32x2*>(acc + dt * 8) = u32x2{pk_f16(o[dt][0], o[dt][1]), pk_f16(o[dt][2], o[dt][3])};
+          return;
+        }
         float mx = 0.f;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
@@ -923,10 +955,8 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         mx = max_across_rows(mx) * fabsf(vscal);
         const int ex = (mx > 0.f) ? clampi(__builtin_amdgcn_frexp_expf(mx), -kHalfExpRange, kHalfExpRange) : 0;
         const float f = ldexpf(vscal, -ex);
-        float* part = a.partials + ((static_cast<size_t>(row) * a.num_hgroups + hgi) * a.nsplit + rank) * kHalfPartStride;
         part[head] = m + static_cast<float>(ex);
         part[kHeadTile + head] = ldexpf(l, -ex);
-        uint32_t* acc = reinterpret_cast<uint32_t*>(part + 2 * kHeadTile) + (head * kDim + tok0) / 2;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
           *reinterpret_cast<u32x2*>(acc + dt * 8) = u32x2{pk_f16(o[dt][0] * f, o[dt][1] * f), pk_f16(o[dt][2] * f, o[dt][3] * f)};

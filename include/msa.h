@@ -219,9 +219,11 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  *   some row of the request selected attends every such row from one copy of
  *   the block's K/V, and the per-block partials are merged. Each partial
  *   keeps its max and sum in fp32 and its 16x128 accumulator in fp16, scaled by a power of two so that its
- *   largest magnitude is below 1 (the error this adds to an output is at most
- *   2^-11 of the largest |V| entry the row attends). Same results up to that
- *   and rounding order; with the smaller workspace the per-row path runs.
+ *   largest magnitude is below 1: from the accumulator itself, or, for bf16
+ *   K/V with no scales, from the bound 128 * max|V| of the block (the error
+ *   this adds to an output is at most about 2^-11 of the largest |V| entry
+ *   of the blocks the row attends). Same results up to that and rounding
+ *   order; with the smaller workspace the per-row path runs.
  * Errors: union of the errors of the steps.
  */
 msa_status msa_sparse_decode(msa_stream_t stream, const msa_batch* batch, const void* index_q,
