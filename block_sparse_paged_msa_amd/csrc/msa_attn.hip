@@ -933,7 +933,9 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
         // accumulator is scaled by 2^-e so that its largest magnitude is below
         // 1, and e is folded into the log2-domain max and the sum
         // (2^(m+e) * l*2^-e = 2^m * l), so the merge weighs the slots exactly
-        // as it weighs fp32 partials. Every path stores the same instructions
+        // as it weighs fp32 partials. For bf16 V with no scales e is the
+        // block's (chosen when it was staged) and the probabilities already
+        // carry 2^-e, so the products come out scaled. Every path stores the same instructions
         // (the four lanes of a head store the same m and l), so the wait for
         // the next entry's query never has to wait for these stores.
         const int head = lane & 15;
