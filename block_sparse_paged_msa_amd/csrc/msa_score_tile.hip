@@ -31,7 +31,7 @@ constexpr int kTileWaves = 8;
 constexpr int kTileThreads = 64 * kTileWaves;
 constexpr int kWaveRows = 64;                  // per wave: four 16-row MFMA tiles
 constexpr int kTileRows = kWaveRows * kTileWaves;  // query rows per workgroup
-constexpr int kRunPages = 8;                   // pages per work item
+constexpr int kRunPages = 8;                   // pages per work item (or twice as many, below)
 
 template <int IDX_FP8>
 struct TileShared {
@@ -98,11 +98,12 @@ __device__ __forceinline__ bf16x8 lds_operand(const TileShared<IDX_FP8>& sh, int
 
 template <int IDX_FP8>
 __global__ __launch_bounds__(kTileThreads, 1) void msa_score_tile_kernel(MsaScoreArgs a) {
-  extern __shared__ int s_dyn[];  // [R+1] row prefix, [R+1] work-item prefix
+  extern __shared__ int s_dyn[];  // [R+1] row prefix, [R+1] work-item prefix for runs of 8 and of 16 pages
   __shared__ TileShared<IDX_FP8> sh;
   __shared__ int s_scan[kTileWaves];
   int* s_cuq = s_dyn;
   int* s_items = s_dyn + a.num_reqs + 1;
+  int* s_items2 = s_dyn + 2 * (a.num_reqs + 1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = a.num_reqs;
@@ -112,28 +113,43 @@ __global__ __launch_bounds__(kTileThreads, 1) void msa_score_tile_kernel(MsaScor
   if (tid == 0) {
     s_cuq[0] = 0;
     s_items[0] = 0;
+    s_items2[0] = 0;
   }
-  int carry_q = 0, carry_i = 0;
+  int carry_q = 0, carry_i = 0, carry_i2 = 0;
   for (int base = 0; base < R; base += kTileThreads) {
     const int r = base + tid;
-    int ql = 0, items = 0;
+    int ql = 0, items = 0, items2 = 0;
     if (r < R) {
       const int L = clampi(a.seq_lens[r], 0, a.len_cap);
       ql = clampi(a.query_lens[r], 0, L);
-      if (ql > kRowsPerUnit)
-        items = ((ql + kTileRows - 1) / kTileRows) * ((L + kPage * kRunPages - 1) / (kPage * kRunPages));
+      if (ql > kRowsPerUnit) {
+        const int rb = (ql + kTileRows - 1) / kTileRows;
+        items = rb * ((L + kPage * kRunPages - 1) / (kPage * kRunPages));
+        items2 = rb * ((L + 2 * kPage * kRunPages - 1) / (2 * kPage * kRunPages));
+      }
     }
-    int tq, ti;
+    int tq, ti, ti2;
     const int eq = tile_exclusive_scan(ql, s_scan, &tq);
     const int ei = tile_exclusive_scan(items, s_scan, &ti);
+    const int ei2 = tile_exclusive_scan(items2, s_scan, &ti2);
     if (r < R) {
       s_cuq[r + 1] = carry_q + eq + ql;
       s_items[r + 1] = carry_i + ei + items;
+      s_items2[r + 1] = carry_i2 + ei2 + items2;
     }
     carry_q += tq;
     carry_i += ti;
+    carry_i2 += ti2;
   }
   __syncthreads();
+  // Runs of 16 pages when they take fewer rounds of the grid times (pages +
+  // about two pages' worth of per-item start-up: the query tiles and the
+  // first page, not overlapped) than runs of 8; every workgroup computes the
+  // same totals, so all take the same choice.
+  const int g = static_cast<int>(gridDim.x);
+  const bool longer = ((s_items2[R] + g - 1) / g) * (2 * kRunPages + 2) < ((s_items[R] + g - 1) / g) * (kRunPages + 2);
+  const int run_pages = longer ? 2 * kRunPages : kRunPages;
+  if (longer) s_items = s_items2;
   const int total = s_items[R];
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -146,10 +162,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void msa_score_tile_kernel(MsaScor
     const int L = clampi(a.seq_lens[r], 0, a.len_cap);
     const int ql = s_cuq[r + 1] - s_cuq[r];
     const int nb_r = (L + kPage - 1) / kPage;
-    const int runs = (L + kPage * kRunPages - 1) / (kPage * kRunPages);
+    const int runs = (L + kPage * run_pages - 1) / (kPage * run_pages);
     const int local = item - s_items[r];
     const int rb = local / runs, run = local - rb * runs;
-    const int j0 = run * kRunPages, j1 = min(j0 + kRunPages, nb_r);
+    const int j0 = run * run_pages, j1 = min(j0 + run_pages, nb_r);
     // rows of this workgroup and of this wave
     const int blk_rows = min(kTileRows, ql - rb * kTileRows);
     const int w_first = rb * kTileRows + wave * kWaveRows;      // first row (within the request)
@@ -159,7 +175,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void msa_score_tile_kernel(MsaScor
     const int jv1 = max(j0, min(j1, pos_blk_last / kPage + 1)); // pages someone in the block sees
     const int32_t* bt = a.block_table + static_cast<size_t>(r) * a.ld_bt;
     // the run's page ids, one per lane, fetched once with the item
-    const int pid_lane = clampi(bt[min(j0 + (lane % kRunPages), max(jv1 - 1, 0))], 0, a.num_pages - 1);
+    const int pid_lane = clampi(bt[min(j0 + (lane % run_pages), max(jv1 - 1, 0))], 0, a.num_pages - 1);
     auto page_id = [&](int j) { return __builtin_amdgcn_readlane(pid_lane, j - j0); };
 
     PageStage<IDX_FP8> st;
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void msa_score_tile_kernel(MsaScor
 }  // namespace
 
 hipError_t msa_launch_score_tile(const MsaScoreArgs& a, int num_wgs, hipStream_t s) {
-  const size_t lds = sizeof(int) * 2 * static_cast<size_t>(a.num_reqs + 1);
+  const size_t lds = sizeof(int) * 3 * static_cast<size_t>(a.num_reqs + 1);
   if (a.index_scale)
     hipLaunchKernelGGL(msa_score_tile_kernel<1>, dim3(num_wgs), dim3(kTileThreads), lds, s, a);
   else
