@@ -13,6 +13,7 @@ import torch
 import block_sparse_paged_msa_amd as msa
 import msa_synth as syn
 from oracle import msa_oracle as O
+from tests import bars
 from tests import helpers as H
 from tests.test_gpu_parity import check_metadata, check_scores, check_selection, _sample_rows
 
@@ -74,6 +75,9 @@ def test_block_major_step(gpu_lib, case, with_extras):
     ref_out, ref_lse = O.attention_lse_from_table(b, table, ctx, rows, sinks)
     err = np.abs(out[rows] - ref_out).max()
     assert err <= ATOL[kv], f"attention max abs err {err}"
+    _, amean = bars.oracle_and_abs_mean(b, table, ctx, rows)
+    ex = bars.detect_excess(out[rows], ref_out, amean)
+    assert ex <= 0, f"attention outside the detector bar by {ex} (max abs err {err})"
     lerr = np.abs(lse[rows] - ref_lse).max()
     assert lerr <= ATOL_LSE, f"lse max abs err {lerr}"
     # the per-row path on the same inputs (the smaller workspace selects it)
@@ -109,6 +113,43 @@ def test_block_major_extreme_values(gpu_lib, vexp):
     ref = O.attention_from_table(b, table, ctx, rows)
     err = np.abs(out[rows] - ref).max() / 2.0 ** vexp
     assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err} (in units of 2^{vexp})"
+
+
+@pytest.mark.parametrize("outlier", [2.0 ** 12, 2.0 ** 16])
+def test_block_major_value_outlier(gpu_lib, outlier):
+    """One token with |V| = outlier in every dim, in the block that most rows
+    of the prefill request keep: every row that attends that block, whatever
+    weight it gives the outlier, stays within the detector bar (the fp16 block
+    partials must not lose the small accumulators of those rows)."""
+    L, ql, topk, hq = [9000, 3000], [2000, 300], 16, 16
+    b = syn.make_batch("bm_outlier", 860, L, ql, topk=topk, num_q_heads=hq, kv_dtype=syn.KV_BF16,
+                       scale_mode=syn.SCALE_NONE)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0)
+    o.ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    o.wsb = wsb
+    H.run_decode(d, o)                       # the selection does not depend on V
+    torch.cuda.synchronize()
+    sel = o.sel.cpu().numpy()[:2000]
+    counts = np.bincount(sel[sel >= 0], minlength=b.ld_s)
+    blk = int(np.argmax(counts[:(9000 - 2000) // 128]))   # a block every row sees whole
+    page = int(b.block_table[0, blk])
+    tok = 77                                  # token 77 of the block: sub-page 4, slot 13
+    sub, slot = 8 * page + tok // 16, tok % 16
+    signs = np.where(syn.SplitMix64(861).uniform(128) < 0.5, -outlier, outlier)
+    b.v_cache[sub, 0, :, slot] = syn.to_bf16_bits(signs)
+    print(f"[block-major] |V| outlier {outlier} in block {blk}, kept by {counts[blk]} of 2000 rows", flush=True)
+    d = H.upload(b)
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    table, ctx = o.table.cpu().numpy(), o.ctx.cpu().numpy()
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    rows = [n for n in range(2000) if blk in sel[n]][:40] + sorted(set(_sample_rows(b, 8, 862)))
+    ref, amean = bars.oracle_and_abs_mean(b, table, ctx, rows)
+    ex = bars.detect_excess(out[rows], ref, amean)
+    assert ex <= 0, f"outside the detector bar by {ex} (max abs err {np.abs(out[rows] - ref).max()})"
 
 
 def test_block_major_scores_in_workspace(gpu_lib):

@@ -129,3 +129,85 @@ def test_insert_then_fused_decode_matches_oracle(gpu_lib):
     out = H.bf16_to_np(o.out)
     err = np.abs(out[rows] - ref["out"]).max()
     assert err <= 6e-2, f"attention after insert: max abs err {err}"
+
+
+# Values exactly halfway between two storage codes, as in the oracle's tie
+# pins: e4m3fn midpoints (stored with scale 1), and 1.5 / 3.0 under the two
+# scalar scales that put fl32(x / s) on a bf16 midpoint.
+E4M3_MIDPOINTS = np.array([1.0625, 1.1875, 1.9375, 2.0 ** -10, 3 * 2.0 ** -10, 5 * 2.0 ** -10,
+                           15 * 2.0 ** -10, 400.0, 432.0])
+BF16_TIE_K_SCALE = np.array([0x3FBF40BF], np.uint32).view(np.float32)   # 1.5 / s = 1 + 2^-8: rounds down
+BF16_TIE_V_SCALE = np.array([0x3FBDC6AC], np.uint32).view(np.float32)   # 1.5 / s = 1 + 3*2^-8: rounds up
+
+
+def _tie_rows(rng, T, values, anchor):
+    """T rows of 128: tie values with random signs at random places, the
+    rest zero, and +-anchor in one slot (448 makes a per-token scale of 1)."""
+    x = np.zeros((T, 128))
+    pick = (rng.uniform(T * 128).reshape(T, 128) * len(values)).astype(np.int64)
+    sign = np.where(rng.uniform(T * 128).reshape(T, 128) < 0.5, -1.0, 1.0)
+    x[:] = values[pick] * sign
+    if anchor is not None:
+        x[np.arange(T), (np.arange(T) * 37) % 128] = anchor * sign[:, 0]
+    return x
+
+
+@pytest.mark.parametrize("mode", ["fp8_scalar", "fp8_per_token_head", "bf16_scalar", "fp8_index"])
+def test_insert_rounding_ties_bitexact(gpu_lib, mode):
+    """Rows made of exact midpoints between storage codes: the device stores
+    the same (even) neighbour as the oracle, byte for byte, on both insert
+    paths (whole in-order sub-pages and scattered single tokens)."""
+    T, P = 160, 8
+    rng = syn.SplitMix64(290 + len(mode))
+    perm = rng.permutation(P)
+    pos = np.arange(T)
+    slots = (perm[pos // 128] * 128 + pos % 128).astype(np.int32)     # tokens 0..127: whole sub-pages
+    # the scattered tail must not hit the in-order tokens' slots
+    used = set(slots[:128].tolist())
+    free = [s for s in rng.permutation(P * 128).tolist() if s not in used]
+    slots[128:] = np.array(free[:32], np.int32)
+    print(f"[insert ties] {mode}", flush=True)
+    if mode == "bf16_scalar":
+        vals = np.array([1.5, 3.0])
+        k, v = _tie_rows(rng, T, vals, None), _tie_rows(rng, T, vals, None)
+        kv_dtype, sm, ks, vs = 0, syn.SCALE_SCALAR, BF16_TIE_K_SCALE.copy(), BF16_TIE_V_SCALE.copy()
+    else:
+        anchor = 448.0 if mode != "fp8_scalar" else None
+        k, v = _tie_rows(rng, T, E4M3_MIDPOINTS, anchor), _tie_rows(rng, T, E4M3_MIDPOINTS, anchor)
+        kv_dtype = 1
+        if mode == "fp8_scalar":
+            sm, ks, vs = syn.SCALE_SCALAR, np.array([1.0], np.float32), np.array([1.0], np.float32)
+        else:
+            sm = syn.SCALE_PER_TOKEN_HEAD
+            ks = np.full((P * 8, 16, 1), 5.0, np.float32)
+            vs = np.full((P * 8, 16, 1), 5.0, np.float32)
+    elt = np.uint8 if kv_dtype == 1 else np.uint16
+    kc = rng.integers(0, 255, P * 8 * 2048).astype(elt).reshape(P * 8, 1, 4, 4, 16, 8)
+    vc = rng.integers(0, 255, P * 8 * 2048).astype(elt).reshape(P * 8, 1, 128, 16)
+    k_bits, v_bits = syn.to_bf16_bits(k[:, None, :]), syn.to_bf16_bits(v[:, None, :])
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    dkc, dvc, dks, dvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    kv = msa.make_kv(dkc, dvc, kv_dtype, sm, P, dks, dvs)
+    want = O.cache_insert(kc, vc, ks, vs, None, slots, k_bits, v_bits, None, kv_dtype, sm)
+    if mode == "fp8_index":
+        ik = syn.to_bf16_bits(_tie_rows(rng, T, E4M3_MIDPOINTS, 448.0))
+        ikc = rng.integers(0, 255, P * 128 * 128).astype(np.uint8).reshape(P, 8, 4, 4, 16, 8)
+        isc = np.full((P, 128), 3.0, np.float32)
+        dikc, disc = dev(ikc), dev(isc)
+        msa.msa_cache_insert_ex(T, dev(slots), dev(k_bits), dev(v_bits), kv, dev(ik), dikc, disc)
+        want_ik, want_isc = O.index_insert_fp8(ikc, isc, slots, ik)
+    else:
+        msa.msa_cache_insert(T, dev(slots), dev(k_bits), dev(v_bits), kv, None, None)
+    torch.cuda.synchronize()
+    got = {"k_cache": dkc.cpu().numpy(), "v_cache": dvc.cpu().numpy()}
+    exp = {"k_cache": want[0], "v_cache": want[1]}
+    if sm == syn.SCALE_PER_TOKEN_HEAD:
+        got["k_scale"], exp["k_scale"] = dks.cpu().numpy().view(np.uint32), want[2].view(np.uint32)
+        got["v_scale"], exp["v_scale"] = dvs.cpu().numpy().view(np.uint32), want[3].view(np.uint32)
+        assert np.all(want[2].reshape(-1)[slots] == 1.0), "every written token-head has scale 1"
+    if mode == "fp8_index":
+        got["index_k"], exp["index_k"] = dikc.cpu().numpy(), want_ik
+        got["index_scale"], exp["index_scale"] = disc.cpu().numpy().view(np.uint32), want_isc.view(np.uint32)
+    for name in got:
+        bad = np.flatnonzero(got[name].reshape(-1) != exp[name].reshape(-1))
+        assert bad.size == 0, f"{name}: {bad.size} elements differ, first at {bad[:5].tolist()}"

@@ -14,6 +14,7 @@ import torch
 
 import msa_synth as syn
 from oracle import msa_oracle as O
+from tests import bars
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +35,9 @@ def _check(b, out, lse, table, ctx, rows, sinks):
     atol = ATOL_FP8 if b.kv_dtype == syn.KV_FP8 else ATOL_BF16
     err = np.abs(out[rows] - ref_out).max()
     assert err <= atol, f"output max abs err {err}"
+    _, amean = bars.oracle_and_abs_mean(b, table, ctx, rows)
+    ex = bars.detect_excess(out[rows], ref_out, amean)
+    assert ex <= 0, f"output outside the detector bar by {ex} (max abs err {err})"
     empty = np.isneginf(ref_lse)
     assert np.array_equal(np.isneginf(lse[rows]), empty), "-inf LSE exactly for rows with nothing to attend"
     lerr = np.abs(lse[rows][~empty] - ref_lse[~empty]).max(initial=0.0)

@@ -11,6 +11,7 @@ import torch
 import block_sparse_paged_msa_amd as msa
 import msa_synth as syn
 from oracle import msa_oracle as O
+from tests import bars
 from tests import helpers as H
 from tests.test_gpu_parity import check_scores, check_selection, _sample_rows
 
@@ -54,9 +55,10 @@ def test_nan_in_unused_slots(gpu_lib, case):
     check_selection(b, scores, table, ctx, sel, rows)
     out = H.bf16_to_np(o.out)
     assert np.isfinite(out).all(), "non-finite output"
-    ref = O.attention_from_table(b, table, ctx, rows)
+    ref, amean = bars.oracle_and_abs_mean(b, table, ctx, rows)
     err = np.abs(out[rows] - ref).max()
     assert err <= ATOL[kv], f"attention max abs err {err}"
+    assert bars.detect_excess(out[rows], ref, amean) <= 0, f"attention outside the detector bar (max abs err {err})"
 
 
 @pytest.mark.parametrize("kv,sm", [(syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD), (syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD),
@@ -75,3 +77,5 @@ def test_nan_in_unused_slots_table_mode(gpu_lib, kv, sm):
     assert np.isfinite(out).all(), "non-finite output"
     err = np.abs(out - ref["out"]).max()
     assert err <= ATOL[kv], f"attention max abs err {err}"
+    _, amean = bars.oracle_and_abs_mean(b, ref["table"], ref["ctx"], list(range(b.num_rows)))
+    assert bars.detect_excess(out, ref["out"], amean) <= 0, f"attention outside the detector bar (max abs err {err})"

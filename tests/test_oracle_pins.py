@@ -723,6 +723,105 @@ def test_insert_scalar_scale_divides_and_clamps():
     assert O.bf16_to_f64(stored)[:5].tolist() == [2.0, -6.0, 1.0, 2000.0, -2000.0]
 
 
+# Values exactly halfway between two e4m3fn codes, with the code that round to
+# nearest, ties to even gives, written out by hand from the OCP layout
+# S.EEEE.MMM (bias 7; E = 0: M/8 * 2^-6). A quantiser that rounds ties away
+# from zero, up, or by truncation fails at least one of them.
+E4M3_TIES = [
+    (1.0625, 0x38),        # 1.0 (M=0) | 1.125 (M=1): even M=0
+    (1.1875, 0x3A),        # 1.125 (M=1) | 1.25 (M=2): even M=2 (rounds up)
+    (-1.0625, 0xB8),
+    (-1.1875, 0xBA),
+    (1.9375, 0x40),        # 1.875 (0x3F) | 2.0 (E=8, M=0): up into the next binade
+    (2.0 ** -10, 0x00),    # 0 | 2^-9, the smallest subnormal: even is zero
+    (3 * 2.0 ** -10, 0x02),   # 2^-9 (M=1) | 2^-8 (M=2)
+    (5 * 2.0 ** -10, 0x02),   # 2^-8 (M=2) | 3*2^-9 (M=3)
+    (15 * 2.0 ** -10, 0x08),  # 7*2^-9, the largest subnormal | 2^-6 (E=1, M=0)
+    (400.0, 0x7C),         # 384 (M=4) | 416 (M=5)
+    (432.0, 0x7E),         # 416 (M=5) | 448 (M=6), the largest finite value
+]
+
+
+def test_quantize_e4m3_ties_round_to_even():
+    """Insert quantisation to e4m3fn rounds to nearest, ties to even: with a
+    scalar scale of 1 the stored code of each halfway value is the one
+    written out by hand; per-token-head scaling of a row whose largest
+    magnitude is exactly 448 has s = 1 and gives the same codes."""
+    x = np.array([v for v, _ in E4M3_TIES])
+    want = np.array([c for _, c in E4M3_TIES], np.uint8)
+    assert np.array_equal(O.bf16_to_f64(bf16_bits(x)), x), "tie values are exact bf16 inputs"
+    row = np.zeros(128)
+    row[:len(x)] = x
+    codes, s = O.quantize_row(bf16_bits(row), 1, 1, 1.0)
+    assert s == 1.0 and codes[:len(x)].tolist() == want.tolist()
+    row[100] = -448.0
+    codes, s = O.quantize_row(bf16_bits(row), 1, 2, None)
+    assert s == 1.0 and codes[:len(x)].tolist() == want.tolist() and codes[100] == 0xFE
+    # just off each tie the nearest code wins, whichever side it is on
+    for v, c in E4M3_TIES[:2]:
+        up = O.quantize_row(bf16_bits(np.full(128, v * (1 + 2.0 ** -7))), 1, 1, 1.0)[0][0]
+        dn = O.quantize_row(bf16_bits(np.full(128, v * (1 - 2.0 ** -7))), 1, 1, 1.0)[0][0]
+        assert O.e4m3fn_to_f64(np.array([dn]))[0] <= O.e4m3fn_to_f64(np.array([c]))[0] <= \
+            O.e4m3fn_to_f64(np.array([up]))[0]
+
+
+# Scalar scales under which fl32(1.5 / s) lands exactly halfway between two
+# bf16 values (found by solving s = fl32(1.5 / y) for the midpoint y and
+# checking fl32(1.5 / s) == y), with the bf16 bits that ties to even give.
+BF16_TIE_SCALES = [
+    # (fp32 bits of s, x, fl32(x / s), bf16 bits of the even neighbour)
+    (0x3FBF40BF, 1.5, 1.0 + 2.0 ** -8, 0x3F80),        # 1.0 | 1.0078125: rounds down
+    (0x3FBF40BF, -1.5, -(1.0 + 2.0 ** -8), 0xBF80),
+    (0x3FBF40BF, 3.0, 2.0 + 2.0 ** -7, 0x4000),        # 2.0 | 2.015625
+    (0x3FBDC6AC, 1.5, 1.0 + 3 * 2.0 ** -8, 0x3F82),    # 1.0078125 | 1.015625: rounds up
+    (0x3FBDC6AC, -1.5, -(1.0 + 3 * 2.0 ** -8), 0xBF82),
+    (0x3FBDC6AC, 3.0, 2.0 + 3 * 2.0 ** -7, 0x4002),    # 2.015625 | 2.03125
+]
+
+
+def test_quantize_bf16_ties_round_to_even():
+    """bf16 storage with a scalar scale keeps bf16 RNE(fl32(x) / s): at the
+    exact midpoints below the even neighbour is stored, one case rounding
+    down and one up, so ties away from zero and truncation both fail."""
+    for sbits in sorted({c[0] for c in BF16_TIE_SCALES}):
+        s = float(np.array([sbits], np.uint32).view(np.float32)[0])
+        cases = [c for c in BF16_TIE_SCALES if c[0] == sbits]
+        row = np.zeros(128)
+        row[:len(cases)] = [c[1] for c in cases]
+        for x, y in ((c[1], c[2]) for c in cases):   # each quotient really is the midpoint
+            assert float(np.float32(np.float32(x) / np.float32(s))) == y
+        stored, s_out = O.quantize_row(bf16_bits(row), 0, 1, s)
+        assert s_out == float(np.float32(s))
+        assert stored[:len(cases)].tolist() == [c[3] for c in cases]
+
+
+def test_tie_pins_catch_a_round_half_away_quantiser(monkeypatch):
+    """Plants rounding half away from zero into the oracle's two casts (on the
+    CPU) and checks that both tie pins above then fail."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = O.e4m3fn_to_f64(finite)
+
+    def e4m3_half_away(x32):
+        x = np.asarray(x32, np.float64).reshape(-1)
+        out = np.empty(x.size, np.uint8)
+        for i, v in enumerate(x):
+            d = np.abs(vals - v)
+            best = np.flatnonzero(d == d.min())
+            out[i] = finite[best[np.argmax(np.abs(vals[best]))]] if v != 0 else 0
+        return out.reshape(np.shape(x32))
+
+    def bf16_half_away(x32):
+        u = np.ascontiguousarray(x32, np.float32).view(np.uint32)
+        return ((u + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)
+
+    monkeypatch.setattr(O, "_f32_to_e4m3fn_codes", e4m3_half_away)
+    with pytest.raises(AssertionError):
+        test_quantize_e4m3_ties_round_to_even()
+    monkeypatch.setattr(O, "_f32_to_bf16_bits", bf16_half_away)
+    with pytest.raises(AssertionError):
+        test_quantize_bf16_ties_round_to_even()
+
+
 def test_insert_then_decode_equals_decode_on_the_written_cache():
     """Writing a request's last token through the insert and then running the
     decode step gives the same output as a cache built with that token in
