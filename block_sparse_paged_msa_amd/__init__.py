@@ -25,11 +25,12 @@ MSA_KV_FP8_E4M3FN = 1
 MSA_SCALE_NONE = 0
 MSA_SCALE_SCALAR = 1
 MSA_SCALE_PER_TOKEN_HEAD = 2
+MSA_STATIC_SCRATCH_BYTES = 32 << 20   # workspace inside the library used by msa_sparse_decode_static
 
 EXPORTS = (
     "msa_build_metadata", "msa_index_score", "msa_topk_block_table", "msa_sparse_paged_attn",
     "msa_sparse_decode", "msa_index_score_ex", "msa_sparse_paged_attn_ex", "msa_sparse_decode_ex",
-    "msa_cache_insert", "msa_cache_insert_ex",
+    "msa_sparse_decode_static", "msa_cache_insert", "msa_cache_insert_ex",
     "msa_workspace_bytes", "msa_decode_workspace_bytes", "msa_status_string", "msa_version",
 )
 
@@ -90,6 +91,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "msa_sparse_paged_attn_ex": ([vp, vp, i32, i32, kp, vp, i32, vp, i32, f32, vp, vp, vp, vp, sz], i32),
         "msa_sparse_decode_ex": ([vp, bp, vp, vp, vp, vp, i32, kp, i32, f32, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                   sz], i32),
+        "msa_sparse_decode_static": ([vp, bp, vp, vp, vp, vp, i32, kp, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                      i32], i32),
         "msa_cache_insert": ([vp, i32, vp, vp, vp, kp, vp, vp], i32),
         "msa_cache_insert_ex": ([vp, i32, vp, vp, vp, kp, vp, vp, vp], i32),
         "msa_workspace_bytes": ([i32, i32, i32, i32], sz),
@@ -200,6 +203,15 @@ def msa_sparse_decode_ex(batch: MsaBatch, index_q, index_k, index_k_scale, q, nu
         _stream(stream), ctypes.byref(batch), _ptr(index_q), _ptr(index_k), _ptr(index_k_scale), _ptr(q),
         num_q_heads, ctypes.byref(kv), topk, sm_scale, _ptr(sinks), _ptr(out), _ptr(lse), _ptr(sparse_table),
         _ptr(ctx_lens), _ptr(sel_blocks), _ptr(block_scores), ld_s, _ptr(workspace), workspace_bytes))
+
+
+def msa_sparse_decode_static(batch: MsaBatch, index_q, index_k, index_k_scale, q, num_q_heads: int, kv: MsaKV,
+                             topk: int, sm_scale: float, sinks, out, lse, sparse_table, ctx_lens, sel_blocks,
+                             block_scores, ld_s: int, stream=None) -> None:
+    _check("msa_sparse_decode_static", load().msa_sparse_decode_static(
+        _stream(stream), ctypes.byref(batch), _ptr(index_q), _ptr(index_k), _ptr(index_k_scale), _ptr(q),
+        num_q_heads, ctypes.byref(kv), topk, sm_scale, _ptr(sinks), _ptr(out), _ptr(lse), _ptr(sparse_table),
+        _ptr(ctx_lens), _ptr(sel_blocks), _ptr(block_scores), ld_s))
 
 
 def msa_cache_insert(num_tokens: int, slot_mapping, k_new, v_new, kv: MsaKV, index_k_new, index_k,

@@ -3,9 +3,17 @@
 // unit count), workspace layout and the stream-ordered launches. No call here
 // allocates, copies between host and device, or synchronises.
 #include <atomic>
+#include <mutex>
 
 #include "msa.h"
 #include "msa_kernels.h"
+
+// Workspace of msa_sparse_decode_static, for callers that cannot allocate:
+// one fixed array per device, loaded with the library's code object and held
+// until the process ends. Host code never uses its name as an address (on
+// the host it is only a stand-in for the symbol); the device address comes
+// from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MSA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -27,6 +35,31 @@ int cu_count() {
   if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
   g_cu_count[dev].store(v, std::memory_order_relaxed);
   return v;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -249,6 +282,23 @@ MsaAttnArgs attn_args(const void* q, int32_t num_rows, int32_t num_q_heads, cons
   return a;
 }
 
+// Host checks of the fused step's arguments (everything but the workspace).
+msa_status check_decode(const msa_batch* batch, const void* index_q, const void* index_k, const void* q,
+                        int32_t num_q_heads, const msa_kv* kv, int32_t topk, const void* out,
+                        const int32_t* sparse_table, const int32_t* ctx_lens, int32_t ld_s) {
+  msa_status st = check_batch(batch, true);
+  if (st != MSA_OK) return st;
+  st = check_kv(kv);
+  if (st != MSA_OK) return st;
+  if (topk < 1 || num_q_heads < 1) return MSA_ERR_INVALID_ARG;
+  if (topk > MSA_MAX_TOPK || num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (batch->num_rows == 0) return MSA_OK;
+  if (!index_q || !index_k || !q || !out || !sparse_table || !ctx_lens) return MSA_ERR_INVALID_ARG;
+  if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
+  if (kv->num_pages != batch->num_pages) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
 msa_status launch_attn_and_merge(hipStream_t s, const MsaAttnArgs& a, const msa_kv* kv) {
   msa_status st = hip_status(msa_launch_attn(a, kv->kv_dtype, kv->scale_mode, s));
   if (st != MSA_OK) return st;
@@ -340,16 +390,9 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
                                 int32_t topk, float sm_scale, const float* sinks, void* out, float* lse,
                                 int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks, float* block_scores,
                                 int32_t ld_s, void* workspace, size_t workspace_bytes) {
-  msa_status st = check_batch(batch, true);
+  msa_status st = check_decode(batch, index_q, index_k, q, num_q_heads, kv, topk, out, sparse_table, ctx_lens, ld_s);
   if (st != MSA_OK) return st;
-  st = check_kv(kv);
-  if (st != MSA_OK) return st;
-  if (topk < 1 || num_q_heads < 1) return MSA_ERR_INVALID_ARG;
-  if (topk > MSA_MAX_TOPK || num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
   if (batch->num_rows == 0) return batch->num_reqs ? msa_build_metadata(stream, batch) : MSA_OK;
-  if (!index_q || !index_k || !q || !out || !sparse_table || !ctx_lens) return MSA_ERR_INVALID_ARG;
-  if (ld_s < blocks_bound(batch) || ld_s < 1) return MSA_ERR_UNSUPPORTED;
-  if (kv->num_pages != batch->num_pages) return MSA_ERR_INVALID_ARG;
   const int32_t max_ctx = kPage * topk;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch->num_rows >= kBlockMajorRows && batch->num_rows <= kBlockMajorMaxRows) {
@@ -416,6 +459,27 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
   a.sinks = sinks;
   a.lse_out = lse;
   return launch_attn_and_merge(s, a, kv);
+}
+
+msa_status msa_sparse_decode_static(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                                    const void* index_k, const float* index_k_scale, const void* q,
+                                    int32_t num_q_heads, const msa_kv* kv, int32_t topk, float sm_scale,
+                                    const float* sinks, void* out, float* lse, int32_t* sparse_table,
+                                    int32_t* ctx_lens, int32_t* sel_blocks, float* block_scores, int32_t ld_s) {
+  msa_status st = check_decode(batch, index_q, index_k, q, num_q_heads, kv, topk, out, sparse_table, ctx_lens, ld_s);
+  if (st != MSA_OK) return st;
+  if (batch->num_rows == 0)  // metadata only: no workspace
+    return msa_sparse_decode_ex(stream, batch, index_q, index_k, index_k_scale, q, num_q_heads, kv, topk, sm_scale,
+                                sinks, out, lse, sparse_table, ctx_lens, sel_blocks, block_scores, ld_s, nullptr, 0);
+  // what the per-row path needs; a launch whose block-major workspace also
+  // fits takes that path, exactly as msa_sparse_decode_ex given this size
+  const size_t need = ws_layout(batch->num_rows, num_q_heads, kPage * topk, block_scores ? 0 : ld_s).total;
+  if (need > static_cast<size_t>(MSA_STATIC_SCRATCH_BYTES)) return MSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess) return MSA_ERR_HIP;
+  return msa_sparse_decode_ex(stream, batch, index_q, index_k, index_k_scale, q, num_q_heads, kv, topk, sm_scale,
+                              sinks, out, lse, sparse_table, ctx_lens, sel_blocks, block_scores, ld_s, ws,
+                              MSA_STATIC_SCRATCH_BYTES);
 }
 
 msa_status msa_cache_insert(msa_stream_t stream, int32_t num_tokens, const int32_t* slot_mapping, const void* k_new,

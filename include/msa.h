@@ -80,7 +80,8 @@ enum {
   MSA_MAX_Q_HEADS = 128,    /* query heads sharing the one KV head */
   MSA_MAX_TOPK = 8192,      /* selected blocks per row */
   MSA_MAX_SEQ_LEN = 1048576, /* tokens per request (8192 blocks) */
-  MSA_SCORE_ROWS_PER_UNIT = 64 /* query rows of one request scored per work unit */
+  MSA_SCORE_ROWS_PER_UNIT = 64, /* query rows of one request scored per work unit */
+  MSA_STATIC_SCRATCH_BYTES = 33554432 /* workspace of msa_sparse_decode_static: 32 MiB per device */
 };
 
 /*
@@ -274,6 +275,33 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
                                 int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
                                 float* block_scores, int32_t ld_s, void* workspace,
                                 size_t workspace_bytes);
+
+/*
+ * msa_sparse_decode_static — msa_sparse_decode_ex with no workspace argument
+ * and no allocation, for callers that cannot call hipMalloc (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid it). The
+ * workspace is a fixed device array of MSA_STATIC_SCRATCH_BYTES inside the
+ * library, one per device, held from the library's load until the process
+ * ends; its address on the current device is looked up (hipGetSymbolAddress)
+ * on the first call made with that device current. Results are those of
+ * msa_sparse_decode_ex given a workspace of MSA_STATIC_SCRATCH_BYTES bytes
+ * (the same path is chosen). Nothing in it needs clearing: every byte a call
+ * reads was written earlier in the same call.
+ * Every call on one device shares that device's array: calls that may
+ * overlap on one device (two streams, or two host threads) race and must be
+ * serialised by the caller.
+ * Errors: as msa_sparse_decode_ex; WORKSPACE when the call needs more than
+ * MSA_STATIC_SCRATCH_BYTES, i.e. msa_workspace_bytes(num_rows, num_q_heads,
+ * 128*topk, block_scores ? 0 : ld_s) > MSA_STATIC_SCRATCH_BYTES (pass
+ * block_scores to keep the scores out of it); HIP if the array's address
+ * cannot be obtained.
+ */
+msa_status msa_sparse_decode_static(msa_stream_t stream, const msa_batch* batch, const void* index_q,
+                                    const void* index_k, const float* index_k_scale, const void* q,
+                                    int32_t num_q_heads, const msa_kv* kv, int32_t topk,
+                                    float sm_scale, const float* sinks, void* out, float* lse,
+                                    int32_t* sparse_table, int32_t* ctx_lens, int32_t* sel_blocks,
+                                    float* block_scores, int32_t ld_s);
 
 /*
  * msa_cache_insert — the step before the path: writes new tokens' K, V and

@@ -225,6 +225,27 @@ def test_ex_entry_points_check_like_the_plain_ones():
     assert _code(msa.msa_cache_insert_ex, 4, 0x1, 0x2, 0x3, kv, 0x4, 0, 0xB, 0) == msa.MSA_ERR_INVALID_ARG
 
 
+def test_decode_rejects_static_scratch_overflow():
+    """msa_sparse_decode_static checks like msa_sparse_decode_ex and refuses a
+    launch whose workspace would not fit its fixed 32 MiB array, before any
+    device call."""
+    kv = _fake_kv()
+    b = _fake_batch()
+    args = [b, 0x1, 0x2, None, 0x3, 16, kv, 4, 0.1, None, 0x4, None, 0x5, 0x6, None, 0x8, 4, 0]
+    for idx, val, expect in ((7, 0, msa.MSA_ERR_INVALID_ARG), (16, 2, msa.MSA_ERR_UNSUPPORTED),
+                             (5, 200, msa.MSA_ERR_UNSUPPORTED)):
+        bad = list(args)
+        bad[idx] = val
+        assert _code(msa.msa_sparse_decode_static, *bad) == expect
+    # 4096 rows whose scores would live in the workspace: 4096 x 8192 x 4 B > 32 MiB
+    big = _fake_batch(num_rows=4096, max_seq_len=1 << 20, ld_bt=8192)
+    need = msa.msa_workspace_bytes(4096, 16, 128 * 4, 8192)
+    assert need > msa.MSA_STATIC_SCRATCH_BYTES
+    bad = list(args)
+    bad[0], bad[15], bad[16] = big, None, 8192
+    assert _code(msa.msa_sparse_decode_static, *bad) == msa.MSA_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("args,kv,expect", [
     (dict(num_tokens=-1), {}, msa.MSA_ERR_INVALID_ARG),
     (dict(slot_mapping=0), {}, msa.MSA_ERR_INVALID_ARG),
