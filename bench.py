@@ -4,11 +4,13 @@
 
 One step = metadata -> index score + pooling -> top-k + page-16 table + ctx ->
 sparse paged attention + split merge (msa_sparse_decode) over one batch of the
-named synthetic workload (default: 8 requests x 1 row, L ~ U{8192..32768},
-top-k 16, 16 query heads, bf16; --index fp8 stores the index keys as e4m3fn
-codes with per-token scales). The step's inputs live in HBM; several copies
-of the caches at different addresses are cycled so that no step finds the
-previous step's data in the 256 MB Infinity Cache. Steps are replayed from a
+named synthetic workload (default: the fp8 K/V decode batch, 11 requests x 1
+row, L ~ U{32768..131072}, e4m3fn K/V with per-token-head scales, top-k 64,
+16 query heads; --index fp8 stores the index keys as e4m3fn codes with
+per-token scales). The step's inputs live in HBM; enough copies of the caches
+at different addresses are cycled that at least 768 MB (three times the
+256 MB Infinity Cache) stream through between two uses of one copy, in the
+step loop and in the dominant-kernel loop alike. Steps are replayed from a
 HIP graph holding one step per copy. Prints one JSON line.
 """
 from __future__ import annotations
@@ -42,12 +44,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="bf16_batch", choices=sorted(WORKLOAD_DESC))
+    p.add_argument("--workload", default="fp8_kv", choices=sorted(WORKLOAD_DESC))
     p.add_argument("--index", default="bf16", choices=("bf16", "fp8"),
                    help="index cache: bf16 keys, or e4m3fn codes with one fp32 scale per token")
-    p.add_argument("--copies", type=int, default=0, help="cache copies cycled (0: enough for 768 MB)")
+    p.add_argument("--copies", type=int, default=0,
+                   help="cache copies cycled (0: enough that >= 768 MB stream between two uses of a copy)")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the other workloads' reduced lines")
     p.add_argument("--counters", action="store_true",
                    help="counter pass: 8 plain copies of 256 MiB, then 8 index-score launches, no timing")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -229,6 +233,184 @@ def time_insert(msa, torch, tokens=8192, copies=32, reps=32):
             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS}
 
 
+EXTRA_WORKLOADS = ("bf16_batch", "spec_decode", "mixed_prefill")   # timed too, as extra keys
+CLEAN_BYTES = 768e6     # bytes streamed between two uses of one cache copy (3 x the 256 MB Infinity Cache)
+MAX_COPIES = 64
+
+
+def copies_for(b, idx_fp8):
+    """Cache copies to cycle: the dominant kernel (the index score) touches
+    every visible index key once, sum_r L_r x (256 B or 132 B), and a whole
+    step touches more, so 1 + ceil(768 MB / that) copies keep at least 768 MB
+    streaming between two uses of one copy in both loops (capped at 64 for
+    the tiny workload, whose 0.5 MB step is latency-bound anyway)."""
+    score_bytes = int(b.seq_lens.astype("int64").sum()) * (132 if idx_fp8 else 256)
+    return min(MAX_COPIES, max(2, 1 + math.ceil(CLEAN_BYTES / max(score_bytes, 1))))
+
+
+class Setup:
+    """One workload on the device: `copies` replicas of its caches (each copy
+    on its own pages), one batch struct per copy, the outputs, a workspace
+    from msa_decode_workspace_bytes (the block-major path for prefill-sized
+    launches) and the step / score launches of copy c."""
+
+    def __init__(self, b, copies, idx_fp8, msa, torch, syn):
+        import numpy as np
+        self.b, self.copies, self.idx_fp8, self.msa, self.torch = b, copies, idx_fp8, msa, torch
+        dev = "cuda"
+        N, R, P, hq, topk, ld_s = b.num_rows, b.num_reqs, b.num_pages, b.num_q_heads, b.topk, b.ld_s
+
+        def t16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()) if a.dtype == np.uint16 \
+                else torch.from_numpy(np.ascontiguousarray(a).copy())
+
+        def pool(a):
+            one = t16(a).to(dev)
+            out = torch.empty((copies,) + tuple(one.shape), dtype=one.dtype, device=dev)
+            out[:] = one
+            return out.view((copies * one.shape[0],) + tuple(one.shape[1:]))
+
+        self.index_k = pool(b.index_k)
+        self.index_scale = pool(b.index_scale) if idx_fp8 else None
+        self.k_cache, self.v_cache = pool(b.k_cache), pool(b.v_cache)
+        k_scale = v_scale = None
+        if b.scale_mode == syn.SCALE_PER_TOKEN_HEAD:
+            k_scale, v_scale = pool(b.k_scale), pool(b.v_scale)
+        elif b.scale_mode == syn.SCALE_SCALAR:
+            k_scale, v_scale = t16(b.k_scale).to(dev), t16(b.v_scale).to(dev)
+        self.scales = (k_scale, v_scale)
+        self.index_q, self.q = t16(b.index_q).to(dev), t16(b.q).to(dev)
+        self.seq_lens = torch.from_numpy(b.seq_lens).to(dev)
+        self.query_lens = torch.from_numpy(b.query_lens).to(dev)
+        self.kv = msa.make_kv(self.k_cache, self.v_cache, b.kv_dtype, b.scale_mode, copies * P, k_scale, v_scale)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.batches, self.keep = [], []
+        for c in range(copies):
+            bt = torch.from_numpy(b.block_table + c * P).to(dev)
+            meta = [torch.empty(R + 1, **i32) for _ in range(4)] + [torch.empty(N, **i32) for _ in range(2)]
+            self.keep += [bt] + meta
+            self.batches.append(msa.make_batch(self.seq_lens, self.query_lens, bt, *meta, R, N, b.max_seq_len,
+                                               copies * P))
+        self.out = torch.empty((N, hq, 128), dtype=torch.int16, device=dev)
+        self.table = torch.empty((N, 8 * topk), **i32)
+        self.ctx = torch.empty((N,), **i32)
+        self.scores = torch.empty((N, ld_s), dtype=torch.float32, device=dev)
+        self.wsb = msa.msa_decode_workspace_bytes(N, b.max_seq_len, hq, topk, 0)
+        self.ws = torch.empty((self.wsb,), dtype=torch.uint8, device=dev)
+
+    def step(self, c, sinks=None, lse=None):
+        b, m = self.b, self.msa
+        if self.idx_fp8 or sinks is not None or lse is not None:
+            m.msa_sparse_decode_ex(self.batches[c], self.index_q, self.index_k, self.index_scale, self.q,
+                                   b.num_q_heads, self.kv, b.topk, b.sm_scale, sinks, self.out, lse, self.table,
+                                   self.ctx, None, self.scores, b.ld_s, self.ws, self.wsb)
+        else:
+            m.msa_sparse_decode(self.batches[c], self.index_q, self.index_k, self.q, b.num_q_heads, self.kv,
+                                b.topk, b.sm_scale, self.out, self.table, self.ctx, None, self.scores, b.ld_s,
+                                self.ws, self.wsb)
+
+    def score(self, c):
+        self.msa.msa_index_score_ex(self.batches[c], self.index_q, self.index_k, self.index_scale, self.scores,
+                                    self.b.ld_s)
+
+
+def graph_of(torch, fns):
+    """One HIP graph holding the launches fns() in order (captured on a side
+    stream, after one eager pass of each)."""
+    stream = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        for f in fns:
+            f()
+        with torch.cuda.graph(g, stream=gs):
+            for f in fns:
+                f()
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_us(torch, g, launches, runs=5, reps=1):
+    """Median over `runs` of the time per launch of `reps` replays of g (which
+    holds `launches` launches), HIP events on the replaying stream."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(runs):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / (reps * launches))
+    return sorted(out)[len(out) // 2]
+
+
+def score_kernel_us(torch, st, reps=32):
+    """The dominant kernel alone: `reps` back-to-back msa_index_score launches
+    cycling the cache copies, captured in one graph and bracketed by HIP events
+    on the launching stream."""
+    g = graph_of(torch, [lambda i=i: st.score(i % st.copies) for i in range(reps)])
+    return replay_us(torch, g, reps)
+
+
+def step_figures(b, st, sec, t_score, ctx_host, table_host):
+    """Throughput and rooflines of a timed step. Step bytes count each
+    request's attended K/V once (rows of one request that keep the same
+    blocks share them): the step's minimum HBM traffic."""
+    import numpy as np
+    nbytes = algorithmic_bytes(b, ctx_host)
+    kv_unique = unique_kv_bytes(b, table_host, ctx_host)
+    step_bytes = nbytes["step"] - nbytes["kv"] + kv_unique
+    prefill = bool((b.query_lens > 64).any())
+    step_gbps = step_bytes / sec / 1e9
+    score_gbps = nbytes["score"] / (t_score * 1e-6) / 1e9
+    res = {
+        "rows_per_s": b.num_rows / sec, "us_per_step": sec * 1e6,
+        "step_roofline": {"bound": "mfma" if prefill else "hbm", "achieved": step_gbps, "peak": PEAK_HBM_GBPS,
+                          "unit": "GB/s", "frac": step_gbps / PEAK_HBM_GBPS, "algorithmic_bytes": step_bytes,
+                          "us_per_step": sec * 1e6},
+        "score_kernel": {"kernel": "msa_score_kernel (msa_index_score)", "bound": "hbm", "achieved": score_gbps,
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
+                         "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},
+        "nbytes": nbytes,
+    }
+    if prefill:
+        res["step_roofline"]["note"] = ("prefill rows: bound by the attention's MFMA work and its block partials; "
+                                        "the HBM figure counts each request's attended K/V once")
+        # requests of more than 64 rows are scored by the MFMA tile kernel:
+        # 2 * 128 flops per (row, visible token) over every row of the launch
+        pos = b.seq_lens.astype(np.int64) - b.query_lens.astype(np.int64)
+        vis = sum(int(ql) * int(p0) + int(ql) * (int(ql) + 1) // 2 for p0, ql in zip(pos, b.query_lens))
+        tflops = 2 * 128 * vis / (t_score * 1e-6) / 1e12
+        res["score_mfma"] = {"kernels": "msa_score_kernel + msa_score_tile_kernel (one msa_index_score call)",
+                             "bound": "mfma", "algorithmic_flop": 2 * 128 * vis, "us_per_call": t_score,
+                             "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tflops / PEAK_BF16_TFLOPS}
+    return res
+
+
+def measure_extra(name, idx_fp8, steps, msa, torch, syn):
+    """A reduced line for another workload: step time (graph replay over
+    cache-clean copies), the score kernel alone, and both rooflines."""
+    b = syn.config(name, index_dtype=syn.INDEX_FP8 if idx_fp8 else syn.INDEX_BF16)
+    copies = copies_for(b, idx_fp8)
+    st = Setup(b, copies, idx_fp8, msa, torch, syn)
+    g = graph_of(torch, [lambda c=c: st.step(c) for c in range(copies)])
+    reps = max(1, steps // copies)
+    sec = replay_us(torch, g, copies, reps=reps) * 1e-6
+    t_score = score_kernel_us(torch, st)
+    f = step_figures(b, st, sec, t_score, st.ctx.cpu().numpy(), st.table.cpu().numpy())
+    f.pop("nbytes")
+    f.update({"workload": WORKLOAD_DESC[name], "rows": b.num_rows, "cache_copies_cycled": copies,
+              "steps_timed": reps * copies})
+    del st, g
+    torch.cuda.empty_cache()
+    return f
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -260,118 +442,51 @@ def main():
         cpu_par = cpu_baseline_parallel(b, list(range(min(b.num_rows, 8))))
     torch.cuda.set_device(0)
     msa.load()
-    N, R, P, hq, topk, ld_s = b.num_rows, b.num_reqs, b.num_pages, b.num_q_heads, b.topk, b.ld_s
-    per_copy = b.index_k.nbytes + b.k_cache.nbytes + b.v_cache.nbytes + (b.index_scale.nbytes if idx_fp8 else 0)
-    copies = args.copies or max(2, math.ceil(768e6 / per_copy))
-    dev = "cuda"
-
-    def t16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()) if a.dtype == np.uint16 \
-            else torch.from_numpy(np.ascontiguousarray(a).copy())
-
-    # cache pools holding `copies` replicas of the pages, each copy on its own pages
-    def pool(a):
-        one = t16(a).to(dev)
-        out = torch.empty((copies,) + tuple(one.shape), dtype=one.dtype, device=dev)
-        out[:] = one
-        return out.view((copies * one.shape[0],) + tuple(one.shape[1:]))
-
-    index_k = pool(b.index_k)
-    index_scale = pool(b.index_scale) if idx_fp8 else None
-    k_cache = pool(b.k_cache)
-    v_cache = pool(b.v_cache)
-    k_scale = v_scale = None
-    if b.scale_mode == syn.SCALE_PER_TOKEN_HEAD:
-        k_scale, v_scale = pool(b.k_scale), pool(b.v_scale)
-    elif b.scale_mode == syn.SCALE_SCALAR:
-        k_scale, v_scale = t16(b.k_scale).to(dev), t16(b.v_scale).to(dev)
-    index_q = t16(b.index_q).to(dev)
-    q = t16(b.q).to(dev)
-    seq_lens = torch.from_numpy(b.seq_lens).to(dev)
-    query_lens = torch.from_numpy(b.query_lens).to(dev)
-    kv = msa.make_kv(k_cache, v_cache, b.kv_dtype, b.scale_mode, copies * P, k_scale, v_scale)
-
-    i32 = dict(dtype=torch.int32, device=dev)
-    batches, keep = [], []
-    for c in range(copies):
-        bt = torch.from_numpy(b.block_table + c * P).to(dev)
-        meta = [torch.empty(R + 1, **i32) for _ in range(4)] + [torch.empty(N, **i32) for _ in range(2)]
-        keep += [bt] + meta
-        batches.append(msa.make_batch(seq_lens, query_lens, bt, *meta, R, N, b.max_seq_len, copies * P))
-
-    out = torch.empty((N, hq, 128), dtype=torch.int16, device=dev)
-    table = torch.empty((N, 8 * topk), **i32)
-    ctx = torch.empty((N,), **i32)
-    scores = torch.empty((N, ld_s), dtype=torch.float32, device=dev)
-    wsb = msa.msa_decode_workspace_bytes(N, b.max_seq_len, hq, topk, 0)  # prefill-sized: block-major path
-    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
-
-    def step(c):
-        if idx_fp8:
-            msa.msa_sparse_decode_ex(batches[c], index_q, index_k, index_scale, q, hq, kv, topk, b.sm_scale, None,
-                                     out, None, table, ctx, None, scores, ld_s, ws, wsb)
-        else:
-            msa.msa_sparse_decode(batches[c], index_q, index_k, q, hq, kv, topk, b.sm_scale, out, table, ctx,
-                                  None, scores, ld_s, ws, wsb)
-
-    def score(c):
-        msa.msa_index_score_ex(batches[c], index_q, index_k, index_scale, scores, ld_s)
+    copies = args.copies or copies_for(b, idx_fp8)
+    st = Setup(b, copies, idx_fp8, msa, torch, syn)
+    N, hq = b.num_rows, b.num_q_heads
 
     for c in range(copies):
-        step(c)
+        st.step(c)
     torch.cuda.synchronize()
     if args.counters:
         # counter pass: plain copies of known size, then the dominant kernel
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(8):
             torch.mul(src, 1, out=dst)   # an elementwise kernel: reads and writes COPY_BYTES
         torch.cuda.synchronize()
         for i in range(8):
-            score(i % copies)
+            st.score(i % copies)
         torch.cuda.synchronize()
         print(json.dumps({"counters_pass": args.workload, "copy_bytes": COPY_BYTES,
-                          "score_algorithmic_bytes": algorithmic_bytes(b, ctx.cpu().numpy())["score"]}))
+                          "score_algorithmic_bytes": algorithmic_bytes(b, st.ctx.cpu().numpy())["score"]}))
         return
-    ctx_host = ctx.cpu().numpy()
-    nbytes = algorithmic_bytes(b, ctx_host)
-    kv_unique = unique_kv_bytes(b, table.cpu().numpy(), ctx_host)
+    ctx_host, table_host = st.ctx.cpu().numpy(), st.table.cpu().numpy()
 
     if args.eager:
-        def run_steps(k0, k):
-            for i in range(k0, k0 + k):
-                step(i % copies)
+        def run_steps(k):
+            for i in range(k):
+                st.step(i % copies)
+        graphs = None
     else:
         # one graph holding one step per cache copy, plus one graph per copy for
         # a remainder, so that exactly the requested number of steps is replayed
-        graphs = []
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            g_all = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_all, stream=s):
-                for c in range(copies):
-                    step(c)
-            for c in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=s):
-                    step(c)
-                graphs.append(g)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
+        g_all = graph_of(torch, [lambda c=c: st.step(c) for c in range(copies)])
+        graphs = [graph_of(torch, [lambda c=c: st.step(c)]) for c in range(copies)]
 
-        def run_steps(k0, k):
+        def run_steps(k):
             full, rem = divmod(k, copies)
             for _ in range(full):
                 g_all.replay()
             for i in range(rem):
                 graphs[i].replay()
 
-    run_steps(0, args.warmup)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(0, args.steps)
+    run_steps(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec = (t1 - t0) / args.steps
@@ -387,8 +502,8 @@ def main():
         c = i % copies
         if i >= 10:
             ev[i - 10][0].record(lat_stream)
-        if args.eager:
-            step(c)
+        if graphs is None:
+            st.step(c)
         else:
             graphs[c].replay()
         if i >= 10:
@@ -400,33 +515,8 @@ def main():
                 "note": "each step a separate replay between two events: includes the per-replay launch "
                         "overhead that back-to-back steps (ms_per_step) hide"}
 
-    # Dominant kernel: back-to-back msa_index_score launches (cycling the cache
-    # copies) captured in one graph and bracketed by HIP events on the
-    # launching stream, so the per-launch figure is the kernel's own duration
-    # plus the small gap between graph nodes.
-    reps = 32
-    stream = torch.cuda.current_stream()
-    gs = torch.cuda.Stream()
-    gs.wait_stream(stream)
-    g_score = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(gs):
-        score(0)
-        with torch.cuda.graph(g_score, stream=gs):
-            for i in range(reps):
-                score(i % copies)
-    stream.wait_stream(gs)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_score_runs = []
-    for _ in range(5):
-        e0.record(stream)
-        g_score.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t_score_runs.append(e0.elapsed_time(e1) * 1e3 / reps)
-    t_score = sorted(t_score_runs)[len(t_score_runs) // 2]
-
-    score_gbps = nbytes["score"] / (t_score * 1e-6) / 1e9
+    t_score = score_kernel_us(torch, st)
+    fig = step_figures(b, st, sec, t_score, ctx_host, table_host)
     traffic = None
     tpath = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(tag(args.workload, args.index)))
     if os.path.exists(tpath):
@@ -436,6 +526,8 @@ def main():
                 traffic = tj.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
+    roof = dict(fig["score_kernel"])
+    roof["traffic"] = traffic
 
     res = {
         "metric": METRIC,
@@ -452,66 +544,38 @@ def main():
         "data": "synthetic (seeded splitmix64 N(0,1) values, random page permutation)",
         "config": {"workload": WORKLOAD_DESC[args.workload] + (
                        ", fp8 e4m3fn index keys + per-token scales" if idx_fp8 else ""),
-                   "requests": R, "rows": N, "top_k": topk,
+                   "requests": b.num_reqs, "rows": N, "top_k": b.topk,
                    "q_heads": hq, "kv_heads": 1, "head_dim": 128, "seq_lens_sum": int(b.seq_lens.sum()),
-                   "cache_copies_cycled": copies, "graphs": not args.eager},
+                   "cache_copies_cycled": copies, "bytes_between_copy_reuses_min": (copies - 1) *
+                   fig["score_kernel"]["algorithmic_bytes"], "graphs": not args.eager},
+        "step_roofline": fig["step_roofline"],
+        "roofline": roof,
         "step_latency": step_lat,
-        "step_hbm_gbps": nbytes["step"] / sec / 1e9,
-        "step_hbm_frac": nbytes["step"] / sec / 1e9 / PEAK_HBM_GBPS,
-        "step_algorithmic_bytes": nbytes["step"],
-        # the same with each request's attended K/V counted once (rows of one
-        # request that select the same blocks share them)
-        "step_unique_bytes": nbytes["step"] - nbytes["kv"] + kv_unique,
-        "step_unique_hbm_frac": (nbytes["step"] - nbytes["kv"] + kv_unique) / sec / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "msa_score_kernel (msa_index_score)", "bound": "hbm", "achieved": score_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": nbytes["score"], "avg_launch_us": t_score},
     }
-    if (b.query_lens > 64).any():
-        # requests of more than 64 rows are scored by the MFMA tile kernel:
-        # 2 * 128 flops per (row, visible token) over every row of the launch
-        pos = b.seq_lens.astype(np.int64) - b.query_lens.astype(np.int64)
-        vis = sum(int(ql) * int(p0) + int(ql) * (int(ql) + 1) // 2 for p0, ql in zip(pos, b.query_lens))
-        tflops = 2 * 128 * vis / (t_score * 1e-6) / 1e12
-        res["score_mfma"] = {"kernels": "msa_score_kernel + msa_score_tile_kernel (one msa_index_score call)",
-                             "bound": "mfma", "algorithmic_flop": 2 * 128 * vis, "us_per_call": t_score,
-                             "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": tflops / PEAK_BF16_TFLOPS}
+    if "score_mfma" in fig:
+        res["score_mfma"] = fig["score_mfma"]
     res["cache_insert"] = time_insert(msa, torch)
 
     # the same step through msa_sparse_decode_ex: LSE written, per-head sinks
     # applied; both variants timed here the same way (one graph of `copies`
     # steps, replayed)
-    sinks = torch.linspace(-1.0, 2.0, hq, device=dev, dtype=torch.float32)
-    lse = torch.empty((N, hq), dtype=torch.float32, device=dev)
-
-    def step_lse(c):
-        msa.msa_sparse_decode_ex(batches[c], index_q, index_k, index_scale, q, hq, kv, topk, b.sm_scale, sinks,
-                                 out, lse, table, ctx, None, scores, ld_s, ws, wsb)
-
-    def graph_us_per_step(fn):
-        gs2 = torch.cuda.Stream()
-        gs2.wait_stream(stream)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(gs2):
-            with torch.cuda.graph(g, stream=gs2):
-                for c in range(copies):
-                    fn(c)
-        stream.wait_stream(gs2)
-        torch.cuda.synchronize()
-        reps_g = max(1, 192 // copies)
-        runs = []
-        for _ in range(5):
-            e0.record(stream)
-            for _ in range(reps_g):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs.append(e0.elapsed_time(e1) * 1e3 / (reps_g * copies))
-        return sorted(runs)[len(runs) // 2]
-
-    res["lse_sinks"] = {"entry": "msa_sparse_decode_ex", "us_per_step": graph_us_per_step(step_lse),
-                        "plain_us_per_step": graph_us_per_step(step), "rows": N, "q_heads": hq}
+    sinks = torch.linspace(-1.0, 2.0, hq, device="cuda", dtype=torch.float32)
+    lse = torch.empty((N, hq), dtype=torch.float32, device="cuda")
+    reps_g = max(1, 192 // copies)
+    g_lse = graph_of(torch, [lambda c=c: st.step(c, sinks, lse) for c in range(copies)])
+    g_plain = graph_of(torch, [lambda c=c: st.step(c) for c in range(copies)])
+    res["lse_sinks"] = {"entry": "msa_sparse_decode_ex", "us_per_step": replay_us(torch, g_lse, copies, reps=reps_g),
+                        "plain_us_per_step": replay_us(torch, g_plain, copies, reps=reps_g), "rows": N,
+                        "q_heads": hq}
+    del st, g_lse, g_plain, graphs
+    if not args.eager:
+        del g_all
+    torch.cuda.empty_cache()
+    if args.workload == "fp8_kv" and not idx_fp8 and not args.no_extras:
+        res["other_workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            print(f"[bench] extra workload {name} ...", file=sys.stderr, flush=True)
+            res["other_workloads"][name] = measure_extra(name, False, 200, msa, torch, syn)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(b, list(range(min(N, 8))))
@@ -535,7 +599,7 @@ def _counter_rows(d):
 PMC_CMD = ("rocprofv3 --pmc {counter} --output-format csv -d <out> -o run -- "
            "python3 -u bench.py --workload {workload}{index} --counters")
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- "
-             "python3 -u bench.py --workload {workload}{index} --steps 50 --warmup 10 --no-cpu-baseline")
+             "python3 -u bench.py --workload {workload}{index} --steps 50 --warmup 10 --no-cpu-baseline --no-extras")
 
 
 def tag(workload, index):
@@ -629,7 +693,7 @@ def summarize_trace(workload, index, trace_dir):
 
 MFMA_CMD = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
             "-d <out> -o run -- python3 -u bench.py --workload {workload}{index} --steps 3 --warmup 1 --eager "
-            "--no-cpu-baseline")
+            "--no-cpu-baseline --no-extras")
 NUM_XCD, NUM_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 
