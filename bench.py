@@ -471,19 +471,19 @@ def main():
                 st.step(i % copies)
         graphs = None
     else:
-        # one graph holding one step per cache copy, plus one graph per copy for
-        # a remainder, so that exactly the requested number of steps is replayed
-        g_all = graph_of(torch, [lambda c=c: st.step(c) for c in range(copies)])
+        # the timed steps are one graph of exactly `steps` steps (cycling the
+        # cache copies), so that the host launches them with one replay; the
+        # warm-up steps are another graph, and one graph per copy serves the
+        # single-step latency samples below
+        g_warm = graph_of(torch, [lambda i=i: st.step(i % copies) for i in range(max(args.warmup, 1))])
+        g_timed = graph_of(torch, [lambda i=i: st.step(i % copies) for i in range(args.steps)])
         graphs = [graph_of(torch, [lambda c=c: st.step(c)]) for c in range(copies)]
 
         def run_steps(k):
-            full, rem = divmod(k, copies)
-            for _ in range(full):
-                g_all.replay()
-            for i in range(rem):
-                graphs[i].replay()
+            (g_timed if k == args.steps else g_warm).replay()
 
-    run_steps(args.warmup)
+    if args.warmup > 0 or args.eager:
+        run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run_steps(args.steps)
@@ -569,7 +569,7 @@ def main():
                         "q_heads": hq}
     del st, g_lse, g_plain, graphs
     if not args.eager:
-        del g_all
+        del g_warm, g_timed
     torch.cuda.empty_cache()
     if args.workload == "fp8_kv" and not idx_fp8 and not args.no_extras:
         res["other_workloads"] = {}

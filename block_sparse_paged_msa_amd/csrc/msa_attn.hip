@@ -44,15 +44,54 @@ constexpr int kHalfPartStride = 2 * kHeadTile + kHeadTile * kDim / 2;  // m[16],
 constexpr int kLdsRow = kDim + 4;                               // padded [head][dim] rows
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / kPage;
 
+// 4x4 transpose of (register, 16-lane row) with the row swaps of gfx950:
+// afterwards register r of lane (row g, column c) holds what register g of
+// lane (row r, column c) held.
+__device__ __forceinline__ void transpose_rows4(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3) {
+  auto s32 = [](uint32_t& a, uint32_t& b) {  // rows 2, 3 of a <-> rows 0, 1 of b
+    const auto p = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = p[0];
+    b = p[1];
+  };
+  auto s16 = [](uint32_t& a, uint32_t& b) {  // rows 1, 3 of a <-> rows 0, 2 of b
+    const auto p = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = p[0];
+    b = p[1];
+  };
+  s32(r0, r2);
+  s32(r1, r3);
+  s16(r0, r1);
+  s16(r2, r3);
+}
+
 // One 16-token sub-page of K and V in registers, as loaded: bf16 operands, or
 // the raw e4m3fn codes (half the registers), widened to bf16 at use.
+// fp8 V arrives as two 16-byte runs per lane (lane l: all 16 tokens of dim l,
+// then of dim 64 + l), a quarter of the load instructions of one operand
+// per load; prep_v() turns them into the operands with a transpose across
+// the four 16-lane rows once they are needed.
 template <int KV_FP8, int SCALE_MODE>
 struct SubPage {
   using KRaw = typename std::conditional<KV_FP8 != 0, u32x2, bf16x8>::type;
   using VRaw = typename std::conditional<KV_FP8 != 0, uint32_t, i16x4>::type;
   KRaw k[4];     // A operand of S^T: token lane%16, dims kc*32 + 8*(lane/16)..+7
   VRaw v[8];     // A operand of O^T: dim dt*16 + lane%16, tokens 4*(lane/16)..+3
+  u32x4 vw[2];   // fp8: V as loaded (dims lane and 64 + lane, 16 tokens each)
   f32x4 ks, vs;  // per-token scales of tokens 4*(lane/16)..+3
+
+  __device__ __forceinline__ void prep_v() {
+    if constexpr (KV_FP8 != 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t r0 = vw[h].x, r1 = vw[h].y, r2 = vw[h].z, r3 = vw[h].w;
+        transpose_rows4(r0, r1, r2, r3);
+        v[4 * h] = r0;
+        v[4 * h + 1] = r1;
+        v[4 * h + 2] = r2;
+        v[4 * h + 3] = r3;
+      }
+    }
+  }
 
   __device__ __forceinline__ bf16x8 k_op(int kc) const {
     if constexpr (KV_FP8 != 0) {
@@ -82,10 +121,17 @@ __device__ __forceinline__ void load_sub(const MsaAttnArgs& a, int sub, int lane
   const char* kp = static_cast<const char*>(a.k_cache) + base + lane * 8 * elt;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) s.k[kc] = __builtin_nontemporal_load(reinterpret_cast<const KRaw*>(kp + kc * 512 * elt));
-  const char* vp = static_cast<const char*>(a.v_cache) + base + ((lane & 15) * kSub + (lane >> 4) * 4) * elt;
+  if constexpr (KV_FP8 != 0) {
+    // dim-major fp8 sub-page: dim d's 16 tokens are the 16 bytes at 16*d
+    const char* vp = static_cast<const char*>(a.v_cache) + base + lane * 16;
+    s.vw[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
+    s.vw[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 64 * kSub));
+  } else {
+    const char* vp = static_cast<const char*>(a.v_cache) + base + ((lane & 15) * kSub + (lane >> 4) * 4) * elt;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    s.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const VRaw*>(vp + dt * 16 * kSub * elt));
+    for (int dt = 0; dt < 8; ++dt)
+      s.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const VRaw*>(vp + dt * 16 * kSub * elt));
+  }
   if constexpr (SCALE_MODE == 2) {
     s.ks = *reinterpret_cast<const f32x4*>(a.k_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
     s.vs = *reinterpret_cast<const f32x4*>(a.v_scale + static_cast<size_t>(sub) * kSub + (lane >> 4) * 4);
@@ -123,6 +169,8 @@ __device__ __forceinline__ void attend_pair(WaveState& st, SubPage<KV_FP8, SCALE
     mloc = fmaxf(mloc, fmaxf(z0[i], z1[i]));
   }
   const float m_new = fmaxf(st.m, max_across_rows(mloc));  // finite: token 0 of sub-page 0 is valid
+  sp[0].prep_v();
+  if (nval1 > 0) sp[1].prep_v();
   const float alpha = fast_exp2(st.m - m_new);
   float psum = 0.f, e0[4], e1[4];
 #pragma unroll
