@@ -100,9 +100,10 @@ WsLayout ws_layout(int num_rows, int num_q_heads, int max_ctx, int ld_s) {
   WsLayout w;
   size_t off = 0;
   w.partials = off;
+  // one slot per (row, head group, split): m[16], l[16] fp32 + fp16 acc[16][128]
   if (p.nsplit > 1)
-    off += align256(sizeof(float) * static_cast<size_t>(num_rows) * p.hgroups * p.nsplit *
-                    (2 * kHeadTile + kHeadTile * kDim));
+    off += align256(static_cast<size_t>(num_rows) * p.hgroups * p.nsplit *
+                    (sizeof(float) * 2 * kHeadTile + sizeof(uint16_t) * kHeadTile * kDim));
   w.scores = off;
   if (ld_s > 0) off += align256(sizeof(float) * static_cast<size_t>(num_rows) * ld_s);
   w.total = off;

@@ -16,8 +16,11 @@
 // scale multiplies the logit, a per-token V scale multiplies the probability
 // fed to the PV product; scalar scales fold into the logit scale and the final
 // normalisation. The four waves merge through LDS. A row split over several
-// workgroups leaves one partial (max, sum, unnormalised output) per split;
-// msa_merge_kernel combines them after the kernel boundary, in split order.
+// workgroups leaves one partial per split, in the block-major path's slot
+// format: max and sum in fp32 and the unnormalised output in fp16, scaled by
+// a power of two that puts each head's largest magnitude in [1/2, 1) (the
+// exponent folded into the max and the sum); msa_merge_kernel combines them
+// after the kernel boundary, in split order.
 //
 // Optional extras (vLLM PR #54404 page, 实现拆解 items 1-2): the natural-log
 // log-sum-exp of each (row, head)'s scaled logits, ln 2 * (m + log2 l) in the
@@ -39,7 +42,6 @@ using namespace msa;
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kPartStride = 2 * kHeadTile + kHeadTile * kDim;  // m[16], l[16], acc[16][128]
 constexpr int kHalfPartStride = 2 * kHeadTile + kHeadTile * kDim / 2;  // m[16], l[16], fp16 acc[16][128]
 constexpr int kLdsRow = kDim + 4;                               // padded [head][dim] rows
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / kPage;
@@ -339,15 +341,25 @@ __device__ __forceinline__ void attend_split(const MsaAttnArgs& a, MergeLds& ml,
       a.lse_out[static_cast<size_t>(n) * a.num_q_heads + hgi * kHeadTile + th] = (M + log2f(Lsum)) * kLn2;
     return;
   }
-  // partial: a scalar V scale is folded in here (the merge is linear in acc);
-  // it is read once, by the merge, so it is stored non-temporal
-  float* part = a.partials + ((static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit + split) * kPartStride;
+  // partial: a scalar V scale is folded in here (the merge is linear in
+  // acc), with the head's exponent ex from its largest |acc| (the 16 threads
+  // of a head are one 16-lane row); it is read once, by the merge, so it is
+  // stored non-temporal
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(acc0[i]), fabsf(acc1[i])));
+  mx = max16(mx) * fabsf(vscal);
+  const int ex = (mx > 0.f) ? clampi(__builtin_amdgcn_frexp_expf(mx), -kHalfExpRange, kHalfExpRange) : 0;
+  const float f = ldexpf(vscal, -ex);
+  float* part = a.partials + ((static_cast<size_t>(n) * a.num_hgroups + hgi) * a.nsplit + split) * kHalfPartStride;
   if ((tid & 15) == 0) {
-    part[th] = M;
-    part[kHeadTile + th] = Lsum;
+    part[th] = M + static_cast<float>(ex);
+    part[kHeadTile + th] = ldexpf(Lsum, -ex);
   }
-  __builtin_nontemporal_store(acc0 * vscal, reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td));
-  __builtin_nontemporal_store(acc1 * vscal, reinterpret_cast<f32x4*>(part + 2 * kHeadTile + th * kDim + td + 4));
+  uint16_t* acc = reinterpret_cast<uint16_t*>(part + 2 * kHeadTile) + th * kDim + td;
+  __builtin_nontemporal_store(u32x4{pk_f16(acc0.x * f, acc0.y * f), pk_f16(acc0.z * f, acc0.w * f),
+                                    pk_f16(acc1.x * f, acc1.y * f), pk_f16(acc1.z * f, acc1.w * f)},
+                              reinterpret_cast<u32x4*>(acc));
 }
 
 __device__ __forceinline__ void write_zero_row(const MsaAttnArgs& a, int n, int hgi) {
@@ -530,11 +542,13 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
                                       ws.kk, ctx, qb);
 }
 
-// Combines the split partials of rows that needed more than one split. One
+// Combines the partials of rows split over several workgroups (ALL_ROWS
+// false: rows of one split were written by the attention kernel) or every
+// row's block partials (ALL_ROWS true: a row with no slot gets zeros). One
 // wave per (row, query head): lane group g = lane/16 takes splits g, g+4,
 // g+8, ... and eight dims (lane%16)*8.. of each, so one round of loads
-// fetches thirty-two splits of 512 B. The four groups are then combined through
-// row and half swaps. All weights are log2-domain 2^(m_s - max).
+// fetches thirty-two splits of 256 B. The four groups are then combined
+// through row and half swaps. All weights are log2-domain 2^(m_s - max).
 constexpr int kMergeThreads = 64;
 
 struct MergeState {
@@ -568,9 +582,9 @@ __device__ __forceinline__ MergeState merge_partner(const MergeState& x) {
   return r;
 }
 
-template <bool HALF>
+template <bool ALL_ROWS>
 __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a, const int32_t* ctxp) {
-  constexpr int kStride = HALF ? kHalfPartStride : kPartStride;
+  constexpr int kStride = kHalfPartStride;
   const int lane = threadIdx.x;
   // workgroups go to the 8 XCDs in turn: the heads of row n are numbered so
   // that they all land on XCD n % 8 and share its L2 copy of each slot's
@@ -595,24 +609,17 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
       const float* ps = base + static_cast<size_t>(min(s0 + sg + 4 * j, a.nsplit - 1)) * kStride;
       ms[j] = ps[th];
       ls[j] = ps[kHeadTile + th];
-      if constexpr (HALF) {
-        const u32x4 h = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ps + 2 * kHeadTile) + th * kDim + td));
-        x0[j] = f32x4{f16_lo(h.x), f16_hi(h.x), f16_lo(h.y), f16_hi(h.y)};
-        x1[j] = f32x4{f16_lo(h.z), f16_hi(h.z), f16_lo(h.w), f16_hi(h.w)};
-      } else {
-        x0[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td));
-        x1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ps + 2 * kHeadTile + th * kDim + td + 4));
-      }
+      const u32x4 h = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ps + 2 * kHeadTile) + th * kDim + td));
+      x0[j] = f32x4{f16_lo(h.x), f16_hi(h.x), f16_lo(h.y), f16_hi(h.y)};
+      x1[j] = f32x4{f16_lo(h.z), f16_hi(h.z), f16_lo(h.w), f16_hi(h.w)};
     }
   };
   fetch(0);
   const float sink2 = a.sinks ? a.sinks[head] * kLog2e : -INFINITY;
   const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
   const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
-  // per-row partials: a row of one split was written by the attention
-  // kernel; block partials: every row is written here (none listed: zeros)
-  if (!HALF && nsplit_n <= 1) return;
+  if (!ALL_ROWS && nsplit_n <= 1) return;
   MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < nsplit_n; s0 += 4 * kPer) {
     if (s0 > 0) fetch(s0);
@@ -1081,6 +1088,7 @@ hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, in
 
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s) {
   if (a.nsplit <= 1 && !a.half_partials) return hipSuccess;  // block partials: always merged, one slot too
+  // (every split partial is in the fp16 slot format)
   const int64_t grid = (static_cast<int64_t>(a.num_rows) + 7) / 8 * 8 * a.num_q_heads;
   const int32_t* ctxp = a.scores ? static_cast<const int32_t*>(a.ctx_out) : a.ctx_in;
   if (a.half_partials)

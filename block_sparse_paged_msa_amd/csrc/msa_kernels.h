@@ -73,8 +73,10 @@ struct MsaAttnArgs {
   uint16_t* out;
   float* lse_out;      // [rows][Hq] natural-log LSE, or null
   const float* sinks;  // [Hq] per-head sink logits, or null
-  float* partials;     // [rows][hgroups][nsplit] slots: m[16], l[16] fp32, then acc[16][128]
-  int32_t half_partials;  // acc stored as fp16 scaled by a power of two (block-major path), else fp32
+  // [rows][hgroups][nsplit] slots: m[16], l[16] fp32, then acc[16][128] fp16
+  // scaled by a power of two folded into m and l
+  float* partials;
+  int32_t half_partials;  // block-major path: every row is merged from its slots (one slot too)
   int32_t ld_table;    // row stride of the table (8*topk in fused mode)
   int32_t ld_s;
   int32_t ld_bt;
