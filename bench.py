@@ -484,12 +484,19 @@ def main():
 
     if args.warmup > 0 or args.eager:
         run_steps(args.warmup)
+    # the K timed steps, bracketed by synchronisations and timed with the
+    # host's wall clock (graph launch and final wait included); HIP events on
+    # the launching stream give the GPU's own time for the same steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     run_steps(args.steps)
+    ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec = (t1 - t0) / args.steps
+    sec_events = ev0.elapsed_time(ev1) * 1e-3 / args.steps
     print(f"[bench] {args.workload}: {sec * 1e6:.2f} us/step over {args.steps} steps, {copies} copies",
           file=sys.stderr, flush=True)
 
@@ -537,6 +544,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": sec * 1e3,
+        "ms_per_step_gpu_events": sec_events * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

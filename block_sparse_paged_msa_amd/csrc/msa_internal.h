@@ -179,6 +179,7 @@ struct MsaScoreArgs {
   int32_t skip_big;        // requests with more than 64 rows are left to the tile kernel
 };
 hipError_t msa_launch_score(const MsaScoreArgs& a, int num_wgs, hipStream_t s);
-// Requests with more than 64 query rows: 256-row x 8-page MFMA tiles.
+// Requests with more than 64 query rows: 512-row blocks x runs of 8 (or 16)
+// index-K pages, one MFMA tile workgroup per item.
 hipError_t msa_launch_score_tile(const MsaScoreArgs& a, int num_wgs, hipStream_t s);
 int msa_score_tile_items_bound(int64_t num_rows, int64_t blocks_bound);
