@@ -168,6 +168,38 @@ __device__ __forceinline__ Unit slot_unit(const MsaScoreArgs& a, int u) {
   return w;
 }
 
+// What a first-group slot's validity and page depend on, loaded together:
+// the request's raw lengths and the slot's raw block-table entry (a slot at
+// or past slots_a loads nothing).
+struct SlotHead {
+  int r, j;
+  int L, ql, bt;
+};
+
+__device__ __forceinline__ SlotHead slot_head(const MsaScoreArgs& a, int u) {
+  SlotHead h = {0, 0, 0, 0, 0};
+  if (u < a.num_reqs * a.blocks_per_req) {
+    h.r = u / a.blocks_per_req;
+    h.j = u - h.r * a.blocks_per_req;
+    h.L = a.seq_lens[h.r];
+    h.ql = a.query_lens[h.r];
+    h.bt = a.block_table[static_cast<size_t>(h.r) * a.ld_bt + h.j];
+  }
+  return h;
+}
+
+// The unit of a first-group slot (the same unit as slot_unit gives).
+__device__ __forceinline__ Unit head_unit(const MsaScoreArgs& a, const SlotHead& h) {
+  Unit w;
+  w.r = h.r;
+  w.j = h.j;
+  w.g = 0;
+  w.L = clampi(h.L, 0, a.len_cap);
+  w.ql = clampi(h.ql, 0, w.L);
+  w.valid = w.ql > 0 && w.j * kPage < w.L && !(a.skip_big && w.ql > kRowsPerUnit);
+  return w;
+}
+
 // Extra row groups (g >= 1): the prefix over requests numbers them.
 __device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_extra, const int* s_cuq, int ue) {
   int lo = 0, hi = a.num_reqs;  // last r with extra[r] <= ue
@@ -207,12 +239,27 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   // sums query_lens below its request itself and never waits on a barrier.
   IndexPage<IDX_FP8> kb;
   if (!writer && a.num_rows <= kRowsPerUnit) {
+    // A slot's lengths and its block-table entry are requested together (the
+    // entry lies inside the table for every slot, j < S <= ld_bt, and is
+    // ignored when the slot is past the request's blocks), and the next
+    // slot's once the current page is requested, so a page load waits for one
+    // round trip at the start and none after it. The rows below the request
+    // are summed from loads issued before the page's and added after it (a
+    // loop that adds as it loads would wait for them first).
+    SlotHead h = slot_head(a, u);
     for (; u < slots_a; u += nwaves) {
-      const Unit w = slot_unit(a, u);
-      if (!w.valid) continue;
-      int q0 = 0;
-      for (int r = lane; r < w.r; r += 64) q0 += clampi(a.query_lens[r], 0, clampi(a.seq_lens[r], 0, a.len_cap));
-      kb.load(a, page_of(a, w), lane);
+      const Unit w = head_unit(a, h);
+      const int page = clampi(h.bt, 0, a.num_pages - 1);
+      if (!w.valid) {
+        h = slot_head(a, u + nwaves);
+        continue;
+      }
+      const int rl = min(lane, R - 1);
+      const int ql_raw = a.query_lens[rl], l_raw = a.seq_lens[rl];
+      kb.load(a, page, lane);
+      h = slot_head(a, u + nwaves);
+      int q0 = (lane < w.r) ? clampi(ql_raw, 0, clampi(l_raw, 0, a.len_cap)) : 0;
+      for (int r = lane + 64; r < w.r; r += 64) q0 += clampi(a.query_lens[r], 0, clampi(a.seq_lens[r], 0, a.len_cap));
       q0 = __builtin_amdgcn_readlane(wave_inclusive_scan(q0), 63);
       score_unit(a, w, q0, kb, lane);
     }
