@@ -156,18 +156,6 @@ __device__ __forceinline__ void score_unit(const MsaScoreArgs& a, const Unit& w,
   }
 }
 
-// Fixed-stride slot r*S + j (first row group), from global memory only.
-__device__ __forceinline__ Unit slot_unit(const MsaScoreArgs& a, int u) {
-  Unit w;
-  w.r = u / a.blocks_per_req;
-  w.j = u - w.r * a.blocks_per_req;
-  w.g = 0;
-  w.L = clampi(a.seq_lens[w.r], 0, a.len_cap);
-  w.ql = clampi(a.query_lens[w.r], 0, w.L);
-  w.valid = w.ql > 0 && w.j * kPage < w.L && !(a.skip_big && w.ql > kRowsPerUnit);
-  return w;
-}
-
 // What a first-group slot's validity and page depend on, loaded together:
 // the request's raw lengths and the slot's raw block-table entry (a slot at
 // or past slots_a loads nothing).
@@ -188,7 +176,7 @@ __device__ __forceinline__ SlotHead slot_head(const MsaScoreArgs& a, int u) {
   return h;
 }
 
-// The unit of a first-group slot (the same unit as slot_unit gives).
+// The unit of a first-group slot r*S + j.
 __device__ __forceinline__ Unit head_unit(const MsaScoreArgs& a, const SlotHead& h) {
   Unit w;
   w.r = h.r;
@@ -200,8 +188,10 @@ __device__ __forceinline__ Unit head_unit(const MsaScoreArgs& a, const SlotHead&
   return w;
 }
 
-// Extra row groups (g >= 1): the prefix over requests numbers them.
-__device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_extra, const int* s_cuq, int ue) {
+// Extra row groups (g >= 1): the prefix over requests numbers them; the
+// request's lengths come from the prefix in LDS.
+__device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_extra, const int* s_cuq,
+                                           const int* s_ctx0, int ue) {
   int lo = 0, hi = a.num_reqs;  // last r with extra[r] <= ue
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -210,7 +200,7 @@ __device__ __forceinline__ Unit extra_unit(const MsaScoreArgs& a, const int* s_e
   Unit w;
   w.r = lo;
   w.ql = s_cuq[lo + 1] - s_cuq[lo];
-  w.L = clampi(a.seq_lens[lo], 0, a.len_cap);
+  w.L = s_ctx0[lo] + w.ql;
   const int more = (w.ql + kRowsPerUnit - 1) / kRowsPerUnit - 1;  // groups 1..more
   const int local = ue - s_extra[lo];
   w.j = more > 0 ? local / more : 0;
@@ -270,8 +260,9 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   Unit w0 = {};
   const bool first_is_a = u < slots_a;
   if (first_is_a) {
-    w0 = slot_unit(a, u);
-    if (w0.valid) kb.load(a, page_of(a, w0), lane);
+    const SlotHead h0 = slot_head(a, u);
+    w0 = head_unit(a, h0);
+    if (w0.valid) kb.load(a, clampi(h0.bt, 0, a.num_pages - 1), lane);
   }
 
   // running sums over the requests of (query rows, KV tokens, blocks, score
@@ -355,9 +346,18 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   }
   const int total = slots_a + s_extra[R];
   for (; u < total; u += nwaves) {
-    const Unit w = u < slots_a ? slot_unit(a, u) : extra_unit(a, s_extra, s_cuq, u - slots_a);
+    Unit w;
+    int page;
+    if (u < slots_a) {  // lengths and block-table entry requested together
+      const SlotHead h = slot_head(a, u);
+      w = head_unit(a, h);
+      page = clampi(h.bt, 0, a.num_pages - 1);
+    } else {
+      w = extra_unit(a, s_extra, s_cuq, s_ctx0, u - slots_a);
+      page = w.valid ? page_of(a, w) : 0;
+    }
     if (!w.valid) continue;
-    kb.load(a, page_of(a, w), lane);
+    kb.load(a, page, lane);
     score_unit(a, w, s_cuq[w.r], kb, lane);
   }
 }
