@@ -86,7 +86,7 @@ struct MsaAttnArgs {
   int32_t num_q_heads;
   int32_t num_hgroups;
   int32_t max_ctx;
-  int32_t split_tok;   // tokens per workgroup, a multiple of 128
+  int32_t split_tok;   // tokens per workgroup, a power of two >= 64 (one sub-page per wave)
   int32_t nsplit;      // ceil(max_ctx / split_tok)
   int32_t num_subpages;
   float scale_log2;    // sm_scale * log2(e)
