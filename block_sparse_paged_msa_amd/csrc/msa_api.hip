@@ -118,14 +118,18 @@ WsLayout ws_layout(int num_rows, int num_q_heads, int max_ctx, int ld_s) {
 // slots, the selected block ids, then the scores as above.
 constexpr int32_t kBlockMajorRows = 2048;
 constexpr int32_t kBlockMajorMaxRows = 1 << 18;  // rows fit the row field of a list entry
+// Launches of at most this many (request, block) items count each item's
+// rows and balance the block-major grid by entries (one 4-byte count per
+// item in the workspace); larger ones hand out items by grid stride.
+constexpr int64_t kBalancedItemsMax = 16384;
 
 struct BmLayout {
-  size_t partials, words, scores, total;
+  size_t partials, words, counts, scores, total;
 };
 
 // Block-major workspace: partial slots, each row's selection words (one
-// 8-byte word per 32 blocks of ceil(max_seq_len / 128)), then the scores when
-// the caller passes no score buffer.
+// 8-byte word per 32 blocks of ceil(max_seq_len / 128)), the per-item row
+// counts, then the scores when the caller passes no score buffer.
 int bm_words(int nbmax) { return (nbmax + 31) / 32; }
 
 BmLayout bm_layout(int num_rows, int nbmax, int num_q_heads, int topk, int ld_s) {
@@ -138,6 +142,8 @@ BmLayout bm_layout(int num_rows, int nbmax, int num_q_heads, int topk, int ld_s)
                   (sizeof(float) * 2 * kHeadTile + sizeof(uint16_t) * kHeadTile * kDim));
   w.words = off;
   off += align256(sizeof(uint64_t) * static_cast<size_t>(num_rows) * bm_words(nbmax));
+  w.counts = off;
+  off += align256(sizeof(int32_t) * static_cast<size_t>(kBalancedItemsMax));
   w.scores = off;
   if (ld_s > 0) off += align256(sizeof(float) * static_cast<size_t>(num_rows) * ld_s);
   w.total = off;
@@ -438,6 +444,12 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
       bk.num_reqs = batch->num_reqs;
       bk.topk = topk;
       bk.len_cap = len_cap(batch);
+      bk.counts = nullptr;
+      if (nbmax >= 1 && static_cast<int64_t>(batch->num_reqs) * nbmax <= kBalancedItemsMax) {
+        bk.counts = reinterpret_cast<int32_t*>(wsb + bw.counts);
+        st = hip_status(msa_launch_block_count(bk, batch->num_rows, s));
+        if (st != MSA_OK) return st;
+      }
       int64_t wgs = static_cast<int64_t>(batch->num_reqs) * nbmax;
       if (wgs > 2LL * cu_count()) wgs = 2LL * cu_count();
       if (wgs < 1) wgs = 1;  // max_seq_len 0: no item, but a valid launch

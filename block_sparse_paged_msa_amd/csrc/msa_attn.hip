@@ -660,15 +660,25 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
 // (request r, block b of r): the workgroup finds the rows of r that selected
 // b from the selection words the top-k step wrote (one 8-byte word per row
 // gives both the bit and the block's rank in the row's selection), compacts
-// them into an LDS list, copies the block's K and V (one contiguous run
-// each: its 8 sub-pages are consecutive) into LDS once if the list is not
-// empty, and every wave takes one (row, head group) of the list at a time:
-// all 128 tokens' logits from LDS, the block's softmax statistics, and the
-// PV products. The block's partial (max, sum, unnormalised output) goes to
-// the row's slot for the block's rank, and msa_merge_kernel combines the
-// slots in rank order (one slot too), as it does for token splits, and
-// applies sinks and the LSE output. The order of a list does not matter:
-// every entry writes its own slot.
+// them in row order into an LDS list, copies the block's K and V (one
+// contiguous run each: its 8 sub-pages are consecutive) into LDS once if the
+// list is not empty, and every wave takes one (row, head group) of the list
+// at a time: all 128 tokens' logits from LDS, the block's softmax
+// statistics, and the PV products. The block's partial (max, sum,
+// unnormalised output) goes to the row's slot for the block's rank, and
+// msa_merge_kernel combines the slots in rank order (one slot too), as it
+// does for token splits, and applies sinks and the LSE output.
+//
+// Items differ in size (a block that many rows choose is a long list), so
+// when msa_block_count_kernel has counted each item's rows the launch is
+// balanced by cost, not items: an item costs kItemCost plus one per entry,
+// items are laid end to end (entries in row order after the fixed part),
+// and workgroup g takes the cost range [C*g/G, C*(g+1)/G) of the C in all,
+// i.e. the entries of the items that fall in it; an item cut between two
+// workgroups is staged by both (vLLM PR #54682 page, 实现拆解 item 1: work
+// mapped to the real amount per request, here per block). Without counts,
+// items go to workgroups by grid stride. Each entry writes its own slot, so
+// the split changes no result.
 constexpr int kBlockThreads = 256;
 constexpr int kRowChunk = 1024;                           // rows of a request examined per pass
 constexpr int kListRankShift = 18;                        // entry = row within the request | rank << 18
@@ -682,9 +692,17 @@ struct BlockLds {
   __attribute__((aligned(16))) uint8_t v[kPlane];                   // V sub-pages, dim-major, pairs interleaved
   float ks[kPage], vs[kPage];
   uint32_t vmax[4];                                                 // per wave: largest |V| bits (bf16, no scales)
-  int ent[kRowChunk];                                               // (row, rank) entries of a chunk
-  int nsel[2];                                                      // entry counters of alternate chunks
+  int ent[kRowChunk];                                               // (row, rank) entries of a pass
+  int scan[4];                                                      // block scan scratch
+  int rng[4];                                                       // balanced range: first and last item, their cost offsets
+  int pcnt[kRowChunk / kBlockThreads][4];                           // hits per (row segment, wave) of a pass
 };
+// Cost of an item in the balanced schedule, in units of one entry: its
+// entries plus a fixed cost for finding its rows (a pass per 1024 rows of
+// the request) and staging its block. Measured on a step of 8198 rows
+// (two 4096-row prefills among decode rows): 4 -> 1170 us, 16 -> 738,
+// 32 -> 708, 48 -> 709, 64 -> 720, 96 -> 790.
+constexpr int kItemCost = 32;
 
 __device__ __forceinline__ bf16x8 lds_k_op(const BlockLds& sh, int i, int kc, int lane) {
   const int e = i * (kSub * kDim) + (kc * 64 + lane) * 8;  // element offset of the operand
@@ -726,10 +744,59 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
   const float zscale = a.scale_log2 * kscal;
   const int pmax = a.num_subpages / kSubsPerPage - 1;
   const int items = bk.num_reqs * bk.nbmax;
-  if (tid == 0) sh.nsel[0] = sh.nsel[1] = 0;
-  int chunk_no = 0;  // running chunk count of this workgroup: picks the counter of a chunk
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+  // this workgroup's items: a grid stride, or with counts the items its cost
+  // range [A, B) meets (the first and the last of them only partly)
+  int it_begin = blockIdx.x, it_stop = items, it_step = gridDim.x;
+  int64_t cost_a = 0, cost_b = 0, p_first = 0, p_last = 0;  // range; cost offsets of its first / last item
+  auto item_cost = [](int c) { return c > 0 ? c + kItemCost : 0; };
+  if (bk.counts) {
+    int64_t t = 0;
+    for (int i = tid; i < items; i += kBlockThreads) t += item_cost(bk.counts[i]);
+    // the total, summed as two 16-bit halves so that no int sum can overflow
+    int t_tot;
+    block256_exclusive_scan(static_cast<int>(t & 0xffff), sh.scan, &t_tot);
+    const int64_t t_lo = t_tot;
+    block256_exclusive_scan(static_cast<int>(t >> 16), sh.scan, &t_tot);
+    const int64_t total_cost = t_lo + (static_cast<int64_t>(t_tot) << 16);
+    cost_a = total_cost * blockIdx.x / gridDim.x;
+    cost_b = total_cost * (blockIdx.x + 1) / gridDim.x;
+    if (tid == 0) {
+      sh.rng[0] = items;
+      sh.rng[1] = -1;
+    }
+    int64_t carry = 0;
+    for (int base = 0; base < items && carry < cost_b; base += kBlockThreads) {
+      const int i = base + tid;
+      const int c = item_cost(i < items ? bk.counts[i] : 0);
+      int tot;
+      const int64_t p = carry + block256_exclusive_scan(c, sh.scan, &tot);
+      if (c > 0 && p <= cost_a && cost_a < p + c) {
+        sh.rng[0] = i;
+        sh.rng[2] = static_cast<int>(cost_a - p);
+      }
+      if (c > 0 && p < cost_b && cost_b <= p + c) {
+        sh.rng[1] = i;
+        sh.rng[3] = static_cast<int>(cost_b - p);
+      }
+      carry += tot;
+    }
+    __syncthreads();
+    it_begin = (cost_a < cost_b) ? sh.rng[0] : items;
+    it_stop = (cost_a < cost_b) ? sh.rng[1] + 1 : items;
+    it_step = 1;
+    p_first = sh.rng[2];  // the range starts this far into its first item
+    p_last = sh.rng[3];   // and ends this far into its last
+  }
+
+  for (int item = it_begin; item < it_stop; item += it_step) {
+    // entries [e_lo, e_hi) of the item (in row order) are this workgroup's:
+    // of an item's cost units the first kItemCost carry no entry
+    const int e_lo = (bk.counts && item == it_begin) ? static_cast<int>(max<int64_t>(p_first - kItemCost, 0)) : 0;
+    const int e_hi = (bk.counts && item == it_stop - 1) ? static_cast<int>(max<int64_t>(p_last - kItemCost, 0))
+                                                         : 0x7fffffff;
+    if (e_lo >= e_hi) continue;
+    if (bk.counts && bk.counts[item] == 0) continue;  // no row chose it
     const int r = item / bk.nbmax, blk = item - r * bk.nbmax;
     const int L = clampi(bk.seq_lens[r], 0, bk.len_cap);
     const int q0 = clampi(bk.cu_q[r], 0, a.num_rows), q1 = clampi(bk.cu_q[r + 1], q0, a.num_rows);
@@ -744,35 +811,50 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
     // top-k step left each row's selection as bit words (block b is bit b%32
     // of word b/32) with the count of selected blocks below each word, so one
     // 8-byte load per row gives both whether the row selected the block and
-    // the block's rank in the row's selection.
-    for (int c0 = q0; c0 < q1; c0 += kRowChunk, ++chunk_no) {
+    // the block's rank in the row's selection. Row i of a pass is held by
+    // thread i % 256 (segment i / 256); each wave's ballot per segment and
+    // the 16 (segment, wave) counts in LDS number the hits in row order.
+    constexpr int kSeg = kRowChunk / kBlockThreads;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int carry = 0;  // entries of the item in earlier passes
+    for (int c0 = q0; c0 < q1 && carry < e_hi; c0 += kRowChunk) {
       const int nc = min(kRowChunk, q1 - c0);
-      uint64_t wd[kRowChunk / kBlockThreads];
+      uint64_t wd[kSeg], hits[kSeg];
 #pragma unroll
-      for (int k = 0; k < kRowChunk / kBlockThreads; ++k) {
+      for (int k = 0; k < kSeg; ++k) {
         const int n = c0 + min(tid + kBlockThreads * k, nc - 1);
         wd[k] = bk.row_words[static_cast<size_t>(n) * bk.row_words_ld + word];
       }
-      const int cur = chunk_no & 1;
-      __syncthreads();  // the previous chunk's entries and the block are no longer read
-      if (tid == 0) sh.nsel[cur ^ 1] = 0;  // the next chunk's counter (its last reader is past this barrier)
 #pragma unroll
-      for (int k = 0; k < kRowChunk / kBlockThreads; ++k) {
-        const int i = tid + kBlockThreads * k;
-        const uint32_t lo = static_cast<uint32_t>(wd[k]), hi = static_cast<uint32_t>(wd[k] >> 32);
-        const bool hit = i < nc && ((lo >> bit) & 1u);
-        const uint64_t mask = __ballot(hit);
-        int base = 0;
-        if (lane == 0 && mask) base = atomicAdd(&sh.nsel[cur], __popcll(mask));
-        base = __shfl(base, 0);
-        if (hit) {
+      for (int k = 0; k < kSeg; ++k) {
+        hits[k] = __ballot(tid + kBlockThreads * k < nc && ((static_cast<uint32_t>(wd[k]) >> bit) & 1u));
+        if (lane == 0) sh.pcnt[k][wave] = __popcll(hits[k]);
+      }
+      // (this barrier also ends every wave's use of the previous pass's
+      // entries and of the staged block)
+      __syncthreads();
+      int pre[kSeg], tot = 0;
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (w == wave) pre[k] = tot;
+          tot += sh.pcnt[k][w];
+        }
+      const int keep_lo = max(e_lo, carry), keep_hi = min(e_hi, carry + tot);
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) {
+        const int idx = carry + pre[k] + __popcll(hits[k] & below);
+        if (((hits[k] >> lane) & 1ull) && idx >= keep_lo && idx < keep_hi) {
+          const uint32_t lo = static_cast<uint32_t>(wd[k]), hi = static_cast<uint32_t>(wd[k] >> 32);
           const int rank = static_cast<int>(hi) + __popc(lo & ((1u << bit) - 1u));
-          sh.ent[base + __popcll(mask & ((1ull << lane) - 1ull))] =
-              static_cast<int>((c0 - q0 + i) | (min(rank, kListRankMax) << kListRankShift));
+          sh.ent[idx - keep_lo] =
+              static_cast<int>((c0 - q0 + tid + kBlockThreads * k) | (min(rank, kListRankMax) << kListRankShift));
         }
       }
+      carry += tot;
       __syncthreads();
-      const int total = sh.nsel[cur];
+      const int total = max(keep_hi - keep_lo, 0);
       if (total == 0) continue;
       if (!staged) {  // the block's K and V, once per item, only when some row selected it
         staged = true;
@@ -1036,6 +1118,46 @@ __global__ __launch_bounds__(kBlockThreads, 2) void msa_attn_block_kernel(MsaAtt
   }
 }
 
+// Rows of each request that selected each of its blocks: workgroup (r, w)
+// counts, over the rows of request r, the bits of selection word w. A wave
+// takes 64 rows at a time and counts each bit with one ballot (lane b keeps
+// bit b's count), so no two lanes ever add to one counter. Every item's
+// count is written (zeros too), so nothing needs clearing.
+__global__ __launch_bounds__(kBlockThreads) void msa_block_count_kernel(MsaBlockArgs bk, int num_rows) {
+  __shared__ int s_cnt[4][32];
+  const int r = blockIdx.x, w = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q0 = clampi(bk.cu_q[r], 0, num_rows), q1 = clampi(bk.cu_q[r + 1], q0, num_rows);
+  int acc = 0;
+  constexpr int kBatch = 8;  // 64-row groups per wave requested at once
+  for (int n0 = q0 + 64 * wave; n0 < q1; n0 += kBatch * kBlockThreads) {
+    uint32_t bits[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int n = n0 + j * kBlockThreads + lane;
+      bits[j] = static_cast<uint32_t>(bk.row_words[static_cast<size_t>(min(n, q1 - 1)) * bk.row_words_ld + w]);
+      if (n >= q1) bits[j] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      // groups with no selected block need no ballots
+      const uint64_t m = __ballot(bits[j] != 0u);
+      if (m == 0ull) continue;
+#pragma unroll
+      for (int b = 0; b < 32; ++b) {
+        const int c = __popcll(__ballot((bits[j] >> b) & 1u));
+        acc += (lane == b) ? c : 0;
+      }
+    }
+  }
+  if (lane < 32) s_cnt[wave][lane] = acc;
+  __syncthreads();
+  const int b = 32 * w + static_cast<int>(threadIdx.x);
+  if (threadIdx.x < 32 && b < bk.nbmax)
+    bk.counts[static_cast<size_t>(r) * bk.nbmax + b] =
+        s_cnt[0][threadIdx.x] + s_cnt[1][threadIdx.x] + s_cnt[2][threadIdx.x] + s_cnt[3][threadIdx.x];
+}
+
 template <int KV_FP8, int SCALE_MODE>
 hipError_t launch(const MsaAttnArgs& a, hipStream_t s) {
   const int64_t grid = static_cast<int64_t>(a.num_rows) * a.num_hgroups * a.nsplit;
@@ -1070,6 +1192,12 @@ hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, h
   }
   if (scale_mode == 1) return launch<1, 1>(a, s);
   return launch<1, 2>(a, s);
+}
+
+hipError_t msa_launch_block_count(const MsaBlockArgs& b, int num_rows, hipStream_t s) {
+  hipLaunchKernelGGL(msa_block_count_kernel, dim3(static_cast<unsigned>(b.num_reqs), static_cast<unsigned>(b.row_words_ld)),
+                     dim3(kBlockThreads), 0, s, b, num_rows);
+  return hipGetLastError();
 }
 
 hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, int kv_dtype, int scale_mode,

@@ -131,6 +131,10 @@ struct MsaBlockArgs {
   int32_t num_reqs;
   int32_t topk;
   int32_t len_cap;
+  int32_t* counts;           // [num_reqs][nbmax] rows per item (msa_block_count_kernel), or null:
+                             // items by grid stride instead of entries balanced over the grid
 };
 hipError_t msa_launch_attn_block(const MsaAttnArgs& a, const MsaBlockArgs& b, int kv_dtype, int scale_mode,
                                  int num_wgs, hipStream_t s);
+// Fills b.counts from the selection words (grid num_reqs x row_words_ld).
+hipError_t msa_launch_block_count(const MsaBlockArgs& b, int num_rows, hipStream_t s);

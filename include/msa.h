@@ -216,9 +216,11 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  *   msa_decode_workspace_bytes(num_rows, max_seq_len, num_q_heads, topk,
  *   block_scores ? 0 : ld_s) bytes take the block-major path instead: the
  *   top-k step runs on its own and also leaves each row's selection as bit
- *   words (4 launches in all); then one workgroup per (request, block) that
- *   some row of the request selected attends every such row from one copy of
- *   the block's K/V, and the per-block partials are merged. Each partial
+ *   words; when the batch has at most 16384 (request, block) pairs the rows
+ *   that chose each block are counted (one more launch) and the attention
+ *   grid is balanced by (row, block) pairs rather than blocks; the
+ *   workgroups attend the rows that chose a block from one copy of the
+ *   block's K/V, and the per-block partials are merged (4 or 5 launches). Each partial
  *   keeps its max and sum in fp32 and its 16x128 accumulator in fp16, scaled by a power of two so that its
  *   largest magnitude is below 1: from the accumulator itself, or, for bf16
  *   K/V with no scales, from the bound 128 * max|V| of the block (the error
@@ -356,7 +358,8 @@ size_t msa_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t max_ct
  * take the block-major path on launches of 2048 to 262144 rows (the batch's
  * num_rows and max_seq_len): per row, num_q_heads/16 (rounded up) x topk
  * partials of 4224 bytes and one 8-byte selection word per 32 blocks of
- * ceil(max_seq_len/128); and the scores when ld_s > 0. For other row counts
+ * ceil(max_seq_len/128); 64 KiB of per-block row counts; and the scores when
+ * ld_s > 0. For other row counts
  * it equals msa_workspace_bytes(num_rows, num_q_heads, 128*topk, ld_s).
  * Returns 0 for invalid arguments.
  */

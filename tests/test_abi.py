@@ -66,18 +66,21 @@ def test_workspace_bytes_monotone_and_aligned():
 def test_decode_workspace_bytes_block_major_layout():
     # below 2048 rows the fused step's per-row workspace; from 2048 rows the
     # block-major one: per row and head group, topk slots of 32 fp32 (m, l)
-    # and 16x128 fp16, plus one 8-byte selection word per 32 blocks, each
-    # region rounded up to 256 bytes, then the scores when ld_s > 0
+    # and 16x128 fp16, plus one 8-byte selection word per 32 blocks, 64 KiB
+    # of per-block row counts, each region rounded up to 256 bytes, then the
+    # scores when ld_s > 0
     def up(x):
         return (x + 255) // 256 * 256
     assert msa.msa_decode_workspace_bytes(100, 32768, 16, 32, 0) == msa.msa_workspace_bytes(100, 16, 128 * 32, 0)
     n, L, hq, topk, ld_s = 8198, 32768, 16, 32, 256
     slots = up(n * 1 * topk * (32 * 4 + 16 * 128 * 2))
     words = up(n * ((L // 128 + 31) // 32) * 8)
+    counts = 16384 * 4
     got = msa.msa_decode_workspace_bytes(n, L, hq, topk, 0)
-    assert got == max(slots + words, msa.msa_workspace_bytes(n, hq, 128 * topk, 0))
+    assert got == max(slots + words + counts, msa.msa_workspace_bytes(n, hq, 128 * topk, 0))
     with_scores = msa.msa_decode_workspace_bytes(n, L, hq, topk, ld_s)
-    assert with_scores == max(slots + words + up(n * ld_s * 4), msa.msa_workspace_bytes(n, hq, 128 * topk, ld_s))
+    assert with_scores == max(slots + words + counts + up(n * ld_s * 4),
+                              msa.msa_workspace_bytes(n, hq, 128 * topk, ld_s))
     # two head groups double the slots
     assert msa.msa_decode_workspace_bytes(n, L, 24, topk, 0) >= 2 * slots
     for bad in ((-1, L, hq, topk, 0), (n, -1, hq, topk, 0), (n, L, 0, topk, 0), (n, L, hq, 0, 0), (n, L, hq, topk, -1)):

@@ -37,6 +37,10 @@ CASES = [
     ([4000, 9000, 500, 7000], [0, 2100, 0, 0], 8, 16, syn.KV_BF16, syn.SCALE_NONE),
     # three head groups, the last one partial
     ([5000, 3000], [1300, 800], 8, 40, syn.KV_BF16, syn.SCALE_NONE),
+    # more (request, block) pairs (40 x 469) than the launches that count
+    # each block's rows and balance the grid by entries: blocks go to
+    # workgroups by grid stride
+    ([60000] + [2000 + 600 * i for i in range(39)], [2100] + [1] * 39, 16, 16, syn.KV_BF16, syn.SCALE_NONE),
 ]
 
 
