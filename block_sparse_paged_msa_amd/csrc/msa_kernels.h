@@ -116,9 +116,10 @@ hipError_t msa_launch_insert(const MsaInsertArgs& a, hipStream_t s);
 constexpr int kMaxSplitTokens = 8192;
 hipError_t msa_launch_attn(const MsaAttnArgs& a, int kv_dtype, int scale_mode, hipStream_t s);
 hipError_t msa_launch_merge(const MsaAttnArgs& a, hipStream_t s);
-// Block-major attention (prefill-sized fused steps): one workgroup per
-// (request, block) serves every row of the request that selected the block,
-// found from the selection words written by the top-k kernel.
+// Block-major attention (prefill-sized fused steps): a work item is a
+// (request, block) and serves every row of the request that selected the
+// block, found from the selection words written by the top-k kernel; items
+// go to workgroups by grid stride, or balanced by cost when counts are given.
 // Uses from MsaAttnArgs: q, caches and scales, block_table, ld_bt, out,
 // lse_out, sinks, partials (nsplit = topk slots per row and head group),
 // num_rows, num_q_heads, num_hgroups, num_subpages, scale_log2.
