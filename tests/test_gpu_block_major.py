@@ -41,6 +41,9 @@ CASES = [
     # each block's rows and balance the grid by entries: blocks go to
     # workgroups by grid stride
     ([60000] + [2000 + 600 * i for i in range(39)], [2100] + [1] * 39, 16, 16, syn.KV_BF16, syn.SCALE_NONE),
+    # a prefill request of 1094 blocks: the top-k's keys past the 1024 held in
+    # registers, and 35 selection words per row
+    ([140000, 3000, 500], [2100, 1, 1], 16, 16, syn.KV_BF16, syn.SCALE_NONE),
 ]
 
 

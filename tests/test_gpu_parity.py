@@ -179,6 +179,15 @@ def _topk_batch():
     return syn.make_batch("topk", 80, L, ql, topk=1, num_q_heads=16, max_seq_len=131072, data=False)
 
 
+@functools.lru_cache(maxsize=1)
+def _topk_batch_long():
+    # rows of more than 1024 blocks: the keys past the 1024 a wave holds in
+    # registers are read again from memory, chunk by chunk
+    L = [140000, 131073, 5000, 1]
+    ql = [1, 2, 1, 1]
+    return syn.make_batch("topk_long", 85, L, ql, topk=1, num_q_heads=16, max_seq_len=140032, data=False)
+
+
 @pytest.mark.parametrize("mode", ["normal", "ties", "zeros", "equal", "few_distinct"])
 @pytest.mark.parametrize("topk", [1, 3, 16, 64, 1500])
 def test_topk_bitexact(gpu_lib, mode, topk):
@@ -186,6 +195,18 @@ def test_topk_bitexact(gpu_lib, mode, topk):
     d = H.upload(b)
     H.run_metadata(d)
     s = _crafted_scores(b, mode, 81 + topk)
+    table, ctx, sel = H.run_topk(d, s)
+    check_selection(b, s, table, ctx, sel, range(b.num_rows))
+
+
+@pytest.mark.parametrize("mode", ["normal", "ties", "few_distinct"])
+@pytest.mark.parametrize("topk", [1, 64, 1500])
+def test_topk_bitexact_long_rows(gpu_lib, mode, topk):
+    b = dataclasses.replace(_topk_batch_long(), topk=topk)
+    assert b.ld_s > 1024
+    d = H.upload(b)
+    H.run_metadata(d)
+    s = _crafted_scores(b, mode, 86 + topk)
     table, ctx, sel = H.run_topk(d, s)
     check_selection(b, s, table, ctx, sel, range(b.num_rows))
 
