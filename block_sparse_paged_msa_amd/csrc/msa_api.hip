@@ -413,8 +413,9 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
     const int nbmax = blocks_bound(batch);
     const BmLayout bw = bm_layout(batch->num_rows, nbmax, num_q_heads, topk, block_scores ? 0 : ld_s);
     if (workspace && workspace_bytes >= bw.total) {
-      // 1) metadata + index scores, 2) top-k + table + ctx + selection
-      // words, 3) block-major attention, 4) merge of the block partials
+      // 1) metadata + index scores (unit and tile kernels), 2) top-k + table
+      // + ctx + selection words, 3) rows per block (at most 16384 items),
+      // 4) block-major attention, 5) merge of the block partials
       char* wsb = static_cast<char*>(workspace);
       float* scores = block_scores ? block_scores : reinterpret_cast<float*>(wsb + bw.scores);
       uint64_t* words = reinterpret_cast<uint64_t*>(wsb + bw.words);

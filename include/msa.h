@@ -203,8 +203,10 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  * synchronisation: metadata, index score + pooling, top-k + page-16 table +
  * context lengths, sparse paged attention and the split merge (#54682 page,
  * 实现拆解 items 2-3: the indexer's selection and sparse table feed attention
- * in the same step). Three launches; no state is carried between calls, so the
- * step can be captured in a HIP graph and replayed. Also writes the batch
+ * in the same step). Three launches: index scores, the selection fused into
+ * attention, the split merge (a second scoring launch for batches of more
+ * than 64 rows; no merge when every row fits one split). No state is carried
+ * between calls, so the step can be captured in a HIP graph and replayed. Also writes the batch
  * metadata arrays (as msa_build_metadata does).
  *   sparse_table [N][8*topk], ctx_lens [N]: written (outputs of the top-k step).
  *   sel_blocks [N][topk]: optional (NULL skips it).
@@ -220,7 +222,8 @@ msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num
  *   that chose each block are counted (one more launch) and the attention
  *   grid is balanced by (row, block) pairs rather than blocks; the
  *   workgroups attend the rows that chose a block from one copy of the
- *   block's K/V, and the per-block partials are merged (4 or 5 launches). Each partial
+ *   block's K/V, and the per-block partials are merged (5 or 6 launches:
+ *   two scoring launches, top-k, the optional count, attention, merge). Each partial
  *   keeps its max and sum in fp32 and its 16x128 accumulator in fp16, scaled by a power of two so that its
  *   largest magnitude is below 1: from the accumulator itself, or, for bf16
  *   K/V with no scales, from the bound 128 * max|V| of the block (the error
