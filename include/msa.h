@@ -12,7 +12,9 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked (host). The caller owns every
  *     buffer, including the workspace; the library allocates nothing and keeps
- *     no state except a per-device cached compute-unit count.
+ *     no state except a per-device cached compute-unit count and, for
+ *     msa_sparse_decode_static, its fixed per-device workspace array and that
+ *     array's address on each device.
  *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the null
  *     stream) and return. They never copy between host and device and never
  *     synchronise, so they can be captured into a HIP graph.
