@@ -145,21 +145,18 @@ __device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int t, int 
 // Sixteen tokens that fill one sub-page in order (a prefill chunk): the
 // workgroup quantises them, lays the K / index-K tiles and the dim-major V
 // sub-page out in LDS, and writes each as one contiguous run. Thread i takes
-// token i/16 and dims 8*(i%16).. of it, so the 16 lanes of a DPP row hold one
+// token i/16 and dims 8*(i%16).. of it (kw, vw, iw: its K, V and index-K
+// pieces, loaded by the caller), so the 16 lanes of a DPP row hold one
 // token's whole row for the scale.
-__device__ __forceinline__ void insert_subpage(const MsaInsertArgs& a, int t0, int slot0, uint8_t* lds) {
+__device__ __forceinline__ void insert_subpage(const MsaInsertArgs& a, int slot0, uint8_t* lds, u32x4 kw, u32x4 vw,
+                                               u32x4 iw) {
   const int tid = threadIdx.x, j = tid >> 4, c = tid & 15;
-  const int t = t0 + j;
   const int page = slot0 >> 7, sub = kSubsPerPage * page + ((slot0 & (kPage - 1)) >> 4);
   const int nbytes = a.kv_fp8 ? 1 : 2;
   const int kv_bytes = kSub * kDim * nbytes;  // one plane of one sub-page
   uint8_t* ks = lds;                 // K tile
   uint8_t* vs = lds + kv_bytes;      // V sub-page
   uint16_t* is = reinterpret_cast<uint16_t*>(lds + 2 * kv_bytes);  // index-K tile
-  const u32x4 kw = *reinterpret_cast<const u32x4*>(a.k_new + static_cast<size_t>(t) * kDim + 8 * c);
-  const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v_new + static_cast<size_t>(t) * kDim + 8 * c);
-  u32x4 iw = {0u, 0u, 0u, 0u};
-  if (a.index_k_new) iw = *reinterpret_cast<const u32x4*>(a.index_k_new + static_cast<size_t>(t) * kDim + 8 * c);
 #pragma unroll
   for (int plane = 0; plane < 2; ++plane) {
     const f32x8 x = widen(plane == 0 ? kw : vw);
@@ -217,13 +214,22 @@ __global__ __launch_bounds__(kInsertThreads) void msa_insert_kernel(MsaInsertArg
   const int t0 = blockIdx.x * kSub;
   const int lt = threadIdx.x & 15;
   const int sl = t0 + lt < a.num_tokens ? a.slot_mapping[t0 + lt] : -1;
+  // the sub-page path's pieces are requested with the slots, before the
+  // path is known (one round trip instead of two); one KV head, so token t's
+  // rows start at t * 128, and the token index is clamped to the last token
+  const int tp = min(t0 + static_cast<int>(threadIdx.x >> 4), a.num_tokens - 1);
+  const size_t po = static_cast<size_t>(tp) * kDim + 8 * lt;
+  const u32x4 kw = *reinterpret_cast<const u32x4*>(a.k_new + po);
+  const u32x4 vw = *reinterpret_cast<const u32x4*>(a.v_new + po);
+  u32x4 iw = {0u, 0u, 0u, 0u};
+  if (a.index_k_new) iw = *reinterpret_cast<const u32x4*>(a.index_k_new + po);
   const int slot0 = __shfl(sl, 0, 16);
   const bool whole = t0 + kSub <= a.num_tokens && slot0 >= 0 && (slot0 & (kSub - 1)) == 0 &&
                      slot0 + kSub <= kPage * a.num_pages && a.num_kv_heads == 1;
   // every lane compares its token's slot (all four waves see the same 16)
   const bool in_order = __all(sl == slot0 + lt);
   if (__builtin_amdgcn_readfirstlane(whole && in_order)) {
-    insert_subpage(a, t0, slot0, lds);
+    insert_subpage(a, slot0, lds, kw, vw, iw);
     return;
   }
   const int wave = threadIdx.x >> 6;
