@@ -177,16 +177,18 @@ def cpu_baseline_parallel(b, rows, budget_s=10.0):
                       f"task on {cores} single-thread worker processes, full step per row, {dt:.1f} s, {cpu_model()}"}
 
 
-def time_insert(msa, torch, tokens=8192, copies=32, reps=32):
+def time_insert(msa, torch, tokens=8192, copies=32, reps=32, decode=False):
     """msa_cache_insert of a prefill chunk (two sequences of 4096 new tokens, the
     mixed workload's prefill shape) into fp8 e4m3fn caches with per-token-head
     scales, index-K included: per-launch time over back-to-back launches in one
     graph, cycling `copies` sets of inputs and caches (>= 256 MB in all, so no
     launch finds its data in the Infinity Cache). Algorithmic bytes per token:
     K, V and index-K rows read (3 x 256 B) + the slot (4 B); fp8 K and V (2 x 128
-    B), their scales (2 x 4 B) and the index-K row (256 B) written."""
+    B), their scales (2 x 4 B) and the index-K row (256 B) written. With
+    decode=True: one new token per request at a random slot of its own page
+    (a decode step's insert), the same caches."""
     dev = "cuda"
-    pages = tokens // 128
+    pages = max(tokens // 128, 64)
     g = torch.Generator(device="cpu").manual_seed(11)
     sets = []
     for c in range(copies):
@@ -195,7 +197,10 @@ def time_insert(msa, torch, tokens=8192, copies=32, reps=32):
         i_new = torch.randn((tokens, 128), generator=g).to(torch.bfloat16).to(dev)
         perm = torch.randperm(pages, generator=g)
         t = torch.arange(tokens)
-        slots = (perm[t // 128] * 128 + t % 128).to(torch.int32).to(dev)
+        if decode:
+            slots = (perm[:tokens] * 128 + torch.randint(0, 128, (tokens,), generator=g)).to(torch.int32).to(dev)
+        else:
+            slots = (perm[t // 128] * 128 + t % 128).to(torch.int32).to(dev)
         kc = torch.zeros((pages * 8, 1, 2048), dtype=torch.uint8, device=dev)
         vc = torch.zeros((pages * 8, 1, 2048), dtype=torch.uint8, device=dev)
         ks = torch.ones((pages * 8, 16, 1), dtype=torch.float32, device=dev)
@@ -563,6 +568,9 @@ def main():
     if "score_mfma" in fig:
         res["score_mfma"] = fig["score_mfma"]
     res["cache_insert"] = time_insert(msa, torch)
+    dec = time_insert(msa, torch, tokens=11, decode=True)
+    res["cache_insert"]["decode_step"] = {"tokens": 11, "slots": "one per request, scattered",
+                                          "us_per_launch": dec["us_per_launch"]}
 
     # the same step through msa_sparse_decode_ex: LSE written, per-head sinks
     # applied; both variants timed here the same way (one graph of `copies`

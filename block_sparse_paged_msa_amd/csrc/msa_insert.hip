@@ -3,12 +3,11 @@
 // separate K and V planes and, unless the layer reuses another layer's index,
 // the index cache; FP8 caches carry per-token-head or scalar K/V scales).
 //
-// One wave per new token. Lanes 0..15 take the K row and lanes 16..31 the
-// index-K row, eight dims each (one 16-byte load per lane), and write them
-// into their shuffled tiles as one contiguous 8-element run per lane. V is
-// dim-major ([128 dims][16 token slots] per sub-page), so all 64 lanes take
-// it, two dims each, and every store instruction fills one token slot of 64
-// dim rows.
+// Sixteen lanes per new token, eight dims each of its K, V and index-K rows
+// (one 16-byte load per row and lane, issued with the slot loads), so the
+// lanes of one DPP row hold a token's whole row for its scale. K and index-K
+// pieces go into their shuffled tiles as one contiguous 8-element run per
+// lane; V is dim-major ([128 dims][16 token slots] per sub-page).
 //
 // Quantisation (each code decided in fp32): per-token-head scale
 // s = max|x| / 448 over the token-head's 128 values (1 for an all-zero row),
@@ -66,79 +65,63 @@ __device__ __forceinline__ u32x2 fp8_row_codes(const f32x8& x, float& s) {
   return u32x2{code[0], code[1]};
 }
 
-// One token with one wave (decode: scattered slots).
-__device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int t, int lane) {
-  const int c = lane & 15;
-  // every load of the token is issued before its slot is known (one round
-  // trip): lanes 0..15 the K row, lanes 16..31 the index-K row (8 dims
-  // each), all lanes two dims of the V row; one KV head (the caller checks)
-  const size_t row = static_cast<size_t>(t) * a.num_kv_heads;
-  u32x4 kw = {0u, 0u, 0u, 0u}, iw = {0u, 0u, 0u, 0u};
-  if (lane < 16) kw = *reinterpret_cast<const u32x4*>(a.k_new + row * kDim + 8 * c);
-  if ((lane >> 4) == 1 && a.index_k_new) iw = *reinterpret_cast<const u32x4*>(a.index_k_new + static_cast<size_t>(t) * kDim + 8 * c);
-  const uint16_t* vsrc = a.v_new + row * kDim;
-  const uint32_t vb0 = vsrc[lane], vb1 = vsrc[lane + 64];
-  const int slot = a.slot_mapping[t];
-  if (slot < 0 || slot >= kPage * a.num_pages) return;  // skipped (or outside the caches)
+// One token whose workgroup's sixteen do not fill one sub-page in order
+// (decode: scattered slots), written by the 16 lanes that hold its pieces (8
+// dims each of its K, V and index-K rows, loaded with the slots): the K and
+// index-K pieces as contiguous runs of their tiles, the V piece as 8 dim rows
+// of the dim-major sub-page. The reductions run in every lane; a skipped slot
+// only writes nothing.
+__device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int slot, u32x4 kw, u32x4 vw, u32x4 iw) {
+  const int c = threadIdx.x & 15;
+  const bool valid = slot >= 0 && slot < kPage * a.num_pages;  // else skipped (or outside the caches)
   const int page = slot >> 7, off = slot & (kPage - 1);
   const int sub = kSubsPerPage * page + (off >> 4), j = off & (kSub - 1);
-  const size_t sp = static_cast<size_t>(sub) * a.num_kv_heads;  // the head's sub-page
-
-  // index-K: a bf16 copy into the page's shuffled tile, or fp8 codes and
-  // the token's scale (lanes 16..31 form one DPP row: the whole index row)
+  const size_t tile = static_cast<size_t>(sub) * (kSub * kDim);  // the sub-page (one KV head)
   if (a.index_k_new) {
     const size_t at = static_cast<size_t>(page) * (kPage * kDim) + (off >> 4) * (kSub * kDim) + (c * 16 + j) * 8;
     if (a.index_scale_out) {
       float s;
       const u32x2 codes = fp8_row_codes(widen(iw), s);
-      if ((lane >> 4) == 1) {
+      if (valid) {
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.index_k) + at) = codes;
         if (c == 0) a.index_scale_out[static_cast<size_t>(page) * kPage + off] = s;
       }
-    } else if ((lane >> 4) == 1) {
+    } else if (valid) {
       *reinterpret_cast<u32x4*>(a.index_k + at) = iw;
     }
   }
-  // K (lanes 0..15, dims 8c..8c+7): one contiguous run of the shuffled tile
-  {
-    const f32x8 x = widen(kw);
+#pragma unroll
+  for (int plane = 0; plane < 2; ++plane) {
+    const f32x8 x = widen(plane == 0 ? kw : vw);
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x.v[i]));
-    const float s = row_scale(a, 0, max16(amax));  // lanes 0..15 hold the whole row
-    if (lane < 16) {
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x.v[e]));
+    const float s = row_scale(a, plane, max16(amax));  // the 16 lanes hold the whole row
+    if (!valid) continue;
+    if (a.scale_mode == 2 && c == 0) (plane == 0 ? a.k_scale_out : a.v_scale_out)[static_cast<size_t>(sub) * kSub + j] = s;
+    if (plane == 0) {  // dims 8c..8c+7 of token j: one run of the shuffled tile
       if (a.kv_fp8) {
         uint32_t code[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) code[e >> 2] |= fp8_code(x.v[e], s) << (8 * (e & 3));
-        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.k_cache) + sp * (kSub * kDim) + (c * 16 + j) * 8) =
-            u32x2{code[0], code[1]};
+        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(a.k_cache) + tile + (c * 16 + j) * 8) = u32x2{code[0], code[1]};
       } else {
         u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           w[i] = f32_to_bf16(x.v[2 * i] / s) | (static_cast<uint32_t>(f32_to_bf16(x.v[2 * i + 1] / s)) << 16);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k_cache) + sp * (kSub * kDim) + (c * 16 + j) * 8) = w;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.k_cache) + tile + (c * 16 + j) * 8) = w;
+      }
+    } else {  // dim rows 8c..8c+7 of the dim-major sub-page, slot j of each
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const size_t at = tile + static_cast<size_t>(8 * c + e) * kSub + j;
+        if (a.kv_fp8)
+          static_cast<uint8_t*>(a.v_cache)[at] = static_cast<uint8_t>(fp8_code(x.v[e], s));
+        else
+          static_cast<uint16_t*>(a.v_cache)[at] = f32_to_bf16(x.v[e] / s);
       }
     }
-    if (a.scale_mode == 2 && lane == 0) a.k_scale_out[(static_cast<size_t>(sub) * kSub + j) * a.num_kv_heads] = s;
-  }
-  // V (all lanes, dims lane and lane+64): the cache is dim-major, so each
-  // store instruction writes one token slot of 64 dim rows
-  {
-    const float x0 = __uint_as_float(vb0 << 16), x1 = __uint_as_float(vb1 << 16);
-    const float s = row_scale(a, 1, max_across_rows(max16(fmaxf(fabsf(x0), fabsf(x1)))));
-    const size_t base = sp * (kSub * kDim) + j;
-    if (a.kv_fp8) {
-      uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
-      vc[base + lane * kSub] = static_cast<uint8_t>(fp8_code(x0, s));
-      vc[base + (lane + 64) * kSub] = static_cast<uint8_t>(fp8_code(x1, s));
-    } else {
-      uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
-      vc[base + lane * kSub] = f32_to_bf16(x0 / s);
-      vc[base + (lane + 64) * kSub] = f32_to_bf16(x1 / s);
-    }
-    if (a.scale_mode == 2 && lane == 0) a.v_scale_out[(static_cast<size_t>(sub) * kSub + j) * a.num_kv_heads] = s;
   }
 }
 
@@ -205,12 +188,12 @@ __device__ __forceinline__ void insert_subpage(const MsaInsertArgs& a, int slot0
   }
 }
 
-// Workgroup = 16 consecutive tokens. When their slots are one whole sub-page
-// in order (a prefill chunk), the sub-page path writes it in contiguous runs;
-// otherwise each wave inserts four of the tokens one by one.
+// Workgroup = 16 consecutive tokens, thread i holding 8 dims of token i/16's
+// K, V and index-K rows. When their slots are one whole sub-page in order (a
+// prefill chunk), the sub-page path writes it in contiguous runs; otherwise
+// every token is written at its own slot by the 16 lanes that hold it.
 __global__ __launch_bounds__(kInsertThreads) void msa_insert_kernel(MsaInsertArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kSub * kDim * 2];
-  const int lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kSub;
   const int lt = threadIdx.x & 15;
   const int sl = t0 + lt < a.num_tokens ? a.slot_mapping[t0 + lt] : -1;
@@ -232,11 +215,9 @@ __global__ __launch_bounds__(kInsertThreads) void msa_insert_kernel(MsaInsertArg
     insert_subpage(a, slot0, lds, kw, vw, iw);
     return;
   }
-  const int wave = threadIdx.x >> 6;
-  for (int k = 0; k < 4; ++k) {
-    const int t = t0 + 4 * wave + k;
-    if (t < a.num_tokens) insert_token(a, t, lane);
-  }
+  // lane group g of wave w: token t0 + 4w + g, whose slot lane 4w + g holds
+  // (past the last token the slot is -1)
+  insert_token(a, __shfl(sl, static_cast<int>(threadIdx.x >> 4) & 15), kw, vw, iw);
 }
 
 }  // namespace
