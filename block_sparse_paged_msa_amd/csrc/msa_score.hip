@@ -325,8 +325,17 @@ __global__ __launch_bounds__(kScoreThreads) void msa_score_kernel(MsaScoreArgs a
   }
   __syncthreads();
 
-  if (writer) {  // per-row request id and absolute position
-    for (int n = tid; n < a.num_rows; n += kScoreThreads) {
+  // per-row request id and absolute position: in a launch of more than 64
+  // rows every workgroup holds the prefix, so each writes its share of the
+  // rows (one workgroup alone would hold the launch open for ~8 us on a
+  // step of 8198 rows); otherwise the metadata writer takes them all
+  const bool spread = a.write_meta && a.num_rows > kRowsPerUnit;
+  if (writer || spread) {
+    const int per = spread ? (a.num_rows + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x)
+                           : a.num_rows;
+    const int n_lo = spread ? static_cast<int>(blockIdx.x) * per : 0;
+    const int n_hi = min(n_lo + per, a.num_rows);
+    for (int n = n_lo + tid; n < n_hi; n += kScoreThreads) {
       int lo = 0, hi = R;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
