@@ -1,8 +1,10 @@
 """msa_sparse_decode_static — the fused step with its workspace in the
 library's fixed device array (for callers that cannot allocate) — against
-msa_sparse_decode_ex given a caller workspace of the same size: on two calls
-in a row, the second with a smaller batch, then the first batch again (the
-array keeps the previous call's bytes), every output is bitwise equal.
+msa_sparse_decode_ex given a caller workspace of the same size: on calls in a
+row, the second with a smaller batch, then a prefill-sized batch whose
+block-major workspace fits the array (so both take the block-major path),
+then the first batch again (the array keeps the previous call's bytes), every
+output is bitwise equal.
 """
 import numpy as np
 import pytest
@@ -36,12 +38,18 @@ def _decode(d, static, with_scores):
 def test_static_scratch_decode_matches_caller_workspace(gpu_lib):
     big = syn.config("fp8_kv", scale_mode=syn.SCALE_PER_TOKEN_HEAD)
     small = syn.make_batch("static2", 901, [9000, 700, 129], [1, 2, 1], topk=16, num_q_heads=16)
-    db, ds = H.upload(big), H.upload(small)
+    prefill = syn.make_batch("static3", 902, [6000, 5000, 300], [2100, 1, 1], topk=2, num_q_heads=16)
+    db, ds, dp = H.upload(big), H.upload(small), H.upload(prefill)
     need_big = msa.msa_workspace_bytes(big.num_rows, 16, 128 * big.topk, big.ld_s)
     assert 0 < need_big <= msa.MSA_STATIC_SCRATCH_BYTES
-    print(f"[static] rows {big.num_rows} then {small.num_rows}; scratch need {need_big} B", flush=True)
+    need_bm = msa.msa_decode_workspace_bytes(prefill.num_rows, prefill.max_seq_len, 16, prefill.topk, prefill.ld_s)
+    need_rows = msa.msa_workspace_bytes(prefill.num_rows, 16, 128 * prefill.topk, prefill.ld_s)
+    assert need_rows < need_bm <= msa.MSA_STATIC_SCRATCH_BYTES  # the block-major path is taken
+    print(f"[static] rows {big.num_rows}, {small.num_rows}, {prefill.num_rows} (block-major); "
+          f"scratch need {need_big} / {need_bm} B", flush=True)
     # scores in the scratch (no caller score buffer), then a caller score buffer
-    for name, d, with_scores in (("big", db, False), ("small", ds, True), ("big again", db, False)):
+    for name, d, with_scores in (("big", db, False), ("small", ds, True), ("block-major", dp, False),
+                                 ("big again", db, False)):
         got = _decode(d, True, with_scores)
         want = _decode(d, False, with_scores)
         for i, (g, w) in enumerate(zip(got, want)):
