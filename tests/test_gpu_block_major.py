@@ -95,6 +95,39 @@ def test_block_major_step(gpu_lib, case, with_extras):
     assert d_out <= ATOL[kv], f"block-major vs per-row max abs diff {d_out}"
 
 
+@pytest.mark.parametrize("sm_scale", [4.0, 1e-3])
+def test_block_major_extreme_softmax_scale(gpu_lib, sm_scale):
+    """Sharp and flat softmax through the block-major path with bf16 K/V and
+    no scales (block partials scaled from the block's 128 max|V| bound): the
+    same bars as the per-row path, and the per-row path agrees."""
+    L, ql, topk, hq = [9000, 3000], [1800, 400], 16, 16
+    b = syn.make_batch("bm_smscale", 880, L, ql, topk=topk, num_q_heads=hq, kv_dtype=syn.KV_BF16,
+                       scale_mode=syn.SCALE_NONE)
+    b = dataclasses.replace(b, sm_scale=sm_scale)
+    print(f"[block-major] sm_scale={sm_scale} rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0)
+    o.ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    o.wsb = wsb
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    table, ctx = o.table.cpu().numpy(), o.ctx.cpu().numpy()
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    rows = sorted(set(_sample_rows(b, 16, 885)))
+    ref_out, amean = bars.oracle_and_abs_mean(b, table, ctx, rows)
+    err = np.abs(out[rows] - ref_out).max()
+    assert err <= ATOL[syn.KV_BF16], f"attention max abs err {err}"
+    ex = bars.detect_excess(out[rows], ref_out, amean)
+    assert ex <= 0, f"attention outside the detector bar by {ex} (max abs err {err})"
+    o2 = H.alloc_decode(d)
+    H.run_decode(d, o2)
+    assert torch.equal(o2.table, o.table)
+    d_out = np.abs(H.bf16_to_np(o2.out) - out).max()
+    assert d_out <= ATOL[syn.KV_BF16], f"block-major vs per-row max abs diff {d_out}"
+
+
 @pytest.mark.parametrize("vexp", [40, -60])
 def test_block_major_extreme_values(gpu_lib, vexp):
     """V scaled by 2^vexp (exact in bf16): the fp16 block partials are scaled

@@ -317,6 +317,27 @@ def test_fused_decode_shapes(gpu_lib, case):
     check_attention(b, H.bf16_to_np(o.out), table, ctx, rows)
 
 
+@pytest.mark.parametrize("sm_scale", [4.0, 1e-3])
+def test_fused_decode_extreme_softmax_scale(gpu_lib, sm_scale):
+    """A sharp softmax (sm_scale 4: logits of standard deviation ~45, nearly
+    one token per head) and a flat one (sm_scale 1e-3: nearly equal weights)
+    through the per-row path with many splits a row: the running max and the
+    merge's rescaling keep both bars."""
+    b = syn.make_batch("smscale", 870, [70000, 9000, 300], [1, 2, 1], topk=64, num_q_heads=16,
+                       kv_dtype=syn.KV_FP8, scale_mode=syn.SCALE_PER_TOKEN_HEAD)
+    b = dataclasses.replace(b, sm_scale=sm_scale)
+    print(f"[fused] sm_scale={sm_scale} rows={b.num_rows}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    rows = list(range(b.num_rows))
+    check_selection(b, o.scores.cpu().numpy(), table, ctx, sel, rows)
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    check_attention(b, out, table, ctx, rows)
+
+
 TIE_SHAPES = [
     # (longest row, lengths): rows past 1024 blocks select wave by wave with
     # the last keys re-read from memory; rows of at most 1024 or 256 blocks
