@@ -26,6 +26,7 @@ MSA_SCALE_NONE = 0
 MSA_SCALE_SCALAR = 1
 MSA_SCALE_PER_TOKEN_HEAD = 2
 MSA_STATIC_SCRATCH_BYTES = 32 << 20   # workspace inside the library used by msa_sparse_decode_static
+MSA_MAX_PAGES = 1 << 24               # physical pages a batch or cache may name
 
 EXPORTS = (
     "msa_build_metadata", "msa_index_score", "msa_topk_block_table", "msa_sparse_paged_attn",

@@ -163,7 +163,7 @@ msa_status check_batch(const msa_batch* b, bool need_meta_outputs) {
   if (need_meta_outputs && (!b->cu_seqlens_q || !b->cu_seqlens_k || !b->cu_blocks || !b->cu_units))
     return MSA_ERR_INVALID_ARG;
   if (need_meta_outputs && b->num_rows > 0 && (!b->row_req || !b->row_pos)) return MSA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(b->num_pages) * msa::kSubsPerPage * kSub * kDim > (1LL << 40)) return MSA_ERR_UNSUPPORTED;
+  if (b->num_pages > MSA_MAX_PAGES) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
 
@@ -174,6 +174,7 @@ msa_status check_kv(const msa_kv* kv) {
   if (kv->kv_dtype != MSA_KV_BF16 && kv->kv_dtype != MSA_KV_FP8_E4M3FN) return MSA_ERR_INVALID_ARG;
   if (kv->scale_mode < MSA_SCALE_NONE || kv->scale_mode > MSA_SCALE_PER_TOKEN_HEAD) return MSA_ERR_INVALID_ARG;
   if (kv->num_pages < 1) return MSA_ERR_INVALID_ARG;
+  if (kv->num_pages > MSA_MAX_PAGES) return MSA_ERR_UNSUPPORTED;
   if (kv->num_kv_heads != 1) return MSA_ERR_UNSUPPORTED;
   if (kv->kv_dtype == MSA_KV_FP8_E4M3FN && kv->scale_mode == MSA_SCALE_NONE) return MSA_ERR_UNSUPPORTED;
   if (kv->scale_mode != MSA_SCALE_NONE && (!kv->k_scale || !kv->v_scale)) return MSA_ERR_INVALID_ARG;

@@ -82,6 +82,7 @@ enum {
   MSA_MAX_Q_HEADS = 128,    /* query heads sharing the one KV head */
   MSA_MAX_TOPK = 8192,      /* selected blocks per row */
   MSA_MAX_SEQ_LEN = 1048576, /* tokens per request (8192 blocks) */
+  MSA_MAX_PAGES = 16777216,  /* physical pages P (int32 slots 128*page + offset; 8*P sub-page ids) */
   MSA_SCORE_ROWS_PER_UNIT = 64, /* query rows of one request scored per work unit */
   MSA_STATIC_SCRATCH_BYTES = 33554432 /* workspace of msa_sparse_decode_static: 32 MiB per device */
 };
@@ -107,7 +108,7 @@ typedef struct msa_batch {
   int32_t num_rows;           /* host, exact: sum of query_lens */
   int32_t ld_bt;              /* host: row stride of block_table (>= blocks of any request) */
   int32_t max_seq_len;        /* host: upper bound of every seq_len (sizes grids) */
-  int32_t num_pages;          /* host: P, physical pages in index_k / k_cache / v_cache */
+  int32_t num_pages;          /* host: P <= MSA_MAX_PAGES, physical pages in index_k / k_cache / v_cache */
 } msa_batch;
 
 /* K/V cache description (host struct with device pointers). Slots of a
@@ -122,7 +123,7 @@ typedef struct msa_kv {
   int32_t kv_dtype;      /* msa_kv_dtype */
   int32_t scale_mode;    /* msa_scale_mode; MSA_SCALE_NONE requires bf16 */
   int32_t num_kv_heads;  /* must be 1 */
-  int32_t num_pages;     /* P: the caches hold 8P sub-pages */
+  int32_t num_pages;     /* P <= MSA_MAX_PAGES: the caches hold 8P sub-pages */
 } msa_kv;
 
 /*
@@ -132,8 +133,9 @@ typedef struct msa_kv {
  * get a request id and an absolute position).
  * Writes cu_seqlens_q, cu_seqlens_k, cu_blocks, cu_units, row_req, row_pos.
  * Errors: INVALID_ARG for null pointers or num_reqs/num_rows < 0;
- * UNSUPPORTED for num_reqs > MSA_MAX_REQS or max_seq_len > MSA_MAX_SEQ_LEN
- * (every call taking a batch checks the same).
+ * UNSUPPORTED for num_reqs > MSA_MAX_REQS, max_seq_len > MSA_MAX_SEQ_LEN or
+ * num_pages > MSA_MAX_PAGES (every call taking a batch checks the same; every
+ * call taking an msa_kv rejects num_pages > MSA_MAX_PAGES likewise).
  */
 msa_status msa_build_metadata(msa_stream_t stream, const msa_batch* batch);
 

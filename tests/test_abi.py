@@ -132,6 +132,7 @@ def _code(fn, *args):
     (dict(cu_units=0), msa.MSA_ERR_INVALID_ARG),
     (dict(ld_bt=0), msa.MSA_ERR_INVALID_ARG),
     (dict(num_reqs=0, num_rows=3), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_pages=(1 << 24) + 1), msa.MSA_ERR_UNSUPPORTED),
 ])
 def test_metadata_rejects(batch, expect):
     assert _code(msa.msa_build_metadata, _fake_batch(**batch), 0) == expect
@@ -156,6 +157,7 @@ def test_topk_rejects():
     (dict(kv_dtype=1, scale_mode=2, k_scale=0x10, v_scale=0), msa.MSA_ERR_INVALID_ARG),
     (dict(kv_dtype=5), msa.MSA_ERR_INVALID_ARG),
     (dict(k_cache=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_pages=(1 << 24) + 1), msa.MSA_ERR_UNSUPPORTED),
 ])
 def test_attention_rejects_kv(kv, expect):
     assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, _fake_kv(**kv), 0x2, 8, 0x3, 128, 0.1,
@@ -265,3 +267,10 @@ def test_insert_rejects(args, kv, expect):
     a.update(args)
     assert _code(msa.msa_cache_insert, a["num_tokens"], a["slot_mapping"], a["k_new"], a["v_new"],
                  _fake_kv(**kv), a["index_k_new"], a["index_k"], 0) == expect
+
+
+def test_insert_rejects_more_pages_than_slots_name():
+    # slots are int32 128*page + offset: caches past 2^24 pages are refused
+    kv = _fake_kv(num_pages=(1 << 24) + 1)
+    assert _code(msa.msa_cache_insert, 4, 0x1, 0x2, 0x3, kv, None, None, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert msa.MSA_MAX_PAGES == 1 << 24
