@@ -409,6 +409,38 @@ def test_fused_prefill_batches(gpu_lib, case):
     check_attention(b, out, table, ctx, rows)
 
 
+def test_two_streams_at_once_match_one_at_a_time(gpu_lib):
+    """Two fused steps enqueued on two streams with nothing ordering them
+    (each with its own workspace and outputs; the per-row path and the
+    block-major path side by side) give the bits each gives alone: no call
+    depends on device state another call writes."""
+    cases = [(syn.config("spec_decode"), False),
+             (syn.make_batch("streams_bm", 890, [6000, 3000], [2100, 1], topk=8, num_q_heads=16), True)]
+    devs, refs, outs = [], [], []
+    for b, bm in cases:
+        d = H.upload(b)
+        devs.append(d)
+        for dst in (refs, outs):
+            o = H.alloc_decode(d)
+            if bm:
+                wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, b.num_q_heads, b.topk, 0)
+                o.ws, o.wsb = torch.empty((wsb,), dtype=torch.uint8, device="cuda"), wsb
+            dst.append(o)
+    for d, o in zip(devs, refs):
+        H.run_decode(d, o)
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print("[streams] two steps on two streams, three rounds", flush=True)
+    for _ in range(3):
+        for d, o, st in zip(devs, outs, streams):
+            with torch.cuda.stream(st):
+                H.run_decode(d, o)
+    torch.cuda.synchronize()
+    for o, r in zip(outs, refs):
+        for field in ("out", "table", "ctx", "sel", "scores"):
+            assert torch.equal(getattr(o, field), getattr(r, field)), field
+
+
 def test_fused_decode_repeat_and_graph_replay_bitwise(gpu_lib):
     b = syn.make_batch("graph", 120, [20000, 3000, 7000], [4, 1, 2], topk=16, num_q_heads=16)
     d = H.upload(b)
