@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the other workloads' reduced lines")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the bench line: the fused step on 16 fp8 K/V decode requests of 2K..64K "
+                        "tokens each, one JSON line per length")
     p.add_argument("--counters", action="store_true",
                    help="counter pass: 8 plain copies of 256 MiB, then 8 index-score launches, no timing")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -401,6 +404,14 @@ def measure_extra(name, idx_fp8, steps, msa, torch, syn):
     """A reduced line for another workload: step time (graph replay over
     cache-clean copies), the score kernel alone, and both rooflines."""
     b = syn.config(name, index_dtype=syn.INDEX_FP8 if idx_fp8 else syn.INDEX_BF16)
+    f = measure_batch(b, idx_fp8, steps, msa, torch, syn)
+    f["workload"] = WORKLOAD_DESC[name]
+    return f
+
+
+def measure_batch(b, idx_fp8, steps, msa, torch, syn):
+    """Step time (graph replay over cache-clean copies), the score kernel
+    alone and both rooflines of one batch."""
     copies = copies_for(b, idx_fp8)
     st = Setup(b, copies, idx_fp8, msa, torch, syn)
     g = graph_of(torch, [lambda c=c: st.step(c) for c in range(copies)])
@@ -409,11 +420,33 @@ def measure_extra(name, idx_fp8, steps, msa, torch, syn):
     t_score = score_kernel_us(torch, st)
     f = step_figures(b, st, sec, t_score, st.ctx.cpu().numpy(), st.table.cpu().numpy())
     f.pop("nbytes")
-    f.update({"workload": WORKLOAD_DESC[name], "rows": b.num_rows, "cache_copies_cycled": copies,
-              "steps_timed": reps * copies})
+    f.update({"rows": b.num_rows, "cache_copies_cycled": copies, "steps_timed": reps * copies})
     del st, g
     torch.cuda.empty_cache()
     return f
+
+
+SWEEP_LENS = (2048, 4096, 8192, 16384, 32768, 65536)
+
+
+def run_sweep(steps, msa, torch, syn):
+    """--sweep: the fused step on 16 decode requests of one length each (fp8
+    e4m3fn K/V with per-token-head scales, bf16 index, top-k 64, 16 query
+    heads), for lengths of 2K to 64K tokens, one JSON line each: the step's
+    algorithmic bytes grow with the length while the chain after the index
+    scorer stays fixed, so the fraction of peak shows from what size a step is
+    bound by HBM."""
+    for i, L in enumerate(SWEEP_LENS):
+        print(f"[bench] sweep: 16 requests of {L} tokens ...", file=sys.stderr, flush=True)
+        b = syn.make_batch("sweep", 990 + i, [L] * 16, [1] * 16, topk=64, num_q_heads=16, kv_dtype=syn.KV_FP8,
+                           scale_mode=syn.SCALE_PER_TOKEN_HEAD)
+        f = measure_batch(b, False, steps, msa, torch, syn)
+        print(json.dumps({"sweep": "fp8 K/V decode, 16 requests x 1 row, top-k 64, 16 q heads", "seq_len": L,
+                          "us_per_step": f["us_per_step"],
+                          "step_algorithmic_mb": f["step_roofline"]["algorithmic_bytes"] / 1e6,
+                          "step_frac": f["step_roofline"]["frac"], "score_us": f["score_kernel"]["avg_launch_us"],
+                          "score_frac": f["score_kernel"]["frac"], "cache_copies_cycled": f["cache_copies_cycled"]}),
+              flush=True)
 
 
 def main():
@@ -438,6 +471,12 @@ def main():
 
     import block_sparse_paged_msa_amd as msa
     import msa_synth as syn
+
+    if args.sweep:
+        torch.cuda.set_device(0)
+        msa.load()
+        run_sweep(args.steps, msa, torch, syn)
+        return
 
     idx_fp8 = args.index == "fp8"
     b = syn.config(args.workload, index_dtype=syn.INDEX_FP8 if idx_fp8 else syn.INDEX_BF16)
