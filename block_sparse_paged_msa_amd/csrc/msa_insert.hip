@@ -73,7 +73,7 @@ __device__ __forceinline__ u32x2 fp8_row_codes(const f32x8& x, float& s) {
 // only writes nothing.
 __device__ __forceinline__ void insert_token(const MsaInsertArgs& a, int slot, u32x4 kw, u32x4 vw, u32x4 iw) {
   const int c = threadIdx.x & 15;
-  const bool valid = slot >= 0 && slot < kPage * a.num_pages;  // else skipped (or outside the caches)
+  const bool valid = slot >= 0 && (slot >> 7) < a.num_pages;  // else skipped (or outside the caches)
   const int page = slot >> 7, off = slot & (kPage - 1);
   const int sub = kSubsPerPage * page + (off >> 4), j = off & (kSub - 1);
   const size_t tile = static_cast<size_t>(sub) * (kSub * kDim);  // the sub-page (one KV head)
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kInsertThreads) void msa_insert_kernel(MsaInsertArg
   if (a.index_k_new) iw = *reinterpret_cast<const u32x4*>(a.index_k_new + po);
   const int slot0 = __shfl(sl, 0, 16);
   const bool whole = t0 + kSub <= a.num_tokens && slot0 >= 0 && (slot0 & (kSub - 1)) == 0 &&
-                     slot0 + kSub <= kPage * a.num_pages && a.num_kv_heads == 1;
+                     (slot0 >> 7) < a.num_pages && a.num_kv_heads == 1;
   // every lane compares its token's slot (all four waves see the same 16)
   const bool in_order = __all(sl == slot0 + lt);
   if (__builtin_amdgcn_readfirstlane(whole && in_order)) {
