@@ -375,7 +375,7 @@ msa_status msa_sparse_paged_attn_ex(msa_stream_t stream, const void* q, int32_t 
                                     void* out, float* lse, void* workspace, size_t workspace_bytes) {
   if (num_rows < 0 || max_ctx < 0 || ld_table < 0) return MSA_ERR_INVALID_ARG;
   if (num_q_heads < 1) return MSA_ERR_INVALID_ARG;
-  if (num_q_heads > MSA_MAX_Q_HEADS) return MSA_ERR_UNSUPPORTED;
+  if (num_q_heads > MSA_MAX_Q_HEADS || max_ctx > MSA_MAX_SEQ_LEN) return MSA_ERR_UNSUPPORTED;
   msa_status st = check_kv(kv);
   if (st != MSA_OK) return st;
   if (num_rows == 0) return MSA_OK;

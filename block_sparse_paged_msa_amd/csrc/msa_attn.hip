@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int rest = blockIdx.x / a.nsplit;
   const int hgi = rest % a.num_hgroups;
   const int n = rest / a.num_hgroups;
-  const int ctx = clampi(a.ctx_in[n], 0, min(a.max_ctx, kSub * a.ld_table));
+  const int ctx = clampi(a.ctx_in[n], 0, a.max_ctx);  // the host checked max_ctx <= 16 * ld_table
   if (ctx == 0) {
     if (split == 0) write_zero_row(a, n, hgi);
     return;
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(kMergeThreads) void msa_merge_kernel(MsaAttnArgs a,
   };
   fetch(0);
   const float sink2 = a.sinks ? a.sinks[head] * kLog2e : -INFINITY;
-  const int ctx = clampi(ctxp[n], 0, min(a.max_ctx, kSub * a.ld_table));
+  const int ctx = clampi(ctxp[n], 0, a.max_ctx);  // the host checked max_ctx <= 16 * ld_table
   const int nsplit_n = (ctx + a.split_tok - 1) / a.split_tok;
   if (!ALL_ROWS && nsplit_n <= 1) return;
   MergeState st = {-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};

@@ -170,6 +170,9 @@ def test_attention_rejects_heads_table_and_workspace():
         == msa.MSA_ERR_UNSUPPORTED
     assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 7, 0x3, 128, 0.1, 0x4, 0x5, 1 << 20, 0) \
         == msa.MSA_ERR_INVALID_ARG
+    # no row attends more tokens than a request can hold
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 1 << 20, 0x3, (1 << 20) + 1, 0.1, 0x4, 0x5,
+                 1 << 40, 0) == msa.MSA_ERR_UNSUPPORTED
     # 4 rows of 4096 tokens are split over several workgroups: partials need space
     need = msa.msa_workspace_bytes(4, 16, 4096, 0)
     assert need > 0
