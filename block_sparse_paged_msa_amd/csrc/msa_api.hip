@@ -3,6 +3,7 @@
 // unit count), workspace layout and the stream-ordered launches. No call here
 // allocates, copies between host and device, or synchronises.
 #include <atomic>
+#include <climits>
 #include <mutex>
 
 #include "msa.h"
@@ -90,6 +91,16 @@ AttnPlan attn_plan(int num_rows, int num_q_heads, int max_ctx) {
   p.split_tok = static_cast<int>(split);
   p.nsplit = static_cast<int>(ceil_div(ctx, split));
   return p;
+}
+
+// A per-row launch whose attention grid (rows x head groups x token splits)
+// or, when rows are split, merge grid (rows rounded up to 8 x query heads)
+// would not fit 31 bits is refused before anything is enqueued.
+bool attn_grid_fits(int num_rows, int num_q_heads, int max_ctx) {
+  const AttnPlan p = attn_plan(num_rows, num_q_heads, max_ctx);
+  const int64_t attn = static_cast<int64_t>(num_rows) * p.hgroups * p.nsplit;
+  const int64_t merge = p.nsplit > 1 ? (static_cast<int64_t>(num_rows) + 7) / 8 * 8 * num_q_heads : 0;
+  return attn <= INT32_MAX && merge <= INT32_MAX;
 }
 
 struct WsLayout {
@@ -383,6 +394,7 @@ msa_status msa_sparse_paged_attn_ex(msa_stream_t stream, const void* q, int32_t 
   if (static_cast<int64_t>(ld_table) * kSub < max_ctx || ld_table < 1) return MSA_ERR_INVALID_ARG;
   const WsLayout w = ws_layout(num_rows, num_q_heads, max_ctx, 0);
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MSA_ERR_WORKSPACE;
+  if (!attn_grid_fits(num_rows, num_q_heads, max_ctx)) return MSA_ERR_UNSUPPORTED;
   MsaAttnArgs a = attn_args(q, num_rows, num_q_heads, kv, ld_table, max_ctx, sm_scale, out, workspace);
   a.table_in = sparse_table;
   a.ctx_in = ctx_lens;
@@ -462,6 +474,7 @@ msa_status msa_sparse_decode_ex(msa_stream_t stream, const msa_batch* batch, con
   }
   const WsLayout w = ws_layout(batch->num_rows, num_q_heads, max_ctx, block_scores ? 0 : ld_s);
   if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return MSA_ERR_WORKSPACE;
+  if (!attn_grid_fits(batch->num_rows, num_q_heads, max_ctx)) return MSA_ERR_UNSUPPORTED;
   float* scores = block_scores ? block_scores : reinterpret_cast<float*>(static_cast<char*>(workspace) + w.scores);
   // 1) metadata + index scores, 2) per-row selection + attention, 3) split merge
   st = launch_score(s, batch, index_q, index_k, index_k_scale, scores, ld_s, true);

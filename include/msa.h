@@ -194,8 +194,9 @@ msa_status msa_topk_block_table(msa_stream_t stream, const msa_batch* batch,
  *   that size is 0 (every row fits one split).
  * Errors: INVALID_ARG for null required pointers or sizes < 0; UNSUPPORTED for
  * num_kv_heads != 1, num_q_heads > MSA_MAX_Q_HEADS, max_ctx > MSA_MAX_SEQ_LEN,
- * bad dtype/scale pairing (MSA_SCALE_NONE with fp8); WORKSPACE if the
- * workspace is too small.
+ * bad dtype/scale pairing (MSA_SCALE_NONE with fp8), or a launch whose grid
+ * (rows x head groups x token splits, or rows x query heads) would pass 2^31
+ * workgroups; WORKSPACE if the workspace is too small.
  */
 msa_status msa_sparse_paged_attn(msa_stream_t stream, const void* q, int32_t num_rows,
                                  int32_t num_q_heads, const msa_kv* kv,

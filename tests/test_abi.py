@@ -170,6 +170,10 @@ def test_attention_rejects_heads_table_and_workspace():
         == msa.MSA_ERR_UNSUPPORTED
     assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 7, 0x3, 128, 0.1, 0x4, 0x5, 1 << 20, 0) \
         == msa.MSA_ERR_INVALID_ARG
+    # a grid past 2^31 workgroups (2^22 rows x 8 head groups x 128 splits of
+    # 2^20 tokens) is refused, not truncated
+    assert _code(msa.msa_sparse_paged_attn, 0x1, 1 << 22, 128, kv, 0x2, 1 << 16, 0x3, 1 << 20, 0.1, 0x4, 0x5,
+                 1 << 62, 0) == msa.MSA_ERR_UNSUPPORTED
     # no row attends more tokens than a request can hold
     assert _code(msa.msa_sparse_paged_attn, 0x1, 4, 16, kv, 0x2, 1 << 20, 0x3, (1 << 20) + 1, 0.1, 0x4, 0x5,
                  1 << 40, 0) == msa.MSA_ERR_UNSUPPORTED
