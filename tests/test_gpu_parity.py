@@ -338,6 +338,48 @@ def test_fused_decode_extreme_softmax_scale(gpu_lib, sm_scale):
     check_attention(b, out, table, ctx, rows)
 
 
+RANDOM_KV = [(syn.KV_BF16, syn.SCALE_NONE), (syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD),
+             (syn.KV_FP8, syn.SCALE_SCALAR), (syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD)]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_batches_match_oracle(gpu_lib, seed):
+    """Small batches whose shape is drawn from the seed (1 to 12 requests,
+    lengths 0 to 12000 so that empty requests and partial last blocks occur,
+    0 to 4 query rows each, top-k, query heads, K/V dtype and scale mode,
+    index dtype) through the fused step: metadata, selections, tables and
+    context lengths bit-exact, scores and attention within their bars, on
+    every row."""
+    rng = syn.SplitMix64(7000 + seed)
+    R = int(rng.integers(1, 12, 1)[0])
+    L = rng.integers(0, 12000, R)
+    L = np.where(rng.uniform(R) < 0.2, L // 128 * 128, L)   # whole blocks only
+    L = np.where(rng.uniform(R) < 0.2, 0, L)                 # empty requests
+    ql = np.minimum(rng.integers(0, 4, R), L)
+    if ql.sum() == 0:
+        L[0], ql[0] = max(int(L[0]), 1), 1
+    pick = lambda opts: opts[int(rng.integers(0, len(opts) - 1, 1)[0])]
+    topk, hq = pick([1, 2, 5, 16, 33, 64]), pick([8, 16, 24, 40, 64])
+    kv, sm = pick(RANDOM_KV)
+    idx = pick([syn.INDEX_BF16, syn.INDEX_FP8])
+    b = syn.make_batch("random_step", 7000 + seed, L, ql, topk=topk, num_q_heads=hq, kv_dtype=kv, scale_mode=sm,
+                       index_dtype=idx)
+    print(f"[random] seed {seed}: L={L.tolist()} ql={ql.tolist()} topk={topk} hq={hq} kv={kv} scale={sm} "
+          f"index={idx}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    H.run_decode(d, o)
+    check_metadata(b, H.read_metadata(d))
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    rows = list(range(b.num_rows))
+    check_scores(b, scores, rows)
+    check_selection(b, scores, table, ctx, sel, rows)
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    check_attention(b, out, table, ctx, rows)
+
+
 TIE_SHAPES = [
     # (longest row, lengths): rows past 1024 blocks select wave by wave with
     # the last keys re-read from memory; rows of at most 1024 or 256 blocks
