@@ -128,6 +128,58 @@ def test_block_major_extreme_softmax_scale(gpu_lib, sm_scale):
     assert d_out <= ATOL[syn.KV_BF16], f"block-major vs per-row max abs diff {d_out}"
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_block_major_random_batches(gpu_lib, seed):
+    """Prefill-sized batches whose shape is drawn from the seed (one to three
+    prefill requests of 700 to 2600 rows on contexts of up to 20000 tokens,
+    up to eight decode or empty requests around them, top-k, query heads, K/V
+    dtype and scale mode) through the block-major path: selections, tables
+    and context lengths bit-exact on every row, attention within the bars on
+    sampled rows, and the per-row path agrees."""
+    rng = syn.SplitMix64(7100 + seed)
+    npf, nd = int(rng.integers(1, 3, 1)[0]), int(rng.integers(0, 8, 1)[0])
+    qpf = rng.integers(700, 2600, npf)
+    Lpf = qpf + rng.integers(0, 17400, npf)
+    Ld = np.where(rng.uniform(nd) < 0.25, 0, rng.integers(1, 20000, nd))
+    L = np.concatenate([Ld, Lpf]).astype(np.int64)
+    ql = np.concatenate([np.minimum(Ld, 1), qpf]).astype(np.int64)
+    if ql.sum() < 2048:
+        ql[-1] += 2048 - ql.sum()
+        L[-1] = max(L[-1], ql[-1])
+    pick = lambda opts: opts[int(rng.integers(0, len(opts) - 1, 1)[0])]
+    topk, hq = pick([1, 4, 16, 32]), pick([16, 24, 32])
+    kv, sm = pick([(syn.KV_BF16, syn.SCALE_NONE), (syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD),
+                   (syn.KV_FP8, syn.SCALE_SCALAR), (syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD)])
+    b = syn.make_batch("bm_random", 7100 + seed, L, ql, topk=topk, num_q_heads=hq, kv_dtype=kv, scale_mode=sm)
+    assert b.num_rows >= 2048
+    print(f"[block-major] random seed {seed}: L={L.tolist()} ql={ql.tolist()} topk={topk} hq={hq} kv={kv} "
+          f"scale={sm}", flush=True)
+    d = H.upload(b)
+    o = H.alloc_decode(d)
+    wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0)
+    o.ws = torch.full((wsb // 4 + 1,), 0x3F3F3F3F, dtype=torch.int32, device="cuda")
+    o.wsb = wsb
+    H.run_decode(d, o)
+    torch.cuda.synchronize()
+    check_metadata(b, H.read_metadata(d))
+    scores = o.scores.cpu().numpy()
+    table, ctx, sel = o.table.cpu().numpy(), o.ctx.cpu().numpy(), o.sel.cpu().numpy()
+    check_selection(b, scores, table, ctx, sel, range(b.num_rows))
+    out = H.bf16_to_np(o.out)
+    assert np.isfinite(out).all()
+    rows = _sample_rows(b, 16, 7150 + seed)
+    rows = sorted(set(rows + [n for n in range(b.num_rows) if ctx[n] <= 128][:8]))
+    ref, amean = bars.oracle_and_abs_mean(b, table, ctx, rows)
+    err = np.abs(out[rows] - ref).max()
+    assert err <= ATOL[kv], f"attention max abs err {err}"
+    ex = bars.detect_excess(out[rows], ref, amean)
+    assert ex <= 0, f"attention outside the detector bar by {ex} (max abs err {err})"
+    o2 = H.alloc_decode(d)
+    H.run_decode(d, o2)
+    assert torch.equal(o2.table, o.table) and torch.equal(o2.ctx, o.ctx)
+    assert np.abs(H.bf16_to_np(o2.out) - out).max() <= ATOL[kv]
+
+
 @pytest.mark.parametrize("vexp", [40, -60])
 def test_block_major_extreme_values(gpu_lib, vexp):
     """V scaled by 2^vexp (exact in bf16): the fp16 block partials are scaled
