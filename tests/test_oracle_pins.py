@@ -14,7 +14,16 @@ import pytest
 import torch
 
 import msa_synth as syn
-from oracle import msa_oracle as O
+
+if os.environ.get("MSA_ORACLE_UNDER_TEST"):
+    # a copy of the oracle with one planted mistake (tests/test_oracle_mutations.py):
+    # the pins below must fail on it
+    import importlib.util
+    _spec = importlib.util.spec_from_file_location("msa_oracle_under_test", os.environ["MSA_ORACLE_UNDER_TEST"])
+    O = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(O)
+else:
+    from oracle import msa_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
