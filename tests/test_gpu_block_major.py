@@ -133,7 +133,7 @@ def test_block_major_random_batches(gpu_lib, seed):
     """Prefill-sized batches whose shape is drawn from the seed (one to three
     prefill requests of 700 to 2600 rows on contexts of up to 20000 tokens,
     up to eight decode or empty requests around them, top-k, query heads, K/V
-    dtype and scale mode) through the block-major path: selections, tables
+    dtype and scale mode, index dtype) through the block-major path: selections, tables
     and context lengths bit-exact on every row, attention within the bars on
     sampled rows, and the per-row path agrees."""
     rng = syn.SplitMix64(7100 + seed)
@@ -150,10 +150,12 @@ def test_block_major_random_batches(gpu_lib, seed):
     topk, hq = pick([1, 4, 16, 32]), pick([16, 24, 32])
     kv, sm = pick([(syn.KV_BF16, syn.SCALE_NONE), (syn.KV_BF16, syn.SCALE_PER_TOKEN_HEAD),
                    (syn.KV_FP8, syn.SCALE_SCALAR), (syn.KV_FP8, syn.SCALE_PER_TOKEN_HEAD)])
-    b = syn.make_batch("bm_random", 7100 + seed, L, ql, topk=topk, num_q_heads=hq, kv_dtype=kv, scale_mode=sm)
+    idx = pick([syn.INDEX_BF16, syn.INDEX_FP8])
+    b = syn.make_batch("bm_random", 7100 + seed, L, ql, topk=topk, num_q_heads=hq, kv_dtype=kv, scale_mode=sm,
+                       index_dtype=idx)
     assert b.num_rows >= 2048
     print(f"[block-major] random seed {seed}: L={L.tolist()} ql={ql.tolist()} topk={topk} hq={hq} kv={kv} "
-          f"scale={sm}", flush=True)
+          f"scale={sm} index={idx}", flush=True)
     d = H.upload(b)
     o = H.alloc_decode(d)
     wsb = msa.msa_decode_workspace_bytes(b.num_rows, b.max_seq_len, hq, topk, 0)
